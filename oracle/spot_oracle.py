@@ -1,0 +1,346 @@
+"""Float64 CPU oracle for block-sparse causal attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+baseline leg of the benchmark may import or call this module; the product
+path never does.  It shares no code with the HIP library and imports nothing
+from it (nor from torch).
+
+Everything here is plain NumPy in float64.  Inputs are the exact values the
+GPU receives (bf16 or fp32 bit patterns widened exactly to float64).
+
+Page key (titles of the five summarised papers):
+  [Spot]  SpotAttention: Plug-In Block-Sparse Routing for Pretrained
+          Long-Context Transformers
+  [PBS]   Sparsere Blok-Sparse Attention via Tokenpermutatie (PBS-Attn)
+  [S2O]   S2O - Vroege Stoppering voor Sparse Attention via Online Permutatie
+  [SPLA]  SPLA - Block Sparse Plus Linear Attention
+
+What each function follows:
+  pool_blocks        [PBS] §4 (mean pooling for block selection, on permuted keys)
+  meanpool_scores    [PBS] §4 with the attention scale; [Spot] §1 (score every
+                     previous block)
+  topp_keep          [Spot] §3 Dual top-p rule (reserved sink/recency blocks,
+                     nucleus on the residual distribution, stop once the mass
+                     reaches p, floor K_min)
+  indexer_scores     [Spot] §1 scoring equation (head-weighted ReLU of q.k)
+  attend_prefill     [PBS] Problem + §2 (block-sparse attention, segment-local
+                     causality), [S2O] §1 (index-array loads) and §3 (own
+                     segment as a dense causal window, history through the
+                     permutation)
+  attend_decode      [Spot] Problem (decode re-reads the KV cache): one query at
+                     the last position, softmax over the kept blocks
+  key_permutation    [PBS] §3 (importance from the last query block by mean
+                     pooling of attention, keys sorted descending per segment)
+
+Readings taken where the pages leave a step open (each is also listed with the
+design notes): the block distribution for top-p is the softmax of the block
+scores over the residual candidates; the mean-pool score carries the attention
+scale 1/sqrt(d); one kept list per KV head (queries pooled over the group);
+crossing is inclusive; ties go to the lower block index; p >= 1 keeps every
+residual block and p <= 0 keeps none; history blocks (earlier segments) are
+read through the permutation and fully visible, blocks of the query's own
+segment are read in natural order under the positional causal mask.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# ----------------------------------------------------------------- helpers
+def n_blocks(n: int, block: int) -> int:
+    return -(-n // block)
+
+
+def block_rows(j: int, block: int, n: int) -> np.ndarray:
+    """Token positions of block j: [jB, min((j+1)B, n))."""
+    return np.arange(j * block, min((j + 1) * block, n))
+
+
+def is_history(j: int, i: int, block: int, segment: int) -> bool:
+    """Key block j lies in a segment strictly before query block i's segment."""
+    if segment <= 0:
+        return False
+    return (j * block) // segment < (i * block) // segment
+
+
+# ----------------------------------------------------------------- O1 pool
+def pool_blocks(q, k, block, perm=None):
+    """Per-block means ([PBS] §4).
+
+    q: (Hq, L, d), k: (Hkv, L, d), perm: (Hkv, L) int or None.
+    Returns qbar (Hkv, nB, d): mean of Q over the G heads of the group and the
+    rows of the block; kbar_nat (Hkv, nB, d): mean of the block's K rows in
+    natural order; kbar_perm: mean of the K rows the permutation maps the
+    block's positions to (equal to kbar_nat without a permutation).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    hq, L, d = q.shape
+    hkv = k.shape[0]
+    G = hq // hkv
+    nb = n_blocks(L, block)
+    qbar = np.empty((hkv, nb, d))
+    kn = np.empty((hkv, nb, d))
+    kp = np.empty((hkv, nb, d))
+    for g in range(hkv):
+        for i in range(nb):
+            rows = block_rows(i, block, L)
+            qbar[g, i] = q[g * G:(g + 1) * G, rows].mean(axis=(0, 1))
+            kn[g, i] = k[g, rows].mean(axis=0)
+            kp[g, i] = k[g, perm[g, rows]].mean(axis=0) if perm is not None else kn[g, i]
+    return qbar, kn, kp
+
+
+# ----------------------------------------------------------------- O2 score
+def meanpool_scores(qbar, kbar_nat, kbar_perm, block, segment, sm_scale):
+    """s[g, i, j] = sm_scale * <qbar[g,i], kbar[g,j]> for j <= i, -inf for j > i.
+
+    kbar is the permuted-key mean for blocks of earlier segments and the
+    natural one otherwise ([PBS] §4 scores blocks of the permuted keys; the
+    query's own segment is read unpermuted, [S2O] §3).
+    """
+    hkv, nb, _ = qbar.shape
+    s = np.full((hkv, nb, nb), -np.inf)
+    for g in range(hkv):
+        for i in range(nb):
+            js = np.arange(i + 1)
+            hist = np.array([is_history(j, i, block, segment) for j in js], dtype=bool)
+            kb = np.where(hist[:, None], kbar_perm[g, :i + 1], kbar_nat[g, :i + 1])
+            s[g, i, :i + 1] = sm_scale * (kb @ qbar[g, i])
+    return s
+
+
+# ----------------------------------------------------------------- D1 indexer score
+def indexer_scores(idx_q, idx_w, idx_k):
+    """[Spot] §1: s[t] = sum_h w_h * ReLU(q^I_h . k^I_{h,t}).
+
+    idx_q: (H_idx, d_idx), idx_w: (H_idx,), idx_k: (nT, H_idx, d_idx) -> (nT,)
+    """
+    idx_q = np.asarray(idx_q, dtype=np.float64)
+    idx_w = np.asarray(idx_w, dtype=np.float64)
+    idx_k = np.asarray(idx_k, dtype=np.float64)
+    nt, h_idx, _ = idx_k.shape
+    s = np.zeros(nt)
+    for h in range(h_idx):
+        dots = idx_k[:, h, :] @ idx_q[h]
+        s += idx_w[h] * np.maximum(dots, 0.0)
+    return s
+
+
+# ----------------------------------------------------------------- O3 select
+def topp_detail(scores, forced, top_p, k_min):
+    """[Spot] §3 dual top-p on one row; returns the steps for inspection.
+
+    scores: (n,) candidate scores; forced: (n,) bool (sink and recency blocks).
+    Residual R = candidates not forced, ordered by (score desc, index asc);
+    pi = softmax over R; c_k = sum of the first k of pi (c_0 = 0);
+    k* = min{k >= 0 : c_k >= p}, raised to min(K_min, |R|); p >= 1 keeps R.
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    forced = np.asarray(forced, dtype=bool)
+    cand = np.arange(scores.shape[0])
+    resid = cand[~forced]
+    order = resid[np.lexsort((resid, -scores[resid]))]
+    n = order.shape[0]
+    if n:
+        sr = scores[order]
+        e = np.exp(sr - sr[0])
+        pi = e / e.sum()
+        c = np.cumsum(pi)
+    else:
+        pi = np.zeros(0)
+        c = np.zeros(0)
+    if top_p >= 1.0:
+        kstar = n
+    elif top_p <= 0.0:
+        kstar = 0
+    else:
+        hit = np.nonzero(c >= top_p)[0]
+        kstar = int(hit[0]) + 1 if hit.size else n
+    kstar = max(kstar, min(int(k_min), n))
+    kept = np.sort(np.concatenate([cand[forced], order[:kstar]])).astype(np.int64)
+    return dict(kept=kept, order=order, pi=pi, cum=c, kstar=kstar)
+
+
+def topp_keep(scores, forced, top_p, k_min):
+    return topp_detail(scores, forced, top_p, k_min)["kept"]
+
+
+def prefill_forced(i, n_sink, n_recent):
+    """Sink blocks j < n_sink and recency blocks i - n_recent < j <= i."""
+    js = np.arange(i + 1)
+    return (js < n_sink) | (js > i - n_recent)
+
+
+def decode_forced(nt, n_sink, n_recent):
+    ts = np.arange(nt)
+    return (ts < n_sink) | (ts > nt - 1 - n_recent)
+
+
+def select_prefill(scores, n_sink, n_recent, top_p, k_min, rows=None):
+    """Kept block lists per (KV head, query block): list[g][i] -> sorted array."""
+    hkv, nb, _ = scores.shape
+    rows = range(nb) if rows is None else rows
+    out = [dict() for _ in range(hkv)]
+    for g in range(hkv):
+        for i in rows:
+            out[g][int(i)] = topp_keep(scores[g, i, :i + 1], prefill_forced(i, n_sink, n_recent),
+                                       top_p, k_min)
+    return out
+
+
+def select_decode(scores, n_sink, n_recent, top_p, k_min):
+    nt = scores.shape[0]
+    return topp_keep(scores, decode_forced(nt, n_sink, n_recent), top_p, k_min)
+
+
+# ----------------------------------------------------------------- O4 attend (prefill)
+def prefill_key_set(kept, i, g, block, segment, perm, L):
+    """Key rows and their logical positions for query block i.
+
+    History blocks (earlier segments) contribute perm[g, t] for t in the
+    block and are fully visible (logical position -1 marks 'always visible');
+    own-segment blocks contribute their natural rows t, visible to row r iff
+    t <= r.
+    """
+    phys, lim = [], []
+    for j in kept:
+        ts = block_rows(int(j), block, L)
+        if perm is not None and is_history(int(j), i, block, segment):
+            phys.append(perm[g, ts])
+            lim.append(np.full(ts.shape, -1))
+        else:
+            phys.append(ts)
+            lim.append(ts)
+    return np.concatenate(phys), np.concatenate(lim)
+
+
+def attend_prefill(q, k, v, kept_lists, block, sm_scale, segment=0, perm=None, qblocks=None):
+    """Softmax attention of each query row over the union of its kept keys.
+
+    q: (Hq, L, d); k, v: (Hkv, L, d); kept_lists[g][i] -> kept block indices.
+    Returns O (Hq, L, d) and natural-log LSE (Hq, L); rows of query blocks
+    not in `qblocks` are NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    hq, L, d = q.shape
+    hkv = k.shape[0]
+    G = hq // hkv
+    nb = n_blocks(L, block)
+    qblocks = range(nb) if qblocks is None else qblocks
+    o = np.full((hq, L, d), np.nan)
+    lse = np.full((hq, L), np.nan)
+    for g in range(hkv):
+        for i in qblocks:
+            i = int(i)
+            rows = block_rows(i, block, L)
+            phys, lim = prefill_key_set(kept_lists[g][i], i, g, block, segment, perm, L)
+            visible = lim[None, :] <= rows[:, None]          # (rows, keys)
+            ks, vs = k[g, phys], v[g, phys]
+            for h in range(g * G, (g + 1) * G):
+                logits = sm_scale * (q[h, rows] @ ks.T)
+                logits = np.where(visible, logits, -np.inf)
+                m = logits.max(axis=1, keepdims=True)
+                e = np.exp(logits - m)
+                z = e.sum(axis=1, keepdims=True)
+                o[h, rows] = (e @ vs) / z
+                lse[h, rows] = (m + np.log(z))[:, 0]
+    return o, lse
+
+
+# ----------------------------------------------------------------- D3 attend (decode)
+def attend_decode(q, k_cache, v_cache, kept, block, T, sm_scale):
+    """One query at position T-1 per head over the keys of the kept blocks.
+
+    q: (Hq, d); k_cache, v_cache: (Hkv, T, d); kept: block indices.
+    Returns O (Hq, d) and LSE (Hq,).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    hq, d = q.shape
+    hkv = k_cache.shape[0]
+    G = hq // hkv
+    keys = np.concatenate([block_rows(int(t), block, T) for t in kept])
+    o = np.empty((hq, d))
+    lse = np.empty(hq)
+    for g in range(hkv):
+        ks = np.asarray(k_cache[g, keys], dtype=np.float64)
+        vs = np.asarray(v_cache[g, keys], dtype=np.float64)
+        for h in range(g * G, (g + 1) * G):
+            logits = sm_scale * (ks @ q[h])
+            m = logits.max()
+            e = np.exp(logits - m)
+            z = e.sum()
+            o[h] = (e @ vs) / z
+            lse[h] = m + np.log(z)
+    return o, lse
+
+
+# ----------------------------------------------------------------- key permutation
+def key_importance(q, k, block, sm_scale):
+    """[PBS] §3: importance of every key from the last query block.
+
+    For each KV head g: the causal attention probabilities of every query row
+    r of the last block, for every head of the group, averaged (mean pooling)
+    over those rows and heads.  Keys after r get probability 0.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    hq, L, d = q.shape
+    hkv = k.shape[0]
+    G = hq // hkv
+    rows = block_rows(n_blocks(L, block) - 1, block, L)
+    pos = np.arange(L)
+    imp = np.zeros((hkv, L))
+    for g in range(hkv):
+        for h in range(g * G, (g + 1) * G):
+            logits = sm_scale * (q[h, rows] @ k[g].T)
+            logits = np.where(pos[None, :] <= rows[:, None], logits, -np.inf)
+            m = logits.max(axis=1, keepdims=True)
+            e = np.exp(logits - m)
+            imp[g] += (e / e.sum(axis=1, keepdims=True)).sum(axis=0)
+        imp[g] /= G * rows.shape[0]
+    return imp
+
+
+def key_permutation(q, k, block, segment, sm_scale):
+    """[PBS] §2-3: inside each segment, positions sorted by importance
+    descending (ties by position ascending).  perm[g, t] is the physical row
+    that logical position t reads."""
+    imp = key_importance(q, k, block, sm_scale)
+    hkv, L = imp.shape
+    perm = np.empty((hkv, L), dtype=np.int64)
+    for g in range(hkv):
+        for s0 in range(0, L, segment):
+            ts = np.arange(s0, min(s0 + segment, L))
+            perm[g, ts] = ts[np.lexsort((ts, -imp[g, ts]))]
+    return perm, imp
+
+
+# ----------------------------------------------------------------- pipelines
+def prefill(q, k, v, block, top_p, n_sink=1, n_recent=1, k_min=0, sm_scale=None,
+            segment=0, perm=None, qblocks=None):
+    """Whole prefill path for one sequence: pool -> score -> select -> attend.
+
+    q: (Hq, L, d), k/v: (Hkv, L, d).  Returns dict with scores, kept lists,
+    O and LSE (rows outside `qblocks` NaN).
+    """
+    d = q.shape[-1]
+    sm_scale = 1.0 / np.sqrt(d) if not sm_scale else sm_scale
+    qbar, kn, kp = pool_blocks(q, k, block, perm)
+    s = meanpool_scores(qbar, kn, kp, block, segment, sm_scale)
+    kept = select_prefill(s, n_sink, n_recent, top_p, k_min, rows=qblocks)
+    o, lse = attend_prefill(q, k, v, kept, block, sm_scale, segment, perm, qblocks)
+    return dict(scores=s, kept=kept, o=o, lse=lse, qbar=qbar, kbar_nat=kn, kbar_perm=kp)
+
+
+def decode(q, k_cache, v_cache, idx_q, idx_w, idx_k, block, T, top_p, n_sink=1, n_recent=1,
+           k_min=0, sm_scale=None):
+    """Whole decode step for one sequence: indexer score -> select -> attend."""
+    d = q.shape[-1]
+    sm_scale = 1.0 / np.sqrt(d) if not sm_scale else sm_scale
+    s = indexer_scores(idx_q, idx_w, idx_k)
+    kept = select_decode(s, n_sink, n_recent, top_p, k_min)
+    o, lse = attend_decode(q, k_cache, v_cache, kept, block, T, sm_scale)
+    return dict(scores=s, kept=kept, o=o, lse=lse)
