@@ -1,0 +1,277 @@
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+One step = the whole prefill path on the GQA workload (L=8192, 32 query / 8 KV
+heads, d=128, bf16, block 64, top-p 0.9): mean-pool block scores, top-p
+selection, sparse attention.  Inputs are resident in HBM before timing.
+
+Prints one JSON line.  `value` is effective TFLOP/s over kept blocks
+(4*d*visible query-key pairs per step / step time).  The line also carries the
+roofline of the dominant kernel (the attention kernel, bf16 MFMA bound), a
+decode measurement on the sparse-decode workload (batch 16, context 131072,
+KV GB/s against HBM) and the float64 oracle timed on a bounded sample on the
+host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+METRIC = "effective TFLOP/s sparse prefill (kept blocks); decode KV GB/s; % roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-sample-blocks", type=int, default=12)
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------- work accounting
+def prefill_visible_pairs(idx: np.ndarray, cnt: np.ndarray, L: int, B: int, G: int) -> np.ndarray:
+    """Visible (query, key) pairs per (batch, KV head, query block), summed over
+    the G query heads: kept blocks before the diagonal count |blk(j)| keys per
+    row, the diagonal counts r - iB + 1 keys for row r."""
+    nb = idx.shape[-1]
+    bs = np.minimum(B, L - np.arange(nb) * B).astype(np.int64)
+    bs_ext = np.concatenate([bs, [0]])
+    safe = np.where(idx >= 0, idx, nb)
+    keys = bs_ext[safe].sum(axis=-1)                                   # keys of all kept blocks
+    i_of_row = np.arange(nb)
+    diag_kept = (idx == i_of_row[:, None]).any(axis=-1)
+    nrow = bs                                                          # rows of query block i
+    full = keys - np.where(diag_kept, nrow, 0)
+    pairs = nrow * full + np.where(diag_kept, nrow * (nrow + 1) // 2, 0)
+    return G * pairs
+
+
+def source_digest(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_file: str, key: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(key)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_digest(kernel_file):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------- prefill
+def bench_prefill(args, torch, B, I):
+    cfg = I.C2
+    dev = torch.device("cuda:0")
+    q, k, v = I.prefill_inputs(cfg)
+    dq = torch.from_numpy(q).to(torch.bfloat16).to(dev)
+    dk = torch.from_numpy(k).to(torch.bfloat16).to(dev)
+    dv = torch.from_numpy(v).to(torch.bfloat16).to(dev)
+    desc = B.prefill_desc(dq, dk, cfg.block, cfg.top_p)
+    bufs = B.alloc_prefill(desc, dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        B.spot_block_score(desc, dq, dk, None, None, None, None, bufs.scores, bufs.workspace)
+        B.spot_select_topp(desc, bufs.scores, bufs.idx, bufs.cnt)
+        if ev is not None:
+            ev[1].record()
+        B.spot_sparse_attn_prefill(desc, dq, dk, dv, None, bufs.idx, bufs.cnt, bufs.o, bufs.lse)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # K steps back to back
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    # per-kernel split with events on the launch stream (same work again)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    ms_sel = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    idx = bufs.idx.cpu().numpy()
+    cnt = bufs.cnt.cpu().numpy()
+    G = cfg.hq // cfg.hkv
+    pairs = prefill_visible_pairs(idx, cnt, cfg.L, cfg.block, G)
+    flops = 4.0 * cfg.d * float(pairs.sum())
+    dense_pairs = G * cfg.hkv * cfg.L * (cfg.L + 1) / 2
+    kept_fraction = float(pairs.sum()) / dense_pairs
+
+    attn_file = os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "kernels", "prefill.hip")
+    achieved = flops / (ms_attn * 1e-3) / 1e12
+    res = dict(
+        cfg=cfg, ms_step=ms_step, ms_sel=ms_sel, ms_attn=ms_attn, flops=flops, kept_fraction=kept_fraction,
+        value=flops / (ms_step * 1e-3) / 1e12,
+        roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                  "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                  "traffic": load_traffic(attn_file, "prefill_mfma_kernel@gqa-bf16-L8192"),
+                  "kernel": "prefill_mfma_kernel<128,8>", "flop_per_launch": flops,
+                  "avg_launch_ms": round(ms_attn, 4)},
+        host=(q, k, v), idx=idx, cnt=cnt,
+    )
+    return res
+
+
+# ----------------------------------------------------------------- decode
+def bench_decode(args, torch, B, I):
+    cfg = I.C4
+    dev = torch.device("cuda:0")
+    D = I.decode_inputs(cfg)
+    up = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)
+    q, kc, vc = up(D["q"]), up(D["k_cache"]), up(D["v_cache"])
+    iq, ik = up(D["idx_q"]), up(D["idx_k"])
+    iw = torch.from_numpy(D["idx_w"]).to(dev)
+    del D
+    desc = B.decode_desc(q, kc, cfg.block, cfg.top_p, cfg.h_idx, cfg.d_idx)
+    bufs = B.alloc_decode(desc, dev)
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+
+    def step(ev):
+        ev[0].record()
+        B.spot_block_score(desc, None, None, None, iq, iw, ik, bufs.scores)
+        B.spot_select_topp(desc, bufs.scores, bufs.idx, bufs.cnt)
+        ev[1].record()
+        B.spot_sparse_attn_decode(desc, q, kc, vc, bufs.idx, bufs.cnt, bufs.o, bufs.lse, bufs.workspace)
+        ev[2].record()
+
+    for _ in range(args.warmup):
+        step([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        flush.fill_(1.0)          # evict the 256 MB last-level cache between steps (outside the events)
+        step(e)
+    torch.cuda.synchronize()
+    ms_front = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_step = ms_front + ms_attn
+    cnt = bufs.cnt.cpu().numpy()[:, 0, 0]
+    idx = bufs.idx.cpu().numpy()[:, 0, 0]
+    bs = np.minimum(cfg.block, cfg.T - np.arange(cfg.nt) * cfg.block)
+    kept_keys = np.array([bs[idx[b, :cnt[b]]].sum() for b in range(cfg.batch)], dtype=np.float64)
+    kv_bytes = float(kept_keys.sum()) * cfg.hkv * cfg.d * 2 * 2
+    scan_bytes = cfg.batch * cfg.nt * cfg.h_idx * cfg.d_idx * 2.0
+    qo_bytes = cfg.batch * cfg.hq * cfg.d * 2 * 2.0 + cfg.batch * cfg.h_idx * (cfg.d_idx * 2 + 4)
+    step_bytes = kv_bytes + scan_bytes + qo_bytes
+    attn_gbs = (kv_bytes + qo_bytes) / (ms_attn * 1e-3) / 1e9
+    return dict(
+        workload=cfg.name, value=round(step_bytes / (ms_step * 1e-3) / 1e9, 1), unit="GB/s",
+        ms_per_step=round(ms_step, 4), ms_score_select=round(ms_front, 4), ms_attention=round(ms_attn, 4),
+        kept_fraction=round(float(kept_keys.sum()) / (cfg.batch * cfg.T), 4), bytes_per_step=step_bytes,
+        roofline={"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "kernel": "decode_split_kernel<128,4>+combine",
+                  "bytes_per_launch": kv_bytes + qo_bytes},
+    )
+
+
+# ----------------------------------------------------------------- oracle on the host
+def cpu_baseline(res, I, sample_blocks: int):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    cfg = res["cfg"]
+    q, k, v = res["host"]
+    rng = np.random.default_rng([cfg.seed, 1234])
+    blocks = sorted({cfg.nb - 1} | set(rng.choice(cfg.nb, sample_blocks - 1, replace=False).tolist()))
+    scale = 1 / math.sqrt(cfg.d)
+    t0 = time.time()
+    out = oracle.prefill(q[0], k[0], v[0], cfg.block, cfg.top_p, qblocks=blocks)
+    dt = time.time() - t0
+    G = cfg.hq // cfg.hkv
+    nb = cfg.nb
+    idx = np.full((1, cfg.hkv, nb, nb), -1, np.int64)
+    sel = np.zeros((1, cfg.hkv, nb), bool)
+    for g in range(cfg.hkv):
+        for i in blocks:
+            kl = out["kept"][g][i]
+            idx[0, g, i, :len(kl)] = kl
+            sel[0, g, i] = True
+    pairs = prefill_visible_pairs(idx, None, cfg.L, cfg.block, G)
+    flops = 4.0 * cfg.d * float(pairs[sel].sum())
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"float64 NumPy oracle, whole pipeline (pool and score every block, select and attend "
+                      f"{len(blocks)} seeded query blocks x {cfg.hkv} KV heads of {cfg.name})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from block_sparse_attention_amd import binding as B
+    from block_sparse_attention_amd import inputs as I
+    B.load_library()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    pre = bench_prefill(args, torch, B, I)
+    print(f"[bench] prefill {pre['cfg'].name}: {pre['ms_step']:.4f} ms/step, attention {pre['ms_attn']:.4f} ms, "
+          f"score+select {pre['ms_sel']:.4f} ms, kept {pre['kept_fraction']:.4f}", file=sys.stderr, flush=True)
+    dec = None
+    if not args.no_decode:
+        dec = bench_decode(args, torch, B, I)
+        print(f"[bench] decode: {dec}", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(pre, I, args.cpu_sample_blocks)
+        print(f"[bench] cpu baseline: {cpu}", file=sys.stderr, flush=True)
+
+    cfg = pre["cfg"]
+    line = {
+        "metric": METRIC, "value": round(pre["value"], 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(pre["ms_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.L, "hq": cfg.hq, "hkv": cfg.hkv,
+                   "d": cfg.d, "block": cfg.block, "top_p": cfg.top_p, "n_sink": cfg.n_sink,
+                   "n_recent": cfg.n_recent, "kept_fraction": round(pre["kept_fraction"], 4),
+                   "ms_attention": round(pre["ms_attn"], 4), "ms_score_select": round(pre["ms_sel"], 4),
+                   "flop_per_step": pre["flops"]},
+        "roofline": pre["roofline"],
+        "cpu_baseline": cpu,
+        "decode": dec,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,226 @@
+// Block scoring kernels for gfx950.
+//
+// pool_blocks      per-block means of Q (over the heads of a KV group and the
+//                  rows of the block) and of K (natural, and through the key
+//                  permutation): mean pooling for block selection as in PBS-Attn
+//                  section 4 ("Implementatie", block selection on permuted keys).
+// meanpool_score   sm_scale * <qbar_i, kbar_j> for every key block j <= i
+//                  (SpotAttention section 1: all previous blocks are scored in
+//                  one contraction); j > i is -inf.
+// indexer_score    SpotAttention section 1 scoring equation:
+//                  sum_h w_h ReLU(q^I_h . k^I_{h,t}), one streaming pass over the
+//                  indexer key cache.
+//
+// All three are HBM- or latency-bound; they use plain fp32 VALU arithmetic.
+#include "../launch.h"
+#include "common.h"
+
+namespace spot {
+
+// ---------------------------------------------------------------- pooling
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&x)[8]);
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&x)[8]) {
+  uint4 u = *reinterpret_cast<const uint4*>(p);
+  x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+  x[4] = bf16_lo(u.z); x[5] = bf16_hi(u.z); x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// Reduce per-thread column partials (rows_par row slots x d columns) through
+// LDS and store sum * inv_count for the d columns.
+__device__ __forceinline__ void reduce_cols_store(float (&acc)[8], float* red, int lr, int rp, int rows_par,
+                                                  int d, float inv_count, float* out) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rp * d + lr * 8 + e] = acc[e];
+  __syncthreads();
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    float s = 0.f;
+    for (int r = 0; r < rows_par; ++r) s += red[r * d + c];
+    out[c] = s * inv_count;
+  }
+  __syncthreads();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void pool_blocks_kernel(PoolArgs a) {
+  __shared__ float red[256 * 8];
+  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int d = a.d, L = a.L, B = a.block;
+  const int G = a.hq / a.hkv;
+  const int lpr = d / 8;              // lanes per row
+  const int rows_par = 256 / lpr;     // rows in flight per pass
+  const int lr = threadIdx.x % lpr, rp = threadIdx.x / lpr;
+  const int r0 = i * B;
+  const int nr = min(B, L - r0);
+  const T* Q = static_cast<const T*>(a.q);
+  const T* K = static_cast<const T*>(a.k);
+  const size_t out_off = ((size_t(b) * a.hkv + g) * a.nb + i) * d;
+
+  float acc[8];
+  // Q: G heads x nr rows
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int rr = rp; rr < G * nr; rr += rows_par) {
+    const int h = g * G + rr / nr, r = r0 + rr % nr;
+    float x[8];
+    load8<T>(Q + ((size_t(b) * a.hq + h) * L + r) * d + lr * 8, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += x[e];
+  }
+  reduce_cols_store(acc, red, lr, rp, rows_par, d, 1.0f / float(G * nr), a.qbar + out_off);
+
+  const size_t kv_row0 = (size_t(b) * a.hkv + g) * L;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int rr = rp; rr < nr; rr += rows_par) {
+    float x[8];
+    load8<T>(K + (kv_row0 + r0 + rr) * d + lr * 8, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += x[e];
+  }
+  reduce_cols_store(acc, red, lr, rp, rows_par, d, 1.0f / float(nr), a.kbar_nat + out_off);
+
+  if (a.perm) {
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int rr = rp; rr < nr; rr += rows_par) {
+      const int phys = a.perm[kv_row0 + r0 + rr];
+      float x[8];
+      load8<T>(K + (kv_row0 + phys) * d + lr * 8, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += x[e];
+    }
+    reduce_cols_store(acc, red, lr, rp, rows_par, d, 1.0f / float(nr), a.kbar_perm + out_off);
+  }
+}
+
+hipError_t launch_pool_blocks(const PoolArgs& a, hipStream_t s) {
+  dim3 grid(a.nb, a.hkv, a.batch);
+  if (a.bf16)
+    pool_blocks_kernel<uint16_t><<<grid, 256, 0, s>>>(a);
+  else
+    pool_blocks_kernel<float><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- mean-pool score
+constexpr int kST = 32;  // score tile (query blocks x key blocks)
+
+__global__ __launch_bounds__(256) void meanpool_score_kernel(MeanpoolScoreArgs a) {
+  extern __shared__ float sm[];
+  const int d = a.d, nb = a.nb;
+  const int ld = d + 1;
+  float* qs = sm;
+  float* kn = qs + kST * ld;
+  float* kp = kn + kST * ld;
+  const int i0 = blockIdx.y * kST, j0 = blockIdx.x * kST;
+  const size_t bg = blockIdx.z;
+  float* out = a.scores + bg * size_t(nb) * nb;
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+
+  if (j0 > i0 + kST - 1) {  // entirely above the diagonal
+    for (int e = threadIdx.x; e < kST * kST; e += 256) {
+      const int i = i0 + e / kST, j = j0 + e % kST;
+      if (i < nb && j < nb) out[size_t(i) * nb + j] = -kInf;
+    }
+    return;
+  }
+  const float* qb = a.qbar + bg * size_t(nb) * d;
+  const float* knb = a.kbar_nat + bg * size_t(nb) * d;
+  const float* kpb = a.kbar_perm ? a.kbar_perm + bg * size_t(nb) * d : nullptr;
+  for (int e = threadIdx.x; e < kST * d; e += 256) {
+    const int r = e / d, c = e % d;
+    qs[r * ld + c] = (i0 + r < nb) ? qb[size_t(i0 + r) * d + c] : 0.f;
+    kn[r * ld + c] = (j0 + r < nb) ? knb[size_t(j0 + r) * d + c] : 0.f;
+    if (kpb) kp[r * ld + c] = (j0 + r < nb) ? kpb[size_t(j0 + r) * d + c] : 0.f;
+  }
+  __syncthreads();
+  float sn[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, sp[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  for (int c = 0; c < d; ++c) {
+    const float q0 = qs[(ty * 2) * ld + c], q1 = qs[(ty * 2 + 1) * ld + c];
+    const float k0 = kn[(tx * 2) * ld + c], k1 = kn[(tx * 2 + 1) * ld + c];
+    sn[0][0] = fmaf(q0, k0, sn[0][0]); sn[0][1] = fmaf(q0, k1, sn[0][1]);
+    sn[1][0] = fmaf(q1, k0, sn[1][0]); sn[1][1] = fmaf(q1, k1, sn[1][1]);
+    if (kpb) {
+      const float p0 = kp[(tx * 2) * ld + c], p1 = kp[(tx * 2 + 1) * ld + c];
+      sp[0][0] = fmaf(q0, p0, sp[0][0]); sp[0][1] = fmaf(q0, p1, sp[0][1]);
+      sp[1][0] = fmaf(q1, p0, sp[1][0]); sp[1][1] = fmaf(q1, p1, sp[1][1]);
+    }
+  }
+  for (int u = 0; u < 2; ++u)
+    for (int w = 0; w < 2; ++w) {
+      const int i = i0 + ty * 2 + u, j = j0 + tx * 2 + w;
+      if (i >= nb || j >= nb) continue;
+      float v = -kInf;
+      if (j <= i) {
+        const bool hist = kpb && a.segment > 0 && (j * a.block) / a.segment < (i * a.block) / a.segment;
+        v = a.scale * (hist ? sp[u][w] : sn[u][w]);
+      }
+      out[size_t(i) * nb + j] = v;
+    }
+}
+
+hipError_t launch_meanpool_score(const MeanpoolScoreArgs& a, hipStream_t s) {
+  const int nt = (a.nb + kST - 1) / kST;
+  dim3 grid(nt, nt, a.batch * a.hkv);
+  size_t lds = size_t(3) * kST * (a.d + 1) * sizeof(float);
+  meanpool_score_kernel<<<grid, 256, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- ReLU indexer score
+// One wave per key block t at a time; each lane owns 4 consecutive elements
+// of the (h_idx x d_idx) row, lanes of one indexer head form a group of
+// d_idx/4 lanes.
+constexpr int kIdxUnroll = 4;
+
+__global__ __launch_bounds__(256) void indexer_score_kernel(IndexerScoreArgs a) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int R = a.h_idx * a.d_idx;
+  const int gs = a.d_idx / 4;  // lanes per indexer head
+  const int e0 = lane * 4;
+  const bool active = e0 < R;
+  const int head = active ? e0 / a.d_idx : 0;
+  uint2 qv = make_uint2(0u, 0u);
+  float w = 0.f;
+  if (active) {
+    qv = *reinterpret_cast<const uint2*>(a.idx_q + size_t(b) * R + e0);
+    w = a.idx_w[size_t(b) * a.h_idx + head];
+  }
+  const int waves_total = gridDim.x * 4;
+  const uint16_t* kb = a.idx_k + size_t(b) * a.nk * R;
+  for (int t0 = (blockIdx.x * 4 + wave) * kIdxUnroll; t0 < a.nk; t0 += waves_total * kIdxUnroll) {
+    uint2 kv[kIdxUnroll];
+#pragma unroll
+    for (int u = 0; u < kIdxUnroll; ++u) {
+      const int t = t0 + u;
+      kv[u] = (active && t < a.nk) ? *reinterpret_cast<const uint2*>(kb + size_t(t) * R + e0) : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kIdxUnroll; ++u) {
+      float dp = dot2_bf16(kv[u].x, qv.x, dot2_bf16(kv[u].y, qv.y, 0.f));
+      for (int o = gs >> 1; o > 0; o >>= 1) dp += __shfl_xor(dp, o);
+      float val = (active && (lane % gs) == 0) ? w * fmaxf(dp, 0.f) : 0.f;
+      val = wave_sum(val);
+      const int t = t0 + u;
+      if (lane == 0 && t < a.nk) a.scores[size_t(b) * a.nk + t] = val;
+    }
+  }
+}
+
+hipError_t launch_indexer_score(const IndexerScoreArgs& a, hipStream_t s) {
+  const int per_block = 4 * kIdxUnroll;
+  int blocks = (a.nk + per_block - 1) / per_block;
+  if (blocks > 1024) blocks = 1024;
+  dim3 grid(blocks, a.batch);
+  indexer_score_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace spot

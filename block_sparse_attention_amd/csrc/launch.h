@@ -1,0 +1,81 @@
+// Host-side launchers of the gfx950 kernels (one definition per kernel file).
+// Arguments are validated by the C ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spot {
+
+struct PoolArgs {
+  const void* q;
+  const void* k;
+  const int32_t* perm;   // nullable
+  float* qbar;           // [batch, hkv, nb, d]
+  float* kbar_nat;
+  float* kbar_perm;      // written only when perm != nullptr
+  int bf16, batch, hq, hkv, d, L, block, nb;
+};
+hipError_t launch_pool_blocks(const PoolArgs& a, hipStream_t s);
+
+struct MeanpoolScoreArgs {
+  const float* qbar;
+  const float* kbar_nat;
+  const float* kbar_perm;  // nullable
+  float* scores;           // [batch, hkv, nb, nb]
+  int batch, hkv, d, nb, block, segment;
+  float scale;
+};
+hipError_t launch_meanpool_score(const MeanpoolScoreArgs& a, hipStream_t s);
+
+struct IndexerScoreArgs {
+  const uint16_t* idx_q;  // [batch, h_idx, d_idx] bf16
+  const float* idx_w;     // [batch, h_idx]
+  const uint16_t* idx_k;  // [batch, nk, h_idx, d_idx] bf16
+  float* scores;          // [batch, nk]
+  int batch, nk, h_idx, d_idx;
+};
+hipError_t launch_indexer_score(const IndexerScoreArgs& a, hipStream_t s);
+
+struct SelectArgs {
+  const float* scores;  // [rows, nk]
+  int32_t* idx;         // [rows, nk]
+  int32_t* cnt;         // [rows]
+  int rows, nk, nq;     // nq == 1: decode rows (candidates 0..nk-1); else row % nq = query block i
+  int n_sink, n_recent, k_min;
+  float top_p;
+};
+hipError_t launch_select_topp(const SelectArgs& a, hipStream_t s);
+constexpr int kSelectMaxCandidates = 16384;
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* perm;  // nullable
+  const int32_t* idx;   // [batch, hkv, nb, nb]
+  const int32_t* cnt;   // [batch, hkv, nb]
+  void* o;
+  float* lse;           // nullable
+  int bf16, batch, hq, hkv, d, L, block, segment, nb;
+  float sm_scale;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+struct DecodeArgs {
+  const uint16_t* q;   // [batch, hq, d]
+  const uint16_t* k;   // [batch, hkv, T, d]
+  const uint16_t* v;
+  const int32_t* idx;  // [batch, nk]
+  const int32_t* cnt;  // [batch]
+  uint16_t* o;         // [batch, hq, d]
+  float* lse;          // nullable
+  float* partials;     // workspace
+  int batch, hq, hkv, d, T, block, nk, nsplit;
+  float sm_scale;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+int decode_num_splits(int batch, int hkv, int nk);
+size_t decode_partials_bytes(int batch, int hq, int d, int nsplit);
+
+}  // namespace spot

@@ -1,0 +1,259 @@
+// C ABI of libspot: host-side validation, workspace sizing and dispatch.
+// Nothing here allocates, frees or synchronises; kernels are enqueued on the
+// caller's stream.  Every check happens before the first launch, so a failed
+// call enqueues nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "../../include/spot.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("SPOT_LOG");
+    return e && e[0] && e[0] != '0';
+  }();
+  return on;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SPOT_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  if (log_enabled()) std::fprintf(stderr, "[spot] %s launched\n", what);
+  g_err.clear();
+  return SPOT_OK;
+}
+
+bool pow2_block(int b) { return b == 16 || b == 32 || b == 64 || b == 128; }
+
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Checks shared by all calls.
+int check_common(const spot_desc* d) {
+  if (!d) return fail(SPOT_ERR_INVALID, "desc is NULL");
+  if (d->version != SPOT_ABI_VERSION) return fail(SPOT_ERR_INVALID, "desc.version %d != %d", d->version, SPOT_ABI_VERSION);
+  if (d->dtype != SPOT_F32 && d->dtype != SPOT_BF16) return fail(SPOT_ERR_INVALID, "unknown dtype %d", d->dtype);
+  if (d->batch < 1 || d->hq < 1 || d->hkv < 1) return fail(SPOT_ERR_INVALID, "batch, hq and hkv must be >= 1");
+  if (d->hq % d->hkv) return fail(SPOT_ERR_INVALID, "hq (%d) not a multiple of hkv (%d)", d->hq, d->hkv);
+  if (d->d != 64 && d->d != 128) return fail(SPOT_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d->d);
+  if (!pow2_block(d->block)) return fail(SPOT_ERR_UNSUPPORTED, "block %d (supported: 16, 32, 64, 128)", d->block);
+  if (d->q_len < 1 || d->kv_len < 1) return fail(SPOT_ERR_INVALID, "q_len and kv_len must be >= 1");
+  if (d->kv_len > (int64_t(1) << 30)) return fail(SPOT_ERR_UNSUPPORTED, "kv_len %lld too long", (long long)d->kv_len);
+  if (!(std::isfinite(d->sm_scale)) || d->sm_scale < 0.f) return fail(SPOT_ERR_INVALID, "sm_scale must be finite and >= 0");
+  return SPOT_OK;
+}
+
+bool is_decode(const spot_desc* d) { return d->q_len == 1 && d->score_kind == SPOT_SCORE_RELU_INDEXER; }
+
+int check_prefill_shape(const spot_desc* d) {
+  if (d->q_len != d->kv_len) return fail(SPOT_ERR_INVALID, "prefill needs q_len == kv_len");
+  if (d->segment < 0) return fail(SPOT_ERR_INVALID, "segment must be >= 0");
+  if (d->segment > 0 && d->segment % d->block) return fail(SPOT_ERR_INVALID, "segment %d not a multiple of block %d", d->segment, d->block);
+  const int64_t nb = ceil_div64(d->q_len, d->block);
+  if (nb > 65536) return fail(SPOT_ERR_UNSUPPORTED, "%lld blocks per sequence (max 65536)", (long long)nb);
+  return SPOT_OK;
+}
+
+int check_selection_params(const spot_desc* d) {
+  if (d->n_sink < 0 || d->n_recent < 0 || d->k_min < 0) return fail(SPOT_ERR_INVALID, "n_sink, n_recent, k_min must be >= 0");
+  if (d->n_sink + d->n_recent < 1) return fail(SPOT_ERR_INVALID, "n_sink + n_recent must be >= 1");
+  if (std::isnan(d->top_p)) return fail(SPOT_ERR_INVALID, "top_p is NaN");
+  return SPOT_OK;
+}
+
+float effective_scale(const spot_desc* d) {
+  return d->sm_scale > 0.f ? d->sm_scale : 1.0f / std::sqrt(float(d->d));
+}
+
+size_t meanpool_ws_bytes(const spot_desc* d) {
+  const size_t nb = size_t(ceil_div64(d->q_len, d->block));
+  return size_t(3) * d->batch * d->hkv * nb * d->d * sizeof(float);
+}
+
+int check_workspace(size_t need, const void* ws, size_t have) {
+  if (need == 0) return SPOT_OK;
+  if (!ws || have < need) return fail(SPOT_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? have : size_t(0), need);
+  return SPOT_OK;
+}
+
+int check_indexer(const spot_desc* d) {
+  if (d->d_idx != 16 && d->d_idx != 32 && d->d_idx != 64 && d->d_idx != 128)
+    return fail(SPOT_ERR_UNSUPPORTED, "d_idx %d (supported: 16, 32, 64, 128)", d->d_idx);
+  if (d->h_idx < 1 || d->h_idx * d->d_idx > 256) return fail(SPOT_ERR_UNSUPPORTED, "h_idx*d_idx must be in [1, 256]");
+  return SPOT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spot_version(void) { return SPOT_ABI_VERSION; }
+
+const char* spot_status_string(int status) {
+  switch (status) {
+    case SPOT_OK: return "ok";
+    case SPOT_ERR_INVALID: return "invalid argument";
+    case SPOT_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SPOT_ERR_WORKSPACE: return "workspace too small";
+    case SPOT_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* spot_last_error(void) { return g_err.c_str(); }
+
+int spot_workspace_size(const spot_desc* desc, int op, size_t* bytes) {
+  if (!bytes) return fail(SPOT_ERR_INVALID, "bytes is NULL");
+  *bytes = 0;
+  int st = check_common(desc);
+  if (st) return st;
+  switch (op) {
+    case SPOT_OP_BLOCK_SCORE:
+      if (desc->score_kind == SPOT_SCORE_MEANPOOL) {
+        if ((st = check_prefill_shape(desc))) return st;
+        *bytes = meanpool_ws_bytes(desc);
+      } else if (desc->score_kind != SPOT_SCORE_RELU_INDEXER) {
+        return fail(SPOT_ERR_INVALID, "unknown score_kind %d", desc->score_kind);
+      }
+      break;
+    case SPOT_OP_SELECT_TOPP:
+    case SPOT_OP_PREFILL:
+      break;
+    case SPOT_OP_DECODE: {
+      const int nk = int(ceil_div64(desc->kv_len, desc->block));
+      const int ns = spot::decode_num_splits(desc->batch, desc->hkv, nk);
+      *bytes = spot::decode_partials_bytes(desc->batch, desc->hq, desc->d, ns);
+      break;
+    }
+    default:
+      return fail(SPOT_ERR_INVALID, "unknown op %d", op);
+  }
+  g_err.clear();
+  return SPOT_OK;
+}
+
+int spot_block_score(const spot_desc* desc, const void* q, const void* k, const int32_t* perm, const void* idx_q,
+                     const float* idx_w, const void* idx_k, float* scores, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  int st = check_common(desc);
+  if (st) return st;
+  if (!scores) return fail(SPOT_ERR_INVALID, "scores is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (desc->score_kind == SPOT_SCORE_MEANPOOL) {
+    if ((st = check_prefill_shape(desc))) return st;
+    if (!q || !k) return fail(SPOT_ERR_INVALID, "q and k are required for MEANPOOL");
+    if (perm && desc->segment <= 0) return fail(SPOT_ERR_INVALID, "perm given but segment is 0");
+    const size_t need = meanpool_ws_bytes(desc);
+    if ((st = check_workspace(need, workspace, workspace_bytes))) return st;
+    const int nb = int(ceil_div64(desc->q_len, desc->block));
+    const size_t slab = size_t(desc->batch) * desc->hkv * nb * desc->d;
+    float* ws = static_cast<float*>(workspace);
+    spot::PoolArgs pa{q, k, perm, ws, ws + slab, ws + 2 * slab, desc->dtype == SPOT_BF16, desc->batch, desc->hq,
+                      desc->hkv, desc->d, int(desc->q_len), desc->block, nb};
+    hipError_t e = spot::launch_pool_blocks(pa, s);
+    if (e != hipSuccess) return launched(e, "pool_blocks");
+    spot::MeanpoolScoreArgs sa{ws, ws + slab, perm ? ws + 2 * slab : nullptr, scores, desc->batch, desc->hkv,
+                               desc->d, nb, desc->block, desc->segment, effective_scale(desc)};
+    return launched(spot::launch_meanpool_score(sa, s), "meanpool_score");
+  }
+  if (desc->score_kind == SPOT_SCORE_RELU_INDEXER) {
+    if ((st = check_indexer(desc))) return st;
+    if (!idx_q || !idx_w || !idx_k) return fail(SPOT_ERR_INVALID, "idx_q, idx_w and idx_k are required for RELU_INDEXER");
+    const int nk = int(ceil_div64(desc->kv_len, desc->block));
+    spot::IndexerScoreArgs ia{static_cast<const uint16_t*>(idx_q), idx_w, static_cast<const uint16_t*>(idx_k), scores,
+                              desc->batch, nk, desc->h_idx, desc->d_idx};
+    return launched(spot::launch_indexer_score(ia, s), "indexer_score");
+  }
+  return fail(SPOT_ERR_INVALID, "unknown score_kind %d", desc->score_kind);
+}
+
+int spot_select_topp(const spot_desc* desc, const float* scores, int32_t* idx, int32_t* cnt, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int st = check_common(desc);
+  if (st) return st;
+  if ((st = check_selection_params(desc))) return st;
+  if (!scores || !idx || !cnt) return fail(SPOT_ERR_INVALID, "scores, idx and cnt are required");
+  const int64_t nk = ceil_div64(desc->kv_len, desc->block);
+  if (nk > spot::kSelectMaxCandidates)
+    return fail(SPOT_ERR_UNSUPPORTED, "%lld candidate blocks per row (max %d)", (long long)nk, spot::kSelectMaxCandidates);
+  spot::SelectArgs a{};
+  a.scores = scores;
+  a.idx = idx;
+  a.cnt = cnt;
+  a.nk = int(nk);
+  if (is_decode(desc)) {
+    a.nq = 1;
+    a.rows = desc->batch;
+  } else {
+    if ((st = check_prefill_shape(desc))) return st;
+    a.nq = int(nk);
+    a.rows = desc->batch * desc->hkv * int(nk);
+  }
+  a.n_sink = desc->n_sink;
+  a.n_recent = desc->n_recent;
+  a.k_min = desc->k_min;
+  a.top_p = desc->top_p;
+  return launched(spot::launch_select_topp(a, static_cast<hipStream_t>(stream)), "select_topp");
+}
+
+int spot_sparse_attn_prefill(const spot_desc* desc, const void* q, const void* k, const void* v, const int32_t* perm,
+                             const int32_t* idx, const int32_t* cnt, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int st = check_common(desc);
+  if (st) return st;
+  if ((st = check_prefill_shape(desc))) return st;
+  if (!q || !k || !v || !idx || !cnt || !o) return fail(SPOT_ERR_INVALID, "q, k, v, idx, cnt and o are required");
+  if (perm && desc->segment <= 0) return fail(SPOT_ERR_INVALID, "perm given but segment is 0");
+  const int nb = int(ceil_div64(desc->q_len, desc->block));
+  if (desc->dtype == SPOT_BF16) {
+    const int G = desc->hq / desc->hkv;
+    const long long units = (long long)desc->batch * desc->hkv * nb * ((G * desc->block + 255) / 256);
+    if (units > 0x7fffffffLL) return fail(SPOT_ERR_UNSUPPORTED, "too many work units");
+  }
+  spot::PrefillArgs a{q, k, v, perm, idx, cnt, o, lse, desc->dtype == SPOT_BF16, desc->batch, desc->hq, desc->hkv,
+                      desc->d, int(desc->q_len), desc->block, desc->segment, nb, effective_scale(desc)};
+  return launched(spot::launch_prefill(a, static_cast<hipStream_t>(stream)), "sparse_attn_prefill");
+}
+
+int spot_sparse_attn_decode(const spot_desc* desc, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* idx, const int32_t* cnt, void* o, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  int st = check_common(desc);
+  if (st) return st;
+  if (desc->q_len != 1) return fail(SPOT_ERR_INVALID, "decode needs q_len == 1");
+  if (desc->dtype != SPOT_BF16) return fail(SPOT_ERR_UNSUPPORTED, "decode supports bf16 only");
+  const int G = desc->hq / desc->hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(SPOT_ERR_UNSUPPORTED, "hq/hkv = %d (supported: 1, 2, 4, 8)", G);
+  if (!q || !k_cache || !v_cache || !idx || !cnt || !o) return fail(SPOT_ERR_INVALID, "q, k_cache, v_cache, idx, cnt and o are required");
+  const int nk = int(ceil_div64(desc->kv_len, desc->block));
+  const int ns = spot::decode_num_splits(desc->batch, desc->hkv, nk);
+  const size_t need = spot::decode_partials_bytes(desc->batch, desc->hq, desc->d, ns);
+  if ((st = check_workspace(need, workspace, workspace_bytes))) return st;
+  spot::DecodeArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+                     static_cast<const uint16_t*>(v_cache), idx, cnt, static_cast<uint16_t*>(o), lse,
+                     static_cast<float*>(workspace), desc->batch, desc->hq, desc->hkv, desc->d, int(desc->kv_len),
+                     desc->block, nk, ns, effective_scale(desc)};
+  return launched(spot::launch_decode(a, static_cast<hipStream_t>(stream)), "sparse_attn_decode");
+}
+
+}  // extern "C"

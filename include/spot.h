@@ -1,0 +1,174 @@
+/*
+ * spot.h - C ABI of the block-sparse causal attention library (libspot.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The library implements one hot path, in four calls:
+ *
+ *   spot_block_score         score every (query block, key block) pair
+ *   spot_select_topp         keep blocks by cumulative-mass top-p
+ *   spot_sparse_attn_prefill online-softmax attention over the kept blocks (GQA prefill)
+ *   spot_sparse_attn_decode  the same for one decode query per sequence
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Ownership.  Every tensor pointer is caller-owned DEVICE memory.  The library
+ *   never allocates, frees or synchronises; each call only enqueues kernels on
+ *   `stream` (a hipStream_t; NULL means the null stream) and returns.  Scratch
+ *   memory is a caller-provided workspace whose size spot_workspace_size reports.
+ * Layouts (all contiguous, row-major):
+ *   Q, O            [batch, hq,  q_len,  d]
+ *   K, V            [batch, hkv, kv_len, d]
+ *   perm            int32 [batch, hkv, q_len]   logical -> physical key row
+ *   scores          float [batch, hsel, nq, nk]
+ *   idx             int32 [batch, hsel, nq, nk] kept block ids, ascending, -1 padded
+ *   cnt             int32 [batch, hsel, nq]     number of kept blocks
+ *   idx_q (q^I)     bf16  [batch, h_idx, d_idx]
+ *   idx_w (w)       float [batch, h_idx]
+ *   idx_k (K^I)     bf16  [batch, nk, h_idx, d_idx]
+ *   lse             float [batch, hq, q_len]    natural-log sum of exp of the logits
+ *   with nk = ceil(kv_len / block); for prefill nq = nk, hsel = hkv; for decode
+ *   nq = 1, hsel = 1 (one list per sequence, shared by all heads).
+ * dtype.  SPOT_F32 or SPOT_BF16 for Q, K, V and O (O takes Q's dtype).
+ *   Scores, lse and all accumulation are fp32.
+ * Errors.  Every call returns SPOT_OK (0) or a negative status; arguments are
+ *   validated on the host before anything is launched, so a failed call
+ *   enqueues nothing.  spot_last_error() gives a thread-local message.
+ *   A launch failure reported by the HIP runtime returns SPOT_ERR_LAUNCH.
+ * State.  None across calls; the library is thread-safe.
+ *
+ * Sources (titles of the summarised papers):
+ *   [Spot] SpotAttention: Plug-In Block-Sparse Routing for Pretrained
+ *          Long-Context Transformers
+ *   [PBS]  PBS-Attn, "Sparsere Blok-Sparse Attention via Tokenpermutatie"
+ *   [S2O]  "S2O - Vroege Stoppering voor Sparse Attention via Online Permutatie"
+ */
+#ifndef SPOT_H
+#define SPOT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPOT_ABI_VERSION 1
+
+enum spot_status {
+  SPOT_OK = 0,
+  SPOT_ERR_INVALID = -1,      /* null required pointer, inconsistent sizes, bad parameter */
+  SPOT_ERR_UNSUPPORTED = -2,  /* valid but outside the built kernels (dtype, d, block, length) */
+  SPOT_ERR_WORKSPACE = -3,    /* workspace smaller than spot_workspace_size reports */
+  SPOT_ERR_LAUNCH = -4        /* the HIP runtime rejected a kernel launch */
+};
+
+enum spot_dtype { SPOT_F32 = 0, SPOT_BF16 = 1 };
+
+enum spot_score_kind {
+  SPOT_SCORE_MEANPOOL = 0,     /* prefill: sm_scale * <mean q, mean k>           ([PBS] §4) */
+  SPOT_SCORE_RELU_INDEXER = 1  /* decode: sum_h w_h ReLU(q^I_h . k^I_{h,t})       ([Spot] §1) */
+};
+
+enum spot_op {
+  SPOT_OP_BLOCK_SCORE = 0,
+  SPOT_OP_SELECT_TOPP = 1,
+  SPOT_OP_PREFILL = 2,
+  SPOT_OP_DECODE = 3
+};
+
+/* Problem descriptor.  `version` must be SPOT_ABI_VERSION. */
+typedef struct spot_desc {
+  int32_t version;
+  int32_t dtype;                  /* enum spot_dtype */
+  int32_t batch, hq, hkv, d;      /* hq % hkv == 0; d in {64, 128} */
+  int64_t q_len, kv_len;          /* prefill: q_len == kv_len == L; decode: q_len == 1, kv_len == T */
+  int32_t block;                  /* B in {16, 32, 64, 128}: query and key block size */
+  int32_t segment;                /* S, a multiple of B, when a permutation is used; else 0 */
+  int32_t n_sink, n_recent;       /* forced blocks: the first n_sink and the last n_recent (>= 1 together) */
+  int32_t k_min;                  /* floor on the number of residual blocks kept */
+  float top_p;                    /* >= 1 keeps every candidate; <= 0 keeps the forced blocks only */
+  float sm_scale;                 /* softmax scale; 0 selects 1/sqrt(d) */
+  int32_t score_kind;             /* enum spot_score_kind */
+  int32_t h_idx, d_idx;           /* indexer heads and width (RELU_INDEXER) */
+} spot_desc;
+
+/* Library version (SPOT_ABI_VERSION). */
+int spot_version(void);
+
+/* Text for a status code (static storage). */
+const char* spot_status_string(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* spot_last_error(void);
+
+/* Workspace bytes that `op` needs for `desc` (0 is possible).  Host only. */
+int spot_workspace_size(const spot_desc* desc, int op, size_t* bytes);
+
+/*
+ * Block scores.
+ *
+ * MEANPOOL (prefill, [PBS] §4; scale as attention): for KV head g, query
+ * block i and key block j <= i
+ *     scores[b,g,i,j] = sm_scale * < qbar[g,i], kbar[g,j] >
+ *   qbar[g,i] = mean of Q over the G = hq/hkv heads of group g and the rows of
+ *   block i; kbar[g,j] = mean of the K rows of block j, taken through `perm`
+ *   (rows perm[b,g,t], t in block j) when perm != NULL and block j lies in an
+ *   earlier segment than block i, else in natural order.  j > i gets -inf.
+ *   Uses q, k, perm (nullable); idx_q, idx_w, idx_k must be NULL or are ignored.
+ *   Workspace: the pooled means (spot_workspace_size).
+ *
+ * RELU_INDEXER (decode, [Spot] §1 scoring equation): for sequence b and key
+ * block t < nk
+ *     scores[b,0,0,t] = sum_h idx_w[b,h] * max(0, < idx_q[b,h], idx_k[b,t,h] >)
+ *   Uses idx_q, idx_w, idx_k; q, k, perm are ignored.
+ */
+int spot_block_score(const spot_desc* desc, const void* q, const void* k, const int32_t* perm,
+                     const void* idx_q, const float* idx_w, const void* idx_k, float* scores,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Dual top-p selection ([Spot] §3), one row per (b, g, i) (prefill) or per b
+ * (decode).  Candidates are key blocks 0..i (prefill) or 0..nk-1 (decode).
+ * Forced: j < n_sink and j > last - n_recent (last = i, or nk-1).  The
+ * residual candidates are ordered by (score desc, block id asc); their
+ * softmax masses are accumulated (fp64) until the sum reaches top_p
+ * (inclusive); at least min(k_min, #residual) are kept; top_p >= 1 keeps all.
+ * Output: kept ids ascending in idx, padded with -1 to nk, count in cnt.
+ * Rows longer than 16384 candidates are unsupported.
+ */
+int spot_select_topp(const spot_desc* desc, const float* scores, int32_t* idx, int32_t* cnt,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sparse prefill attention ([PBS] Problem and §2, [S2O] §1 and §3).
+ * For query head h (group g = h / G) and row r of query block i:
+ *     O[b,h,r] = sum_t softmax_t(sm_scale * q.k_t) v_t
+ * over the keys of the kept blocks idx[b,g,i,0..cnt): a block of an earlier
+ * segment contributes rows perm[b,g,t] (t in the block), all visible; a block
+ * of the query's own segment (or every block when perm == NULL) contributes
+ * its natural rows t <= r.  lse (nullable) receives ln(sum exp(logits)).
+ * Kept lists must be ascending, with block ids < nk; every row must see at
+ * least one key (guaranteed when the diagonal or block 0 is kept).
+ */
+int spot_sparse_attn_prefill(const spot_desc* desc, const void* q, const void* k, const void* v,
+                             const int32_t* perm, const int32_t* idx, const int32_t* cnt, void* o,
+                             float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sparse decode attention ([Spot] Problem and §3 at decode time): one query
+ * per (sequence b, head h) at position kv_len - 1 attends every key of the
+ * kept blocks idx[b,0,0,0..cnt) (shared by all heads; all visible).
+ * q: [batch, hq, d]; k_cache, v_cache: [batch, hkv, kv_len, d];
+ * o: [batch, hq, d]; lse (nullable): [batch, hq].
+ * Work is split over the kept list; partial (max, sum, accumulator) triples go
+ * to the workspace and are merged in a fixed order (deterministic).
+ */
+int spot_sparse_attn_decode(const spot_desc* desc, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* idx, const int32_t* cnt, void* o,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPOT_H */

@@ -1,0 +1,162 @@
+"""C ABI boundary on the CPU: the library loads, exports every function
+include/spot.h declares, and every validation path returns its documented
+status before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "spot.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(spot_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_entry_points_and_helpers():
+    names = header_functions()
+    for n in ("spot_block_score", "spot_select_topp", "spot_sparse_attn_prefill", "spot_sparse_attn_decode",
+              "spot_workspace_size", "spot_status_string", "spot_last_error", "spot_version"):
+        assert n in names
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load_library()
+    for n in header_functions():
+        assert hasattr(lib, n), n
+    assert B.spot_version() == B.ABI_VERSION
+
+
+def test_descriptor_layout_matches_header():
+    # int32 x6, int64 x2, int32 x5, float x2, int32 x3 -> 80 bytes with natural alignment
+    assert ctypes.sizeof(B.spot_desc) == 80
+    assert B.spot_desc.q_len.offset == 24 and B.spot_desc.top_p.offset == 60
+
+
+def test_status_strings():
+    lib = B.load_library()
+    for st in (0, -1, -2, -3, -4):
+        assert lib.spot_status_string(st)
+    assert lib.spot_status_string(7) == b"unknown status"
+
+
+def _prefill(**kw):
+    base = dict(dtype=B.SPOT_BF16, batch=1, hq=8, hkv=2, d=128, q_len=1024, kv_len=1024, block=64, top_p=0.9)
+    base.update(kw)
+    return B.make_desc(**base)
+
+
+def _decode(**kw):
+    base = dict(dtype=B.SPOT_BF16, batch=2, hq=8, hkv=2, d=128, q_len=1, kv_len=4096, block=16, top_p=0.9,
+                score_kind=B.SPOT_SCORE_RELU_INDEXER, h_idx=4, d_idx=64)
+    base.update(kw)
+    return B.make_desc(**base)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def call_score(d, ws_bytes=1 << 30, q=FAKE, k=FAKE, perm=None, iq=None, iw=None, ik=None, scores=FAKE, ws=FAKE):
+    lib = B.load_library()
+    return lib.spot_block_score(ctypes.byref(d) if d is not None else None, q, k, perm, iq, iw, ik, scores, ws,
+                                ws_bytes, None)
+
+
+def call_select(d, scores=FAKE, idx=FAKE, cnt=FAKE):
+    return B.load_library().spot_select_topp(ctypes.byref(d), scores, idx, cnt, None, 0, None)
+
+
+def call_prefill(d, q=FAKE, k=FAKE, v=FAKE, perm=None, idx=FAKE, cnt=FAKE, o=FAKE):
+    return B.load_library().spot_sparse_attn_prefill(ctypes.byref(d), q, k, v, perm, idx, cnt, o, None, None, 0, None)
+
+
+def call_decode(d, ws=FAKE, ws_bytes=1 << 30, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cnt=FAKE, o=FAKE):
+    return B.load_library().spot_sparse_attn_decode(ctypes.byref(d), q, k, v, idx, cnt, o, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(version=2), B.SPOT_ERR_INVALID),
+    (dict(dtype=7), B.SPOT_ERR_INVALID),
+    (dict(batch=0), B.SPOT_ERR_INVALID),
+    (dict(hq=6, hkv=4), B.SPOT_ERR_INVALID),
+    (dict(d=96), B.SPOT_ERR_UNSUPPORTED),
+    (dict(block=48), B.SPOT_ERR_UNSUPPORTED),
+    (dict(block=256), B.SPOT_ERR_UNSUPPORTED),
+    (dict(q_len=0, kv_len=0), B.SPOT_ERR_INVALID),
+    (dict(kv_len=1000), B.SPOT_ERR_INVALID),            # prefill needs q_len == kv_len
+    (dict(segment=100), B.SPOT_ERR_INVALID),            # not a multiple of the block
+    (dict(segment=-64), B.SPOT_ERR_INVALID),
+    (dict(sm_scale=-1.0), B.SPOT_ERR_INVALID),
+    (dict(sm_scale=float("inf")), B.SPOT_ERR_INVALID),
+])
+def test_common_validation(case, expect):
+    case = dict(case)
+    version = case.pop("version", None)
+    d = _prefill(**case)
+    if version is not None:
+        d.version = version
+    assert call_score(d) == expect
+    assert B.load_library().spot_last_error()
+
+
+def test_null_and_missing_arguments():
+    assert call_score(None) == B.SPOT_ERR_INVALID
+    assert call_score(_prefill(), q=None) == B.SPOT_ERR_INVALID
+    assert call_score(_prefill(), scores=None) == B.SPOT_ERR_INVALID
+    assert call_score(_prefill(), perm=FAKE) == B.SPOT_ERR_INVALID          # perm without a segment
+    assert call_score(_prefill(), ws=None) == B.SPOT_ERR_WORKSPACE
+    assert call_score(_prefill(), ws_bytes=100) == B.SPOT_ERR_WORKSPACE
+    assert call_score(_prefill(score_kind=9)) == B.SPOT_ERR_INVALID
+    assert call_prefill(_prefill(), v=None) == B.SPOT_ERR_INVALID
+    assert call_prefill(_prefill(), perm=FAKE) == B.SPOT_ERR_INVALID
+    assert call_prefill(_prefill(), o=None) == B.SPOT_ERR_INVALID
+    assert call_select(_prefill(), cnt=None) == B.SPOT_ERR_INVALID
+
+
+def test_selection_parameters():
+    assert call_select(_prefill(n_sink=0, n_recent=0)) == B.SPOT_ERR_INVALID
+    assert call_select(_prefill(n_sink=-1)) == B.SPOT_ERR_INVALID
+    assert call_select(_prefill(k_min=-2)) == B.SPOT_ERR_INVALID
+    assert call_select(_prefill(top_p=float("nan"))) == B.SPOT_ERR_INVALID
+    # too many candidate blocks for one row
+    assert call_select(_prefill(q_len=16 * 20000, kv_len=16 * 20000, block=16)) == B.SPOT_ERR_UNSUPPORTED
+
+
+def test_indexer_and_decode_validation():
+    assert call_score(_decode(), q=None, k=None) == B.SPOT_ERR_INVALID                 # idx_* missing
+    assert call_score(_decode(d_idx=48), iq=FAKE, iw=FAKE, ik=FAKE) == B.SPOT_ERR_UNSUPPORTED
+    assert call_score(_decode(h_idx=8, d_idx=64), iq=FAKE, iw=FAKE, ik=FAKE) == B.SPOT_ERR_UNSUPPORTED
+    assert call_decode(_decode(q_len=2)) == B.SPOT_ERR_INVALID
+    assert call_decode(_decode(dtype=B.SPOT_F32)) == B.SPOT_ERR_UNSUPPORTED
+    assert call_decode(_decode(hq=12, hkv=4)) == B.SPOT_ERR_UNSUPPORTED                 # G = 3
+    assert call_decode(_decode(), ws=None) == B.SPOT_ERR_WORKSPACE
+    assert call_decode(_decode(), ws_bytes=8) == B.SPOT_ERR_WORKSPACE
+    assert call_decode(_decode(), o=None) == B.SPOT_ERR_INVALID
+
+
+def test_workspace_sizes():
+    d = _prefill()
+    assert B.spot_workspace_size(d, B.SPOT_OP_BLOCK_SCORE) == 3 * 1 * 2 * 16 * 128 * 4
+    assert B.spot_workspace_size(d, B.SPOT_OP_SELECT_TOPP) == 0
+    assert B.spot_workspace_size(d, B.SPOT_OP_PREFILL) == 0
+    dd = _decode()
+    assert B.spot_workspace_size(dd, B.SPOT_OP_DECODE) > 0
+    assert B.spot_workspace_size(_decode(), B.SPOT_OP_BLOCK_SCORE) == 0
+    with pytest.raises(B.SpotError):
+        B.spot_workspace_size(d, 17)
+    with pytest.raises(B.SpotError):
+        B.spot_workspace_size(_prefill(d=80), B.SPOT_OP_BLOCK_SCORE)
+
+
+def test_error_message_is_thread_local_and_cleared():
+    lib = B.load_library()
+    assert call_score(None) == B.SPOT_ERR_INVALID
+    assert lib.spot_last_error() == b"desc is NULL"
+    B.spot_workspace_size(_prefill(), B.SPOT_OP_PREFILL)
+    assert lib.spot_last_error() == b""
