@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--cpu-sample-blocks", type=int, default=12)
+    ap.add_argument("--cpu-sample-blocks", type=int, default=0, help="0: every query block")
     return ap.parse_args()
 
 
@@ -208,8 +208,11 @@ def cpu_baseline(res, I, sample_blocks: int):
         threads = 1
     cfg = res["cfg"]
     q, k, v = res["host"]
-    rng = np.random.default_rng([cfg.seed, 1234])
-    blocks = sorted({cfg.nb - 1} | set(rng.choice(cfg.nb, sample_blocks - 1, replace=False).tolist()))
+    if sample_blocks <= 0 or sample_blocks >= cfg.nb:
+        blocks = list(range(cfg.nb))
+    else:
+        rng = np.random.default_rng([cfg.seed, 1234])
+        blocks = sorted({cfg.nb - 1} | set(rng.choice(cfg.nb, sample_blocks - 1, replace=False).tolist()))
     scale = 1 / math.sqrt(cfg.d)
     t0 = time.time()
     out = oracle.prefill(q[0], k[0], v[0], cfg.block, cfg.top_p, qblocks=blocks)

@@ -33,24 +33,27 @@ namespace spot {
 
 constexpr int kKT = 64;          // key slots per tile
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr uint32_t kOnes = 0x3F803F80u;    // bf16 pair (1, 1)
 
 struct SlotMap {
   const int32_t* list;   // kept block ids of this (b, g, i)
   const int32_t* permg;  // perm row of (b, g) or nullptr
-  int nkept, B, L, S, seg_i;
+  int nkept, lgB, L;
+  int seg_start;         // first position of the query block's segment; 0 without a permutation
 
-  // physical row and mask limit of kept slot s: lim = -1 (history, always
-  // visible), the logical position (own segment: visible iff <= query row),
-  // or INT_MAX (no key: beyond the list or beyond L)
-  __device__ __forceinline__ void at(int s, int& phys, int& lim) const {
-    const int bi = s / B;
-    if (bi >= nkept) { phys = 0; lim = 0x7fffffff; return; }
-    const int j = list[bi];
-    const int pos = j * B + (s - bi * B);
-    if (pos >= L) { phys = 0; lim = 0x7fffffff; return; }
-    if (permg && (j * B) / S < seg_i) { phys = permg[pos]; lim = -1; }
-    else { phys = pos; lim = pos; }
+  // Logical position of kept slot s (requires nkept >= 1), whether its block
+  // lies in an earlier segment (read through the permutation, always
+  // visible; otherwise natural row, visible iff <= the query row), and
+  // whether s is inside the kept list at all.  Slots with pos >= L are empty.
+  __device__ __forceinline__ void at(int s, int& pos, bool& hist, bool& inlist) const {
+    const int bi = s >> lgB;
+    inlist = bi < nkept;
+    const int j = list[inlist ? bi : 0];
+    const int base = j << lgB;
+    pos = base + (s & ((1 << lgB) - 1));
+    hist = base < seg_start;
   }
+  __device__ __forceinline__ int phys_of(int pos, bool hist) const { return hist ? permg[pos] : pos; }
 };
 
 __device__ __forceinline__ void unit_of(int w, int pairs, int nb, int chunks, int& pair, int& i, int& chunk) {
@@ -116,10 +119,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
   sm.list = a.idx + row_id * a.nb;
   sm.nkept = a.cnt[row_id];
   sm.permg = a.perm ? a.perm + size_t(pair) * L : nullptr;
-  sm.B = B;
+  sm.lgB = 31 - __builtin_clz(B);
   sm.L = L;
-  sm.S = a.segment > 0 ? a.segment : 1;
-  sm.seg_i = a.segment > 0 ? (i * B) / a.segment : 0;
+  sm.seg_start = (a.perm && a.segment > 0) ? ((i * B) / a.segment) * a.segment : 0;
   const int total = sm.nkept * B;
   const int ntiles = (total + kKT - 1) / kKT;
   const int last_block_start = (sm.nkept - 1) * B;
@@ -134,28 +136,32 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
     for (int c = 0; c < CK; ++c) {
       const int cid = tid + c * NT;
       const int row = cid / (D / 8), col8 = cid % (D / 8);
-      int phys, lim;
-      sm.at(s0 + row, phys, lim);
-      kreg[c] = (cid < kKT * D / 8 && lim != 0x7fffffff)
-                    ? *reinterpret_cast<const uint4*>(Kg + size_t(phys) * D + col8 * 8)
-                    : make_uint4(0u, 0u, 0u, 0u);
+      int pos;
+      bool hist, inl;
+      sm.at(s0 + row, pos, hist, inl);
+      const bool ok = cid < kKT * D / 8 && inl && pos < L;
+      kreg[c] = make_uint4(0u, 0u, 0u, 0u);
+      if (ok) kreg[c] = *reinterpret_cast<const uint4*>(Kg + size_t(sm.phys_of(pos, hist)) * D + col8 * 8);
     }
 #pragma unroll
     for (int c = 0; c < CV; ++c) {
       const int vb = tid + c * NT;
       const int dg = vb % (D / 4), kq = vb / (D / 4);
+      int pos;
+      bool hist, inl;
+      sm.at(s0 + 4 * kq, pos, hist, inl);   // 4 consecutive slots of one block (B >= 4)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        int phys, lim;
-        sm.at(s0 + 4 * kq + rr, phys, lim);
-        vreg[c][rr] = (vb < NVB && lim != 0x7fffffff)
-                          ? *reinterpret_cast<const uint2*>(Vg + size_t(phys) * D + dg * 4)
-                          : make_uint2(0u, 0u);
+        const bool ok = vb < NVB && inl && pos + rr < L;
+        vreg[c][rr] = make_uint2(0u, 0u);
+        if (ok) vreg[c][rr] = *reinterpret_cast<const uint2*>(Vg + size_t(sm.phys_of(pos + rr, hist)) * D + dg * 4);
       }
     }
     if (tid < kKT) {
-      int phys;
-      sm.at(s0 + tid, phys, kp_lim);
+      int pos;
+      bool hist, inl;
+      sm.at(s0 + tid, pos, hist, inl);
+      kp_lim = (inl && pos < L) ? (hist ? -1 : pos) : 0x7fffffff;
     }
   };
 
@@ -257,16 +263,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
       m_run = m_new;
     }
     const float msub = (m_run == -kInf) ? 0.f : m_run;
-    float rs = 0.f;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[rt][e], scale_log2, -msub));
-        sacc[rt][e] = p;
-        rs += p;
-      }
-    l_run += rs;
+      for (int e = 0; e < 16; ++e) sacc[rt][e] = __builtin_amdgcn_exp2f(fmaf(sacc[rt][e], scale_log2, -msub));
+    float rs = 0.f;   // row sum of the bf16-rounded P that enters the PV product
 
     // O^T += V^T P^T over 4 k-steps of 16 keys
 #pragma unroll
@@ -278,6 +279,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
       pp.z = pack_bf16x2(sacc[rt][hb + 4], sacc[rt][hb + 5]);
       pp.w = pack_bf16x2(sacc[rt][hb + 6], sacc[rt][hb + 7]);
       const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pp);
+      rs = dot2_bf16(pp.x, kOnes, dot2_bf16(pp.y, kOnes, dot2_bf16(pp.z, kOnes, dot2_bf16(pp.w, kOnes, rs))));
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const uint16_t* vrow = &Vt[buf][(dt * 32 + ql) * VLD + kk * 16 + 4 * hf];
@@ -287,6 +289,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[dt], 0, 0, 0);
       }
     }
+
+    l_run += rs;
 
     if (t + 1 < ntiles) store_tile(buf ^ 1);
     __syncthreads();
@@ -340,19 +344,21 @@ __global__ __launch_bounds__(256) void prefill_rows_kernel(PrefillArgs a, float 
   sm.list = a.idx + row_id * a.nb;
   sm.nkept = a.cnt[row_id];
   sm.permg = a.perm ? a.perm + size_t(pair) * L : nullptr;
-  sm.B = B;
+  sm.lgB = 31 - __builtin_clz(B);
   sm.L = L;
-  sm.S = a.segment > 0 ? a.segment : 1;
-  sm.seg_i = a.segment > 0 ? (i * B) / a.segment : 0;
+  sm.seg_start = (a.perm && a.segment > 0) ? ((i * B) / a.segment) * a.segment : 0;
   const int total = sm.nkept * B;
 
   float m = -kInf, l = 0.f, acc[DU];
 #pragma unroll
   for (int u = 0; u < DU; ++u) acc[u] = 0.f;
   for (int s0 = 0; s0 < total; s0 += 64) {
-    int phys, lim;
-    sm.at(s0 + lane, phys, lim);
-    const bool vis = lim <= r;
+    int pos;
+    bool hist, inl;
+    sm.at(s0 + lane, pos, hist, inl);
+    const bool valid = inl && pos < L;
+    const bool vis = valid && (hist || pos <= r);
+    const int phys = vis ? sm.phys_of(pos, hist) : 0;
     float x = -kInf;
     if (vis) {
       const T* krow = K + size_t(phys) * D;

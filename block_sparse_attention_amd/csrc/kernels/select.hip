@@ -2,157 +2,242 @@
 // Selectieregel"): reserved sink and recency blocks, nucleus selection on the
 // residual distribution until the cumulative mass reaches p, floor K_min.
 //
-// One workgroup per row.  The residual candidates are sorted in LDS (bitonic
-// network on 64-bit keys: inverted order-preserving score bits above the
-// block id, so ascending keys are score-descending with ties to the lower id),
-// their softmax masses are prefix-summed in fp64, the crossing index is found,
-// and the kept set is compacted to ascending block ids.
+// One workgroup per row; each thread owns a contiguous run of candidate ids.
+// Instead of sorting, the kernel searches the cutoff directly: with
+// key(s) = order-preserving bits of the score, the kept residual set of the
+// rule (scores descending, ties to the lower block id, shortest prefix whose
+// mass reaches p) is {key > K} plus the first m candidates with key == K in
+// id order, where K is the largest key whose upper set {key >= K} still holds
+// mass >= p.  K is found by binary search over the 32-bit key space; every
+// mass is a fixed-order fp64 reduction (per-thread runs, then wave
+// butterflies, then waves in order), so the result is deterministic.
 #include "../launch.h"
 #include "common.h"
 
 namespace spot {
 
-__device__ __forceinline__ uint32_t score_desc_bits(float s) {
+constexpr int kSelMaxPerThread = 16;   // candidates per thread (16384 / 1024)
+
+__device__ __forceinline__ uint32_t score_key(float s) {
   const uint32_t u = __float_as_uint(s);
-  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ~asc;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Block-wide exclusive scan of one value per thread (blockDim.x <= 1024).
-template <typename V>
-__device__ V block_exclusive_scan(V x, V* buf, V& total) {
-  const int t = threadIdx.x, n = blockDim.x;
-  buf[t] = x;
+struct SelScratch {
+  double d[32];
+  int i[32];
+  uint32_t u[32];
+  float f[32];
+};
+
+__device__ double block_sum_f64(double x, SelScratch& sc) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  if (lane == 0) sc.d[w] = x;
   __syncthreads();
-  for (int o = 1; o < n; o <<= 1) {
-    V y = (t >= o) ? buf[t - o] : V(0);
-    __syncthreads();
-    buf[t] += y;
-    __syncthreads();
+  double t = 0.0;
+  for (int k = 0; k < nw; ++k) t += sc.d[k];
+  __syncthreads();
+  return t;
+}
+
+__device__ int block_sum_i32(int x, SelScratch& sc) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  if (lane == 0) sc.i[w] = x;
+  __syncthreads();
+  int t = 0;
+  for (int k = 0; k < nw; ++k) t += sc.i[k];
+  __syncthreads();
+  return t;
+}
+
+__device__ float block_max_f32(float x, SelScratch& sc) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  x = wave_max(x);
+  if (lane == 0) sc.f[w] = x;
+  __syncthreads();
+  float t = -kInf;
+  for (int k = 0; k < nw; ++k) t = fmaxf(t, sc.f[k]);
+  __syncthreads();
+  return t;
+}
+
+// exclusive prefix (in thread order) of one int per thread, plus the total
+__device__ int block_excl_scan_i32(int x, SelScratch& sc, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
   }
-  const V incl = buf[t];
-  total = buf[n - 1];
+  if (lane == 63) sc.i[w] = incl;
   __syncthreads();
-  return incl - x;
+  int before = 0, tot = 0;
+  for (int k = 0; k < nw; ++k) {
+    if (k < w) before += sc.i[k];
+    tot += sc.i[k];
+  }
+  __syncthreads();
+  total = tot;
+  return before + incl - x;
 }
 
 __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
-  extern __shared__ unsigned char lds[];
+  __shared__ SelScratch sc;
   const int nk = a.nk;
   const int row = blockIdx.x;
   const int tid = threadIdx.x, nthr = blockDim.x;
   const bool decode = a.nq == 1;
-  const int n = decode ? nk : (row % a.nq) + 1;  // candidates 0..n-1
+  const int n = decode ? nk : (row % a.nq) + 1;   // candidates 0..n-1
   const int last = n - 1;
-  int sort_n = 2;
-  while (sort_n < n) sort_n <<= 1;
-
-  int cap = 2;
-  while (cap < nk) cap <<= 1;
-  uint64_t* keys = reinterpret_cast<uint64_t*>(lds);                       // [cap >= sort_n]
-  double* scan = reinterpret_cast<double*>(lds + sizeof(uint64_t) * cap);  // [1024]
-  uint8_t* flag = reinterpret_cast<uint8_t*>(scan + 1024);                 // [nk]
-  __shared__ int s_kstar;
-
+  const int per = (n + nthr - 1) / nthr;          // <= kSelMaxPerThread
+  const int c0 = min(tid * per, n);
   const float* srow = a.scores + size_t(row) * nk;
-  auto forced = [&](int c) { return c < a.n_sink || c > last - a.n_recent; };
 
-  for (int c = tid; c < sort_n; c += nthr) {
-    uint64_t key = ~0ull;
-    if (c < n && !forced(c)) key = (uint64_t(score_desc_bits(srow[c])) << 32) | uint32_t(c);
-    keys[c] = key;
-  }
-  for (int c = tid; c < nk; c += nthr) flag[c] = (c < n && forced(c)) ? 1 : 0;
-  int n_forced = 0;
-  {
-    // |{c < n : c < n_sink or c > last - n_recent}|
-    const int lo = min(max(a.n_sink, 0), n);
-    const int hi_start = max(last - a.n_recent + 1, 0);
-    const int hi = n - max(hi_start, lo);
-    n_forced = lo + max(hi, 0);
-  }
-  const int n_res = n - n_forced;
-  __syncthreads();
-
-  // bitonic sort, ascending
-  for (int k = 2; k <= sort_n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int e = tid; e < sort_n; e += nthr) {
-        const int p = e ^ j;
-        if (p > e) {
-          const uint64_t x = keys[e], y = keys[p];
-          const bool up = (e & k) == 0;
-          if ((x > y) == up) {
-            keys[e] = y;
-            keys[p] = x;
-          }
-        }
+  // this thread's run: candidate c0 + e, e < per
+  uint32_t key[kSelMaxPerThread];
+  double ex[kSelMaxPerThread];
+  uint32_t resid = 0, forcedm = 0;   // bit masks over the run
+  float smax = -kInf;
+#pragma unroll
+  for (int e = 0; e < kSelMaxPerThread; ++e) {
+    key[e] = 0u;
+    ex[e] = 0.0;
+    const int c = c0 + e;
+    if (e < per && c < n) {
+      const bool f = c < a.n_sink || c > last - a.n_recent;
+      if (f) {
+        forcedm |= 1u << e;
+      } else {
+        const float s = srow[c];
+        resid |= 1u << e;
+        key[e] = score_key(s);
+        smax = fmaxf(smax, s);
       }
-      __syncthreads();
     }
   }
+  const int n_res = block_sum_i32(__popc(resid), sc);
 
-  int kstar;
+  // kept residual: key > kcut, plus the first mtie candidates with key == kcut
+  uint32_t kcut = 0u;
+  int mtie = 0;
+  bool keep_all = false, keep_none = false;
   if (a.top_p >= 1.0f) {
-    kstar = n_res;
-  } else if (a.top_p <= 0.0f || n_res == 0) {
-    kstar = 0;
+    keep_all = true;
   } else {
-    // masses exp(s_k - s_top) in sorted order, prefix sums in fp64
-    const double s_top = double(srow[uint32_t(keys[0])]);
-    const int per = (n_res + nthr - 1) / nthr;
-    const int k0 = min(tid * per, n_res), k1 = min(k0 + per, n_res);
-    double local = 0.0;
-    for (int kk = k0; kk < k1; ++kk) local += exp(double(srow[uint32_t(keys[kk])]) - s_top);
-    double total;
-    const double before = block_exclusive_scan<double>(local, scan, total);
-    if (tid == 0) s_kstar = n_res;
-    __syncthreads();
-    const double target = double(a.top_p) * total;
-    double c = before;
-    for (int kk = k0; kk < k1; ++kk) {
-      const double prev = c;
-      c += exp(double(srow[uint32_t(keys[kk])]) - s_top);
-      if (c >= target && !(prev >= target)) atomicMin(&s_kstar, kk + 1);
+    int kstar = 0;
+    if (a.top_p > 0.0f && n_res > 0) {
+      const float gmax = block_max_f32(smax, sc);
+      double local = 0.0;
+#pragma unroll
+      for (int e = 0; e < kSelMaxPerThread; ++e)
+        if (resid & (1u << e)) {
+          ex[e] = double(__expf(key_score(key[e]) - gmax));
+          local += ex[e];
+        }
+      const double z = block_sum_f64(local, sc);
+      const double target = double(a.top_p) * z;
+      // largest K with mass(key >= K) >= target (K = 0 always qualifies)
+      uint32_t lo = 0u, hi = 0xffffffffu;
+      while (lo < hi) {
+        const uint32_t mid = lo + ((hi - lo) >> 1) + 1u;
+        double part = 0.0;
+#pragma unroll
+        for (int e = 0; e < kSelMaxPerThread; ++e)
+          if ((resid & (1u << e)) && key[e] >= mid) part += ex[e];
+        if (block_sum_f64(part, sc) >= target) lo = mid;
+        else hi = mid - 1u;
+      }
+      kcut = lo;
+      double above = 0.0;
+      int n_above = 0, n_tie = 0;
+#pragma unroll
+      for (int e = 0; e < kSelMaxPerThread; ++e)
+        if (resid & (1u << e)) {
+          if (key[e] > kcut) { above += ex[e]; ++n_above; }
+          else if (key[e] == kcut) ++n_tie;
+        }
+      above = block_sum_f64(above, sc);
+      n_above = block_sum_i32(n_above, sc);
+      n_tie = block_sum_i32(n_tie, sc);
+      // ties share one mass; take the fewest (in id order) that reach the target
+      const double e_tie = double(__expf(key_score(kcut) - gmax));
+      const double need = ceil((target - above) / e_tie);
+      mtie = need < 1.0 ? 1 : (need > double(n_tie) ? n_tie : int(need));
+      kstar = n_above + mtie;
     }
-    __syncthreads();
-    kstar = s_kstar;
+    const int kfloor = min(a.k_min, n_res);
+    if (kstar < kfloor) {
+      // floor K_min: largest K with count(key >= K) >= kfloor, ties by id
+      uint32_t lo = 0u, hi = 0xffffffffu;
+      while (lo < hi) {
+        const uint32_t mid = lo + ((hi - lo) >> 1) + 1u;
+        int part = 0;
+#pragma unroll
+        for (int e = 0; e < kSelMaxPerThread; ++e)
+          if ((resid & (1u << e)) && key[e] >= mid) ++part;
+        if (block_sum_i32(part, sc) >= kfloor) lo = mid;
+        else hi = mid - 1u;
+      }
+      kcut = lo;
+      int n_above = 0;
+#pragma unroll
+      for (int e = 0; e < kSelMaxPerThread; ++e)
+        if ((resid & (1u << e)) && key[e] > kcut) ++n_above;
+      n_above = block_sum_i32(n_above, sc);
+      mtie = kfloor - n_above;
+      kstar = kfloor;
+    }
+    keep_none = kstar == 0;
   }
-  kstar = max(kstar, min(a.k_min, n_res));
 
-  for (int kk = tid; kk < kstar; kk += nthr) flag[uint32_t(keys[kk])] = 1;
-  __syncthreads();
+  // rank of this thread's ties in id order
+  int my_ties = 0;
+#pragma unroll
+  for (int e = 0; e < kSelMaxPerThread; ++e)
+    if ((resid & (1u << e)) && key[e] == kcut) ++my_ties;
+  int tie_total;
+  int tie_rank = block_excl_scan_i32(my_ties, sc, tie_total);
 
-  // compact flags to ascending ids
-  const int per = (nk + nthr - 1) / nthr;
-  const int c0 = min(tid * per, nk), c1 = min(c0 + per, nk);
-  int mine = 0;
-  for (int c = c0; c < c1; ++c) mine += flag[c];
+  uint32_t keepm = forcedm;
+#pragma unroll
+  for (int e = 0; e < kSelMaxPerThread; ++e) {
+    if (!(resid & (1u << e))) continue;
+    bool k;
+    if (keep_all) {
+      k = true;
+    } else if (keep_none) {
+      k = false;
+    } else if (key[e] == kcut) {
+      k = tie_rank < mtie;
+      ++tie_rank;
+    } else {
+      k = key[e] > kcut;
+    }
+    if (k) keepm |= 1u << e;
+  }
   int total_kept;
-  int pos = block_exclusive_scan<int>(mine, reinterpret_cast<int*>(scan), total_kept);
+  int pos = block_excl_scan_i32(__popc(keepm), sc, total_kept);
   int32_t* irow = a.idx + size_t(row) * nk;
-  for (int c = c0; c < c1; ++c)
-    if (flag[c]) irow[pos++] = c;
+#pragma unroll
+  for (int e = 0; e < kSelMaxPerThread; ++e)
+    if (keepm & (1u << e)) irow[pos++] = c0 + e;
   for (int c = total_kept + tid; c < nk; c += nthr) irow[c] = -1;
   if (tid == 0) a.cnt[row] = total_kept;
 }
 
-static size_t select_lds_bytes(int nk) {
-  size_t cap = 2;
-  while (cap < size_t(nk)) cap <<= 1;
-  return sizeof(uint64_t) * cap + sizeof(double) * 1024 + size_t(nk);
-}
-
 hipError_t launch_select_topp(const SelectArgs& a, hipStream_t s) {
+  // enough threads that each owns at most kSelMaxPerThread candidates (and ~4 when possible)
   int threads = 64;
-  while (threads < 1024 && threads * 2 < a.nk) threads <<= 1;
-  const size_t lds = select_lds_bytes(a.nk);
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(select_topp_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
-  }
-  select_topp_kernel<<<a.rows, threads, lds, s>>>(a);
+  while (threads < 1024 && threads * 4 < a.nk) threads <<= 1;
+  select_topp_kernel<<<a.rows, threads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,67 @@
+"""Fixed workload for rocprofv3 runs (kernel trace and HBM counters).
+
+Runs, on cuda:0: `--steps` prefill steps of the GQA workload (L=8192, 32/8
+heads, d=128, bf16, block 64, top-p 0.9), `--steps` decode steps of the sparse
+decode workload (batch 16, context 131072), and `--steps` plain device copies
+of 1 GiB, whose counter readings calibrate FETCH_SIZE / WRITE_SIZE against a
+known byte count.
+
+  rocprofv3 --kernel-trace --stats -d OUT -o run -- python -m block_sparse_attention_amd.prof_workload
+  rocprofv3 --pmc FETCH_SIZE -d OUT -o fetch -- python -m block_sparse_attention_amd.prof_workload
+  rocprofv3 --pmc WRITE_SIZE -d OUT -o write -- python -m block_sparse_attention_amd.prof_workload
+"""
+from __future__ import annotations
+
+import argparse
+import sys
+
+import torch
+
+from . import binding as B
+from . import inputs as I
+
+COPY_BYTES = 1 << 30
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    B.load_library()
+    dev = torch.device("cuda:0")
+
+    cfg = I.C2
+    q, k, v = I.prefill_inputs(cfg)
+    dq, dk, dv = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q, k, v))
+    desc = B.prefill_desc(dq, dk, cfg.block, cfg.top_p)
+    bufs = B.alloc_prefill(desc, dev)
+    for _ in range(args.steps):
+        B.prefill(dq, dk, dv, cfg.block, cfg.top_p, bufs=bufs)
+    torch.cuda.synchronize()
+    print(f"prefill steps done: {args.steps}", flush=True)
+
+    if not args.no_decode:
+        dc = I.C4
+        D = I.decode_inputs(dc)
+        up = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)
+        t = {kk: (torch.from_numpy(vv).to(dev) if kk == "idx_w" else up(vv)) for kk, vv in D.items()}
+        del D
+        dbufs = None
+        for _ in range(args.steps):
+            dbufs = B.decode(t["q"], t["k_cache"], t["v_cache"], t["idx_q"], t["idx_w"], t["idx_k"], dc.block,
+                             dc.top_p, bufs=dbufs)
+        torch.cuda.synchronize()
+        print(f"decode steps done: {args.steps}", flush=True)
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy steps done: {args.steps} x {COPY_BYTES} bytes", flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
