@@ -73,22 +73,33 @@ __device__ __forceinline__ void unit_of(int w, int pairs, int nb, int chunks, in
   }
 }
 
-template <int D, int NW>
+__device__ __forceinline__ float xhalf_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float xhalf_sum(float x) { return x + __shfl_xor(x, 32); }
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+constexpr int kListCap = 2048;   // kept-list entries staged in LDS
+
+template <int D, int NW, bool PERM>
 __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, int chunks, float scale_log2) {
   constexpr int NT = NW * 64;
-  constexpr int KLD = D + 8;        // K tile row stride (elements)
-  constexpr int VLD = kKT + 4;      // Vt row stride (elements)
-  constexpr int CK = (kKT * D / 8 + NT - 1) / NT;   // 16-byte K chunks per thread
-  constexpr int NVB = (kKT / 4) * (D / 4);           // 4x4 V blocks per tile
-  constexpr int CV = (NVB + NT - 1) / NT;
+  constexpr int KLD = D + 8;                        // K and V tile row stride (elements)
+  constexpr int CPR = D / 8;                        // 16-byte chunks per row
+  constexpr int CH = (kKT * CPR + NT - 1) / NT;     // chunks per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKT * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VLD];
-  __shared__ int kpos[2][kKT];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKT * KLD];
+  __shared__ int kpos[3][kKT];
+  __shared__ int s_list[kListCap];
 
   const int pairs = a.batch * a.hkv;
   int pair, i, chunk;
   unit_of(blockIdx.x, pairs, a.nb, chunks, pair, i, chunk);
-  const int b = pair / a.hkv, g = pair % a.hkv;
+  const int b = pair / a.hkv;
   const int G = a.hq / a.hkv, B = a.block, L = a.L;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -96,160 +107,146 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
   const int GB = G * B;
   const int pr = chunk * (NW * 32) + wv * 32 + ql;
   const int prc = min(pr, GB - 1);
-  const int h = g * G + prc / B;
+  const int h = (pair % a.hkv) * G + prc / B;
   const int r_raw = i * B + prc % B;
   const bool qvalid = pr < GB && r_raw < L;
   const int r = min(r_raw, L - 1);
 
-  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + size_t(pair) * L * D;
-  const uint16_t* Vg = static_cast<const uint16_t*>(a.v) + size_t(pair) * L * D;
-
   // Q fragments (B operand of S^T = K Q^T): lane (query ql, half hf)
   bf16x8_t qf[D / 16];
   {
-    const uint16_t* qrow = Q + ((size_t(b) * a.hq + h) * L + r) * D;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((size_t(b) * a.hq + h) * L + r) * D;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + ks * 16 + hf * 8));
   }
 
-  SlotMap sm;
-  const size_t row_id = (size_t(pair) * a.nb + i);
-  sm.list = a.idx + row_id * a.nb;
-  sm.nkept = a.cnt[row_id];
-  sm.permg = a.perm ? a.perm + size_t(pair) * L : nullptr;
-  sm.lgB = 31 - __builtin_clz(B);
-  sm.L = L;
-  sm.seg_start = (a.perm && a.segment > 0) ? ((i * B) / a.segment) * a.segment : 0;
-  const int total = sm.nkept * B;
-  const int ntiles = (total + kKT - 1) / kKT;
-  const int last_block_start = (sm.nkept - 1) * B;
+  const size_t row_id = size_t(pair) * a.nb + i;
+  const int nkept = a.cnt[row_id];
+  const int32_t* glist = a.idx + row_id * a.nb;
+  for (int k = tid; k < min(nkept, kListCap); k += NT) s_list[k] = glist[k];
+  const int* lst = nkept <= kListCap ? s_list : glist;
+  const int lgB = 31 - __builtin_clz(B);
+  const int seg_start = (PERM && a.segment > 0) ? ((i * B) / a.segment) * a.segment : 0;
+  const int32_t* permg = PERM ? a.perm + size_t(pair) * L : nullptr;
+  const int ntiles = (nkept * B + kKT - 1) / kKT;
+  // tiles before the last kept block need no mask (history and earlier own-segment blocks are visible)
+  const int nfull = min(ntiles, ((nkept - 1) * B) / kKT);
 
-  uint4 kreg[CK];
-  uint2 vreg[CV][4];
-  int kp_lim = 0;
+  // K/V slabs of this (batch, KV head) as buffer resources: out-of-range reads return zero
+  const uint32_t nrec = uint32_t(L) * D * 2;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k) + size_t(pair) * L * D), 0, int(nrec), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.v) + size_t(pair) * L * D), 0, int(nrec), 0x00020000);
 
-  auto load_tile = [&](int t) {
-    const int s0 = t * kKT;
+  // where this thread's chunks of tile t come from: byte offset in the slab
+  // (out of range for an empty slot) and the row's mask limit (-1: always
+  // visible, position: visible iff <= query row, INT_MAX: no key)
+  struct RowMap {
+    uint32_t off[CH];
+    int lim[CH];
+  };
+  auto map_tile = [&](int t, RowMap& m) {
 #pragma unroll
-    for (int c = 0; c < CK; ++c) {
+    for (int c = 0; c < CH; ++c) {
       const int cid = tid + c * NT;
-      const int row = cid / (D / 8), col8 = cid % (D / 8);
-      int pos;
-      bool hist, inl;
-      sm.at(s0 + row, pos, hist, inl);
-      const bool ok = cid < kKT * D / 8 && inl && pos < L;
-      kreg[c] = make_uint4(0u, 0u, 0u, 0u);
-      if (ok) kreg[c] = *reinterpret_cast<const uint4*>(Kg + size_t(sm.phys_of(pos, hist)) * D + col8 * 8);
-    }
-#pragma unroll
-    for (int c = 0; c < CV; ++c) {
-      const int vb = tid + c * NT;
-      const int dg = vb % (D / 4), kq = vb / (D / 4);
-      int pos;
-      bool hist, inl;
-      sm.at(s0 + 4 * kq, pos, hist, inl);   // 4 consecutive slots of one block (B >= 4)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const bool ok = vb < NVB && inl && pos + rr < L;
-        vreg[c][rr] = make_uint2(0u, 0u);
-        if (ok) vreg[c][rr] = *reinterpret_cast<const uint2*>(Vg + size_t(sm.phys_of(pos + rr, hist)) * D + dg * 4);
+      const int s = t * kKT + cid / CPR;
+      const int bi = s >> lgB;
+      const bool inl = bi < nkept && cid < kKT * CPR;
+      const int base = lst[inl ? bi : 0] << lgB;
+      const int pos = base + (s & (B - 1));
+      const bool valid = inl && pos < L;
+      const bool hist = base < seg_start;
+      int phys = pos;
+      if constexpr (PERM) {
+        const int pp = permg[valid ? pos : 0];
+        phys = hist ? pp : pos;
       }
+      m.off[c] = valid ? uint32_t(phys) * (D * 2) + uint32_t(cid % CPR) * 16 : 0x80000000u;
+      m.lim[c] = valid ? (hist ? -1 : pos) : 0x7fffffff;
     }
-    if (tid < kKT) {
-      int pos;
-      bool hist, inl;
-      sm.at(s0 + tid, pos, hist, inl);
-      kp_lim = (inl && pos < L) ? (hist ? -1 : pos) : 0x7fffffff;
+  };
+  auto gather = [&](const __amdgpu_buffer_rsrc_t& rs, const RowMap& m, uint4 (&reg)[CH]) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      reg[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, m.off[c], 0, 0));
+  };
+  auto put = [&](uint16_t* dst, const uint4 (&reg)[CH]) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int cid = tid + c * NT;
+      if (cid < kKT * CPR) *reinterpret_cast<uint4*>(&dst[(cid / CPR) * KLD + (cid % CPR) * 8]) = reg[c];
+    }
+  };
+  auto put_kpos = [&](int* kp, const RowMap& m) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int cid = tid + c * NT;
+      if (cid < kKT * CPR && cid % CPR == 0) kp[cid / CPR] = m.lim[c];
     }
   };
 
-  auto store_tile = [&](int buf) {
+  // S^T tile = K_tile Q^T (64 keys x 32 queries per wave)
+  auto qk = [&](const uint16_t* kt, f32x16_t (&s)[2]) {
 #pragma unroll
-    for (int c = 0; c < CK; ++c) {
-      const int cid = tid + c * NT;
-      if (cid < kKT * D / 8) {
-        const int row = cid / (D / 8), col8 = cid % (D / 8);
-        *reinterpret_cast<uint4*>(&Ks[buf][row * KLD + col8 * 8]) = kreg[c];
-      }
+    for (int rt = 0; rt < 2; ++rt) {
+      const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(&kt[(rt * 32 + ql) * KLD + hf * 8]);
+      s[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[0], f32x16_t{}, 0, 0, 0);
     }
 #pragma unroll
-    for (int c = 0; c < CV; ++c) {
-      const int vb = tid + c * NT;
-      if (vb < NVB) {
-        const int dg = vb % (D / 4), kq = vb / (D / 4);
-        // 4 keys x 4 dims -> 4 rows of Vt, each 4 consecutive keys
-        const uint2* v4 = vreg[c];
-        uint2 o0, o1, o2, o3;
-        o0.x = __builtin_amdgcn_perm(v4[1].x, v4[0].x, 0x05040100u);
-        o0.y = __builtin_amdgcn_perm(v4[3].x, v4[2].x, 0x05040100u);
-        o1.x = __builtin_amdgcn_perm(v4[1].x, v4[0].x, 0x07060302u);
-        o1.y = __builtin_amdgcn_perm(v4[3].x, v4[2].x, 0x07060302u);
-        o2.x = __builtin_amdgcn_perm(v4[1].y, v4[0].y, 0x05040100u);
-        o2.y = __builtin_amdgcn_perm(v4[3].y, v4[2].y, 0x05040100u);
-        o3.x = __builtin_amdgcn_perm(v4[1].y, v4[0].y, 0x07060302u);
-        o3.y = __builtin_amdgcn_perm(v4[3].y, v4[2].y, 0x07060302u);
-        uint16_t* base = &Vt[buf][(4 * dg) * VLD + 4 * kq];
-        *reinterpret_cast<uint2*>(base) = o0;
-        *reinterpret_cast<uint2*>(base + VLD) = o1;
-        *reinterpret_cast<uint2*>(base + 2 * VLD) = o2;
-        *reinterpret_cast<uint2*>(base + 3 * VLD) = o3;
+    for (int ks = 1; ks < D / 16; ++ks)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&kt[(rt * 32 + ql) * KLD + ks * 16 + hf * 8]);
+        s[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[rt], 0, 0, 0);
       }
-    }
-    if (tid < kKT) kpos[buf][tid] = kp_lim;
   };
 
   f32x16_t oacc[D / 32];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
+  for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16_t{};
   float m_run = -kInf, l_run = 0.f;
+  const int jl = lane & 15, g16 = lane >> 4;
+  const int vrow = 4 * (g16 >> 1) + (jl >> 2);          // key row within a 16-key step
+  const int vcol = 16 * (g16 & 1) + 4 * (jl & 3);       // column within a 32-wide d tile
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  __syncthreads();   // kept list staged
+
+  RowMap mV, mK, mN;
+  uint4 kreg[CH], vreg[CH];
+  map_tile(0, mN);
+  gather(rk, mN, kreg);
+  gather(rv, mN, vreg);
+  map_tile(1, mV);
+  put(Ks[0], kreg);
+  put(Vs[0], vreg);
+  put_kpos(kpos[0], mN);
+  gather(rk, mV, kreg);
+  map_tile(2, mK);
+  put(Ks[1], kreg);
+  put_kpos(kpos[1], mV);
   __syncthreads();
+  f32x16_t s_cur[2], s_nxt[2];
+  qk(Ks[0], s_cur);
+  __syncthreads();   // iteration 0 overwrites Ks[0]
 
+  // K runs one tile ahead of V: iteration t reads K(t+1) and V(t) from LDS,
+  // fetches K(t+2) and V(t+1) from HBM, and maps tile t+3.
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-
-    // S^T tile (64 keys x 32 queries per wave)
-    f32x16_t sacc[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[rt][e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const bf16x8_t kf =
-            *reinterpret_cast<const bf16x8_t*>(&Ks[buf][(rt * 32 + ql) * KLD + ks * 16 + hf * 8]);
-        sacc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[rt], 0, 0, 0);
-      }
-    }
-
-    if (t * kKT + kKT > last_block_start) {  // tile touches the last kept block: apply the mask
+    // (A) mask, max, rare rescale of the running state (tile t)
+    if (t >= nfull) {
+      const int* kp = kpos[t % 3];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int slot = rt * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-          if (kpos[buf][slot] > r) sacc[rt][e] = -kInf;
-        }
+        for (int e = 0; e < 16; ++e)
+          if (kp[rt * 32 + 8 * (e >> 2) + 4 * hf + (e & 3)] > r) s_cur[rt][e] = -kInf;
     }
-
-    // online softmax (per lane = per query; halves share the max)
-    float mx = sacc[0][0];
+    float mx = fmaxf(s_cur[0][0], s_cur[1][0]);
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[rt][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s_cur[0][e], s_cur[1][e]));
+    mx = xhalf_max(mx);
     const float mcand = mx * scale_log2;
     const bool need = mcand > m_run + kRescaleThreshold;
     if (__ballot(need)) {
@@ -263,40 +260,51 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
       m_run = m_new;
     }
     const float msub = (m_run == -kInf) ? 0.f : m_run;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[rt][e] = __builtin_amdgcn_exp2f(fmaf(sacc[rt][e], scale_log2, -msub));
-    float rs = 0.f;   // row sum of the bf16-rounded P that enters the PV product
 
-    // O^T += V^T P^T over 4 k-steps of 16 keys
+    // (B) straight-line: HBM fetches, next map, QK(t+1) on MFMA beside exp(t), PV(t)
+    gather(rk, mK, kreg);
+    gather(rv, mV, vreg);
+    __builtin_amdgcn_sched_barrier(0);   // keep the HBM fetches at the top of the block
+    map_tile(t + 3, mN);
+    qk(Ks[(t + 1) & 1], s_nxt);   // stale but in bounds on the last tile
+    const uint16_t* vt = Vs[t & 1];
+    float rs = 0.f;   // row sum of the bf16-rounded P that enters the PV product
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int rt = kk >> 1, hb = (kk & 1) * 8;
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(s_cur[rt][hb + e], scale_log2, -msub));
       uint4 pp;
-      pp.x = pack_bf16x2(sacc[rt][hb + 0], sacc[rt][hb + 1]);
-      pp.y = pack_bf16x2(sacc[rt][hb + 2], sacc[rt][hb + 3]);
-      pp.z = pack_bf16x2(sacc[rt][hb + 4], sacc[rt][hb + 5]);
-      pp.w = pack_bf16x2(sacc[rt][hb + 6], sacc[rt][hb + 7]);
-      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pp);
+      pp.x = pack_bf16x2(pv[0], pv[1]);
+      pp.y = pack_bf16x2(pv[2], pv[3]);
+      pp.z = pack_bf16x2(pv[4], pv[5]);
+      pp.w = pack_bf16x2(pv[6], pv[7]);
       rs = dot2_bf16(pp.x, kOnes, dot2_bf16(pp.y, kOnes, dot2_bf16(pp.z, kOnes, dot2_bf16(pp.w, kOnes, rs))));
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pp);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const uint16_t* vrow = &Vt[buf][(dt * 32 + ql) * VLD + kk * 16 + 4 * hf];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+        const uint16_t* base = &vt[(kk * 16 + vrow) * KLD + dt * 32 + vcol];
+        const uint2 lo = lds_read_tr16(base);              // keys kk*16 + 4*hf + 0..3
+        const uint2 hi = lds_read_tr16(base + 8 * KLD);    // keys kk*16 + 8 + 4*hf + 0..3
         const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[dt], 0, 0, 0);
       }
     }
-
     l_run += rs;
 
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    // (C) stage K(t+2) and V(t+1)
+    put(Ks[t & 1], kreg);
+    put(Vs[(t + 1) & 1], vreg);
+    put_kpos(kpos[(t + 2) % 3], mK);
     __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) s_cur[rt] = s_nxt[rt];
+    mV = mK;
+    mK = mN;
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xhalf_sum(l_run);
   if (qvalid) {
     const float inv = 1.0f / l_tot;
     uint16_t* orow = static_cast<uint16_t*>(a.o) + ((size_t(b) * a.hq + h) * L + r) * D;
@@ -405,7 +413,10 @@ static hipError_t launch_mfma(const PrefillArgs& a, hipStream_t s, float scale_l
   const int G = a.hq / a.hkv;
   const int chunks = (G * a.block + NW * 32 - 1) / (NW * 32);
   const long long units = (long long)a.batch * a.hkv * a.nb * chunks;
-  prefill_mfma_kernel<D, NW><<<dim3(unsigned(units)), NW * 64, 0, s>>>(a, chunks, scale_log2);
+  if (a.perm)
+    prefill_mfma_kernel<D, NW, true><<<dim3(unsigned(units)), NW * 64, 0, s>>>(a, chunks, scale_log2);
+  else
+    prefill_mfma_kernel<D, NW, false><<<dim3(unsigned(units)), NW * 64, 0, s>>>(a, chunks, scale_log2);
   return hipGetLastError();
 }
 
