@@ -88,11 +88,15 @@ constexpr int kListCap = 2048;   // kept-list entries staged in LDS
 template <int D, int NW, bool PERM>
 __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, int chunks, float scale_log2) {
   constexpr int NT = NW * 64;
-  constexpr int KLD = D + 8;                        // K and V tile row stride (elements)
+  // Row strides (elements): K rows start 4 banks apart (conflict-free 16-byte
+  // fragment reads); V rows start 16 banks apart, so the four rows of a
+  // transposing read cover all 64 banks.
+  constexpr int KLD = D + 8;
+  constexpr int VLD = D + 32;
   constexpr int CPR = D / 8;                        // 16-byte chunks per row
   constexpr int CH = (kKT * CPR + NT - 1) / NT;     // chunks per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKT * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKT * KLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKT * VLD];
   __shared__ int kpos[3][kKT];
   __shared__ int s_list[kListCap];
 
@@ -172,11 +176,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
     for (int c = 0; c < CH; ++c)
       reg[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, m.off[c], 0, 0));
   };
-  auto put = [&](uint16_t* dst, const uint4 (&reg)[CH]) {
+  auto put = [&](uint16_t* dst, int ld, const uint4 (&reg)[CH]) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int cid = tid + c * NT;
-      if (cid < kKT * CPR) *reinterpret_cast<uint4*>(&dst[(cid / CPR) * KLD + (cid % CPR) * 8]) = reg[c];
+      if (cid < kKT * CPR) *reinterpret_cast<uint4*>(&dst[(cid / CPR) * ld + (cid % CPR) * 8]) = reg[c];
     }
   };
   auto put_kpos = [&](int* kp, const RowMap& m) {
@@ -219,22 +223,23 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
   gather(rk, mN, kreg);
   gather(rv, mN, vreg);
   map_tile(1, mV);
-  put(Ks[0], kreg);
-  put(Vs[0], vreg);
+  put(Ks[0], KLD, kreg);
+  put(Vs[0], VLD, vreg);
   put_kpos(kpos[0], mN);
   gather(rk, mV, kreg);
   map_tile(2, mK);
-  put(Ks[1], kreg);
+  put(Ks[1], KLD, kreg);
   put_kpos(kpos[1], mV);
   __syncthreads();
-  f32x16_t s_cur[2], s_nxt[2];
-  qk(Ks[0], s_cur);
+  f32x16_t sa[2], sb[2];
+  qk(Ks[0], sa);
   __syncthreads();   // iteration 0 overwrites Ks[0]
 
-  // K runs one tile ahead of V: iteration t reads K(t+1) and V(t) from LDS,
-  // fetches K(t+2) and V(t+1) from HBM, and maps tile t+3.
-  for (int t = 0; t < ntiles; ++t) {
-    // (A) mask, max, rare rescale of the running state (tile t)
+  // One tile t: softmax of s_cur (scores of tile t) and PV(t); QK(t+1) -> s_nxt.
+  // K runs one tile ahead of V: reads K(t+1) and V(t) from LDS, fetches
+  // K(t+2) and V(t+1) from HBM, and maps tile t+3.
+  auto step = [&](int t, f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2]) {
+    // (A) mask, max, rare rescale of the running state
     if (t >= nfull) {
       const int* kp = kpos[t % 3];
 #pragma unroll
@@ -243,9 +248,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
         for (int e = 0; e < 16; ++e)
           if (kp[rt * 32 + 8 * (e >> 2) + 4 * hf + (e & 3)] > r) s_cur[rt][e] = -kInf;
     }
-    float mx = fmaxf(s_cur[0][0], s_cur[1][0]);
+    float mx = __builtin_fmaxf(s_cur[0][0], s_cur[1][0]);
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s_cur[0][e], s_cur[1][e]));
+    for (int e = 1; e < 16; ++e) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s_cur[0][e]), s_cur[1][e]);
     mx = xhalf_max(mx);
     const float mcand = mx * scale_log2;
     const bool need = mcand > m_run + kRescaleThreshold;
@@ -284,9 +289,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
       const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pp);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const uint16_t* base = &vt[(kk * 16 + vrow) * KLD + dt * 32 + vcol];
+        const uint16_t* base = &vt[(kk * 16 + vrow) * VLD + dt * 32 + vcol];
         const uint2 lo = lds_read_tr16(base);              // keys kk*16 + 4*hf + 0..3
-        const uint2 hi = lds_read_tr16(base + 8 * KLD);    // keys kk*16 + 8 + 4*hf + 0..3
+        const uint2 hi = lds_read_tr16(base + 8 * VLD);    // keys kk*16 + 8 + 4*hf + 0..3
         const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[dt], 0, 0, 0);
       }
@@ -294,15 +299,21 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
     l_run += rs;
 
     // (C) stage K(t+2) and V(t+1)
-    put(Ks[t & 1], kreg);
-    put(Vs[(t + 1) & 1], vreg);
+    put(Ks[t & 1], KLD, kreg);
+    put(Vs[(t + 1) & 1], VLD, vreg);
     put_kpos(kpos[(t + 2) % 3], mK);
     __syncthreads();
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) s_cur[rt] = s_nxt[rt];
     mV = mK;
     mK = mN;
+  };
+
+  // unrolled by two so the score tiles alternate between register sets
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, sa, sb);
+    step(t + 1, sb, sa);
   }
+  if (t < ntiles) step(t, sa, sb);
 
   const float l_tot = xhalf_sum(l_run);
   if (qvalid) {
