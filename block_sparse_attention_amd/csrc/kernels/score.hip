@@ -67,6 +67,7 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(PoolArgs a) {
   float acc[8];
   // Q: G heads x nr rows
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll 4
   for (int rr = rp; rr < G * nr; rr += rows_par) {
     const int h = g * G + rr / nr, r = r0 + rr % nr;
     float x[8];
@@ -78,6 +79,7 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(PoolArgs a) {
 
   const size_t kv_row0 = (size_t(b) * a.hkv + g) * L;
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll 4
   for (int rr = rp; rr < nr; rr += rows_par) {
     float x[8];
     load8<T>(K + (kv_row0 + r0 + rr) * d + lr * 8, x);
@@ -88,6 +90,7 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(PoolArgs a) {
 
   if (a.perm) {
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll 4
     for (int rr = rp; rr < nr; rr += rows_par) {
       const int phys = a.perm[kv_row0 + r0 + rr];
       float x[8];
@@ -133,11 +136,17 @@ __global__ __launch_bounds__(256) void meanpool_score_kernel(MeanpoolScoreArgs a
   const float* qb = a.qbar + bg * size_t(nb) * d;
   const float* knb = a.kbar_nat + bg * size_t(nb) * d;
   const float* kpb = a.kbar_perm ? a.kbar_perm + bg * size_t(nb) * d : nullptr;
-  for (int e = threadIdx.x; e < kST * d; e += 256) {
-    const int r = e / d, c = e % d;
-    qs[r * ld + c] = (i0 + r < nb) ? qb[size_t(i0 + r) * d + c] : 0.f;
-    kn[r * ld + c] = (j0 + r < nb) ? knb[size_t(j0 + r) * d + c] : 0.f;
-    if (kpb) kp[r * ld + c] = (j0 + r < nb) ? kpb[size_t(j0 + r) * d + c] : 0.f;
+  for (int e = threadIdx.x; e < kST * d / 4; e += 256) {
+    const int r = e / (d / 4), c = (e % (d / 4)) * 4;
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 vq = (i0 + r < nb) ? *reinterpret_cast<const float4*>(qb + size_t(i0 + r) * d + c) : zero;
+    const float4 vn = (j0 + r < nb) ? *reinterpret_cast<const float4*>(knb + size_t(j0 + r) * d + c) : zero;
+    qs[r * ld + c] = vq.x; qs[r * ld + c + 1] = vq.y; qs[r * ld + c + 2] = vq.z; qs[r * ld + c + 3] = vq.w;
+    kn[r * ld + c] = vn.x; kn[r * ld + c + 1] = vn.y; kn[r * ld + c + 2] = vn.z; kn[r * ld + c + 3] = vn.w;
+    if (kpb) {
+      const float4 vp = (j0 + r < nb) ? *reinterpret_cast<const float4*>(kpb + size_t(j0 + r) * d + c) : zero;
+      kp[r * ld + c] = vp.x; kp[r * ld + c + 1] = vp.y; kp[r * ld + c + 2] = vp.z; kp[r * ld + c + 3] = vp.w;
+    }
   }
   __syncthreads();
   float sn[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, sp[2][2] = {{0.f, 0.f}, {0.f, 0.f}};

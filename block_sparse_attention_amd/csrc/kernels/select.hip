@@ -3,7 +3,11 @@
 // residual distribution until the cumulative mass reaches p, floor K_min.
 //
 // One workgroup per row; each thread owns a contiguous run of candidate ids.
-// Instead of sorting, the kernel searches the cutoff directly: with
+// Rows of at most 2048 candidates are ordered exactly: each residual
+// candidate's rank is the number of candidates ahead of it (higher score, or
+// equal score and lower id), the masses are prefix-summed in fp64 in rank
+// order and the first prefix reaching p ends the kept set.  Longer rows
+// (decode) search the cutoff instead of sorting: with
 // key(s) = order-preserving bits of the score, the kept residual set of the
 // rule (scores descending, ties to the lower block id, shortest prefix whose
 // mass reaches p) is {key > K} plus the first m candidates with key == K in
@@ -17,6 +21,7 @@
 namespace spot {
 
 constexpr int kSelMaxPerThread = 16;   // candidates per thread (16384 / 1024)
+constexpr int kRankMax = 2048;         // rows up to this length are ranked exactly
 
 __device__ __forceinline__ uint32_t score_key(float s) {
   const uint32_t u = __float_as_uint(s);
@@ -89,8 +94,44 @@ __device__ int block_excl_scan_i32(int x, SelScratch& sc, int& total) {
   return before + incl - x;
 }
 
+__device__ double block_excl_scan_f64(double x, SelScratch& sc, double& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  double incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) sc.d[w] = incl;
+  __syncthreads();
+  double before = 0.0, tot = 0.0;
+  for (int k = 0; k < nw; ++k) {
+    if (k < w) before += sc.d[k];
+    tot += sc.d[k];
+  }
+  __syncthreads();
+  total = tot;
+  return before + (incl - x);
+}
+
+// kept ids ascending (thread runs are contiguous and in order), -1 padding, count
+__device__ void write_row(const SelectArgs& a, int row, uint32_t keepm, int c0, SelScratch& sc) {
+  int total_kept;
+  int pos = block_excl_scan_i32(__popc(keepm), sc, total_kept);
+  int32_t* irow = a.idx + size_t(row) * a.nk;
+#pragma unroll
+  for (int e = 0; e < kSelMaxPerThread; ++e)
+    if (keepm & (1u << e)) irow[pos++] = c0 + e;
+  for (int c = total_kept + threadIdx.x; c < a.nk; c += blockDim.x) irow[c] = -1;
+  if (threadIdx.x == 0) a.cnt[row] = total_kept;
+}
+
 __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
   __shared__ SelScratch sc;
+  __shared__ uint32_t s_key[kRankMax];
+  __shared__ uint16_t s_sorted[kRankMax];
+  __shared__ uint8_t s_flag[kRankMax];
+  __shared__ int s_kstar;
   const int nk = a.nk;
   const int row = blockIdx.x;
   const int tid = threadIdx.x, nthr = blockDim.x;
@@ -124,6 +165,71 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
     }
   }
   const int n_res = block_sum_i32(__popc(resid), sc);
+
+  if (n <= kRankMax) {
+    // ---- exact order by rank (rows up to kRankMax candidates)
+#pragma unroll
+    for (int e = 0; e < kSelMaxPerThread; ++e) {
+      const int c = c0 + e;
+      if (e < per && c < n) {
+        s_key[c] = (resid & (1u << e)) ? key[e] : 0u;   // 0: not a residual candidate
+        s_flag[c] = (forcedm & (1u << e)) ? 1 : 0;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kSelMaxPerThread; ++e) {
+      if (!(resid & (1u << e))) continue;
+      const int c = c0 + e;
+      const uint32_t k = key[e];
+      int rank = 0;
+      for (int o = 0; o < n; ++o) {
+        const uint32_t ko = s_key[o];
+        rank += (ko > k || (ko == k && o < c)) ? 1 : 0;
+      }
+      s_sorted[rank] = uint16_t(c);
+    }
+    __syncthreads();
+    int kstar;
+    if (a.top_p >= 1.0f) {
+      kstar = n_res;
+    } else if (a.top_p <= 0.0f || n_res == 0) {
+      kstar = 0;
+    } else {
+      const float gmax = block_max_f32(smax, sc);
+      const int rper = (n_res + nthr - 1) / nthr;
+      const int k0 = min(tid * rper, n_res), k1 = min(k0 + rper, n_res);
+      double local = 0.0;
+      for (int kk = k0; kk < k1; ++kk) local += double(__expf(srow[s_sorted[kk]] - gmax));
+      double z;
+      const double before = block_excl_scan_f64(local, sc, z);
+      if (tid == 0) s_kstar = n_res;
+      __syncthreads();
+      const double target = double(a.top_p) * z;
+      double cum = before;
+      for (int kk = k0; kk < k1; ++kk) {
+        const double prev = cum;
+        cum += double(__expf(srow[s_sorted[kk]] - gmax));
+        if (cum >= target && !(prev >= target)) {
+          atomicMin(&s_kstar, kk + 1);
+          break;
+        }
+      }
+      __syncthreads();
+      kstar = s_kstar;
+    }
+    kstar = max(kstar, min(a.k_min, n_res));
+    for (int kk = tid; kk < kstar; kk += nthr) s_flag[s_sorted[kk]] = 1;
+    __syncthreads();
+    uint32_t keepm = 0;
+#pragma unroll
+    for (int e = 0; e < kSelMaxPerThread; ++e) {
+      const int c = c0 + e;
+      if (e < per && c < n && s_flag[c]) keepm |= 1u << e;
+    }
+    write_row(a, row, keepm, c0, sc);
+    return;
+  }
 
   // kept residual: key > kcut, plus the first mtie candidates with key == kcut
   uint32_t kcut = 0u;
@@ -223,14 +329,7 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
     }
     if (k) keepm |= 1u << e;
   }
-  int total_kept;
-  int pos = block_excl_scan_i32(__popc(keepm), sc, total_kept);
-  int32_t* irow = a.idx + size_t(row) * nk;
-#pragma unroll
-  for (int e = 0; e < kSelMaxPerThread; ++e)
-    if (keepm & (1u << e)) irow[pos++] = c0 + e;
-  for (int c = total_kept + tid; c < nk; c += nthr) irow[c] = -1;
-  if (tid == 0) a.cnt[row] = total_kept;
+  write_row(a, row, keepm, c0, sc);
 }
 
 hipError_t launch_select_topp(const SelectArgs& a, hipStream_t s) {
