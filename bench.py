@@ -2,7 +2,9 @@
 
 One step = the whole prefill path on the GQA workload (L=8192, 32 query / 8 KV
 heads, d=128, bf16, block 64, top-p 0.9): mean-pool block scores, top-p
-selection, sparse attention.  Inputs are resident in HBM before timing.
+selection, sparse attention.  Inputs are resident in HBM before timing.  The
+four launches of a step are captured once as a HIP graph and replayed (the
+eager, call-by-call step time is reported beside it).
 
 Prints one JSON line.  `value` is effective TFLOP/s over kept blocks
 (4*d*visible query-key pairs per step / step time).  The line also carries the
@@ -105,13 +107,27 @@ def bench_prefill(args, torch, B, I):
         step()
     torch.cuda.synchronize()
 
-    # K steps back to back
+    # K steps back to back, launched one call at a time
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
     for _ in range(args.steps):
         step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step_eager = t0.elapsed_time(t1) / args.steps
+
+    # the same step captured once as a HIP graph and replayed K times
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        graph.replay()
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
@@ -135,7 +151,8 @@ def bench_prefill(args, torch, B, I):
     attn_file = os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "kernels", "prefill.hip")
     achieved = flops / (ms_attn * 1e-3) / 1e12
     res = dict(
-        cfg=cfg, ms_step=ms_step, ms_sel=ms_sel, ms_attn=ms_attn, flops=flops, kept_fraction=kept_fraction,
+        cfg=cfg, ms_step=ms_step, ms_step_eager=ms_step_eager, ms_sel=ms_sel, ms_attn=ms_attn, flops=flops,
+        kept_fraction=kept_fraction,
         value=flops / (ms_step * 1e-3) / 1e12,
         roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                   "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
@@ -178,7 +195,23 @@ def bench_decode(args, torch, B, I):
     torch.cuda.synchronize()
     ms_front = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     ms_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    ms_step = ms_front + ms_attn
+    ms_step_eager = ms_front + ms_attn
+
+    # the step's four launches as one HIP graph, replayed with a cold cache each time
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.spot_block_score(desc, None, None, None, iq, iw, ik, bufs.scores)
+        B.spot_select_topp(desc, bufs.scores, bufs.idx, bufs.cnt)
+        B.spot_sparse_attn_decode(desc, q, kc, vc, bufs.idx, bufs.cnt, bufs.o, bufs.lse, bufs.workspace)
+    graph.replay()
+    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in gev:
+        flush.fill_(1.0)
+        e[0].record()
+        graph.replay()
+        e[1].record()
+    torch.cuda.synchronize()
+    ms_step = float(np.mean([e[0].elapsed_time(e[1]) for e in gev]))
     cnt = bufs.cnt.cpu().numpy()[:, 0, 0]
     idx = bufs.idx.cpu().numpy()[:, 0, 0]
     bs = np.minimum(cfg.block, cfg.T - np.arange(cfg.nt) * cfg.block)
@@ -190,7 +223,8 @@ def bench_decode(args, torch, B, I):
     attn_gbs = (kv_bytes + qo_bytes) / (ms_attn * 1e-3) / 1e9
     return dict(
         workload=cfg.name, value=round(step_bytes / (ms_step * 1e-3) / 1e9, 1), unit="GB/s",
-        ms_per_step=round(ms_step, 4), ms_score_select=round(ms_front, 4), ms_attention=round(ms_attn, 4),
+        ms_per_step=round(ms_step, 4), ms_per_step_eager_launches=round(ms_step_eager, 4),
+        ms_score_select=round(ms_front, 4), ms_attention=round(ms_attn, 4),
         kept_fraction=round(float(kept_keys.sum()) / (cfg.batch * cfg.T), 4), bytes_per_step=step_bytes,
         roofline={"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "kernel": "decode_split_kernel<128,4>+combine",
@@ -248,7 +282,8 @@ def main():
         sys.exit(1)
 
     pre = bench_prefill(args, torch, B, I)
-    print(f"[bench] prefill {pre['cfg'].name}: {pre['ms_step']:.4f} ms/step, attention {pre['ms_attn']:.4f} ms, "
+    print(f"[bench] prefill {pre['cfg'].name}: {pre['ms_step']:.4f} ms/step (graph), "
+          f"{pre['ms_step_eager']:.4f} ms/step (eager), attention {pre['ms_attn']:.4f} ms, "
           f"score+select {pre['ms_sel']:.4f} ms, kept {pre['kept_fraction']:.4f}", file=sys.stderr, flush=True)
     dec = None
     if not args.no_decode:
@@ -268,6 +303,7 @@ def main():
                    "d": cfg.d, "block": cfg.block, "top_p": cfg.top_p, "n_sink": cfg.n_sink,
                    "n_recent": cfg.n_recent, "kept_fraction": round(pre["kept_fraction"], 4),
                    "ms_attention": round(pre["ms_attn"], 4), "ms_score_select": round(pre["ms_sel"], 4),
+                   "ms_per_step_eager_launches": round(pre["ms_step_eager"], 4), "step_launch": "hip_graph_replay",
                    "flop_per_step": pre["flops"]},
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,

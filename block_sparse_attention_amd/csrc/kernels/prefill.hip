@@ -83,10 +83,20 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-constexpr int kListCap = 2048;   // kept-list entries staged in LDS
+// Build-time tuning knobs (defaults are the measured best on MI355X).
+#ifndef SPOT_PREFILL_WAVES
+#define SPOT_PREFILL_WAVES 8        // waves per workgroup (32 packed query rows each)
+#endif
+#ifndef SPOT_PREFILL_SCHED
+#define SPOT_PREFILL_SCHED 3        // 0: compiler default; 1, 2: iglp strategy 0 / 1; 3: raised wave priority over the MFMA block
+#endif
+#ifndef SPOT_PREFILL_LIST_CAP
+#define SPOT_PREFILL_LIST_CAP 2048  // kept-list entries staged in LDS (0: read from HBM)
+#endif
+constexpr int kListCap = SPOT_PREFILL_LIST_CAP;
 
 template <int D, int NW, bool PERM>
-__global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, int chunks, float scale_log2) {
+__global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a, int chunks, float scale_log2) {
   constexpr int NT = NW * 64;
   // Row strides (elements): K rows start 4 banks apart (conflict-free 16-byte
   // fragment reads); V rows start 16 banks apart, so the four rows of a
@@ -98,7 +108,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKT * KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKT * VLD];
   __shared__ int kpos[3][kKT];
-  __shared__ int s_list[kListCap];
+  __shared__ int s_list[kListCap > 0 ? kListCap : 1];
 
   const int pairs = a.batch * a.hkv;
   int pair, i, chunk;
@@ -128,8 +138,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
   const size_t row_id = size_t(pair) * a.nb + i;
   const int nkept = a.cnt[row_id];
   const int32_t* glist = a.idx + row_id * a.nb;
-  for (int k = tid; k < min(nkept, kListCap); k += NT) s_list[k] = glist[k];
-  const int* lst = nkept <= kListCap ? s_list : glist;
+  if constexpr (kListCap > 0)
+    for (int k = tid; k < min(nkept, kListCap); k += NT) s_list[k] = glist[k];
+  const int* lst = (kListCap > 0 && nkept <= kListCap) ? s_list : glist;
   const int lgB = 31 - __builtin_clz(B);
   const int seg_start = (PERM && a.segment > 0) ? ((i * B) / a.segment) * a.segment : 0;
   const int32_t* permg = PERM ? a.perm + size_t(pair) * L : nullptr;
@@ -270,6 +281,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
     gather(rk, mK, kreg);
     gather(rv, mV, vreg);
     __builtin_amdgcn_sched_barrier(0);   // keep the HBM fetches at the top of the block
+#if SPOT_PREFILL_SCHED == 1
+    __builtin_amdgcn_iglp_opt(0);
+#elif SPOT_PREFILL_SCHED == 2
+    __builtin_amdgcn_iglp_opt(1);
+#elif SPOT_PREFILL_SCHED == 3
+    __builtin_amdgcn_s_setprio(1);
+#endif
     map_tile(t + 3, mN);
     qk(Ks[(t + 1) & 1], s_nxt);   // stale but in bounds on the last tile
     const uint16_t* vt = Vs[t & 1];
@@ -297,6 +315,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
       }
     }
     l_run += rs;
+#if SPOT_PREFILL_SCHED == 3
+    __builtin_amdgcn_s_setprio(0);
+#endif
 
     // (C) stage K(t+2) and V(t+1)
     put(Ks[t & 1], KLD, kreg);
@@ -420,7 +441,7 @@ __global__ __launch_bounds__(256) void prefill_rows_kernel(PrefillArgs a, float 
 
 template <int D>
 static hipError_t launch_mfma(const PrefillArgs& a, hipStream_t s, float scale_log2) {
-  constexpr int NW = 8;
+  constexpr int NW = SPOT_PREFILL_WAVES;
   const int G = a.hq / a.hkv;
   const int chunks = (G * a.block + NW * 32 - 1) / (NW * 32);
   const long long units = (long long)a.batch * a.hkv * a.nb * chunks;
