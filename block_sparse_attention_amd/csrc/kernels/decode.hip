@@ -7,14 +7,16 @@
 // loads, several blocks in flight per thread, and keeps the arithmetic on the
 // VALU (bf16 pair dot products, fp32 accumulation).
 //
-// decode_split_kernel: workgroup = (split s, KV head g, sequence b).  The kept
-//   list of sequence b is cut into `nsplit` equal ranges.  A row of 16 lanes
-//   owns one key slot of every block in the range (lane c holds dims
-//   c*D/16 .. +D/16), keeps its own online-softmax state for the G query
-//   heads of the group, and the 16 slot streams are merged through LDS into
-//   one partial (acc, m, l) per head.
+// decode_split_kernel: workgroup = (split s, KV head g, sequence b).  Split s
+//   takes kept blocks s, s + nsplit, s + 2*nsplit, ... of sequence b, so the
+//   block ids it needs do not depend on the kept count and their loads
+//   overlap the count's.  A row of 16 lanes owns one key slot of every block
+//   of the split (lane c holds dims c*D/16 .. +D/16), keeps its own
+//   online-softmax state for the G query heads of the group, and the 16 slot
+//   streams are merged through LDS into one partial (acc, m, l) per head.
 // decode_combine_kernel: merges the partials of the splits in split order
-//   (deterministic) and writes O (bf16) and the natural-log LSE.
+//   (deterministic; all loads issued before the merge) and writes O (bf16)
+//   and the natural-log LSE.
 #include "../launch.h"
 #include "common.h"
 
@@ -23,6 +25,7 @@ namespace spot {
 constexpr int kDecThreads = 256;
 constexpr int kDecUnroll = 4;
 constexpr float kDecRescale = 8.0f;
+constexpr int kDecMaxSplits = 32;
 
 template <int EPL> struct DVec;
 template <> struct DVec<8> {
@@ -51,11 +54,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a,
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, c = tid & 15, ks = tid >> 4;
   const int B = a.block, T = a.T;
-  const int n = a.cnt[b];
-  const int per = (n + a.nsplit - 1) / a.nsplit;
-  const int blk0 = min(s * per, n), blk1 = min(n, blk0 + per);
-  const int nslots = (blk1 - blk0) * B;
   const int32_t* il = a.idx + size_t(b) * a.nk;
+  // this split's first kDecUnroll block ids, loaded beside the count
+  int pre[kDecUnroll];
+#pragma unroll
+  for (int u = 0; u < kDecUnroll; ++u) {
+    const int bi = s + u * a.nsplit;
+    pre[u] = il[bi < a.nk ? bi : 0];
+  }
+  const int n = a.cnt[b];
+  if (s >= n) return;   // the combine reads splits [0, min(n, nsplit)) only
+  const int nmine = (n - s + a.nsplit - 1) / a.nsplit;   // blocks s, s+nsplit, ... below n
+  const int nslots = nmine * B;
   const size_t kvbase = (size_t(b) * a.hkv + g) * size_t(T) * D;
   const uint16_t* Kg = a.k + kvbase;
   const uint16_t* Vg = a.v + kvbase;
@@ -73,6 +83,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a,
     for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
   }
 
+  // slot = (local block k, key j); stream ks walks keys ks, ks + KS, ...
   for (int base = ks; base < nslots; base += KS * kDecUnroll) {
     typename V::T kv[kDecUnroll], vv[kDecUnroll];
     bool ok[kDecUnroll];
@@ -83,8 +94,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a,
       kv[u] = V::zero();
       vv[u] = V::zero();
       if (sl < nslots) {
-        const int bi = blk0 + sl / B;
-        const int pos = il[bi] * B + sl % B;
+        const int kb = sl / B;
+        int blk;
+        if (kb < kDecUnroll) {
+          blk = pre[0];
+#pragma unroll
+          for (int u2 = 1; u2 < kDecUnroll; ++u2) blk = (kb == u2) ? pre[u2] : blk;
+        } else {
+          blk = il[s + kb * a.nsplit];
+        }
+        const int pos = blk * B + sl % B;
         if (pos < T) {
           ok[u] = true;
           kv[u] = V::ld(Kg + size_t(pos) * D + c * EPL);
@@ -163,15 +182,26 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const int g = h / G, hh = h % G;
   const float* part = a.partials + ((size_t(b) * a.hkv + g) * a.nsplit) * G * (D + 2) + hh * (D + 2);
   const size_t stride = size_t(G) * (D + 2);
+  const int ns = min(a.cnt[b], a.nsplit);
+  float ms[kDecMaxSplits], ls[kDecMaxSplits], as[kDecMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kDecMaxSplits; ++s) {
+    const bool on = s < ns;
+    const float* ps = part + (on ? s : 0) * stride;
+    ms[s] = on ? ps[D] : -kInf;
+    ls[s] = on ? ps[D + 1] : 0.f;
+    as[s] = on ? ps[dd] : 0.f;
+  }
   float M = -kInf;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, part[s * stride + D]);
+#pragma unroll
+  for (int s = 0; s < kDecMaxSplits; ++s) M = fmaxf(M, ms[s]);
   float A = 0.f, Lsum = 0.f;
   if (M != -kInf) {
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float* ps = part + s * stride;
-      const float f = __builtin_amdgcn_exp2f(ps[D] - M);
-      A = fmaf(ps[dd], f, A);
-      Lsum = fmaf(ps[D + 1], f, Lsum);
+#pragma unroll
+    for (int s = 0; s < kDecMaxSplits; ++s) {
+      const float f = __builtin_amdgcn_exp2f(ms[s] - M);   // 0 for empty splits
+      A = fmaf(as[s], f, A);
+      Lsum = fmaf(ls[s], f, Lsum);
     }
   }
   const float val = Lsum > 0.f ? A / Lsum : 0.f;
@@ -179,12 +209,15 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   if (a.lse && dd == 0) a.lse[size_t(b) * a.hq + h] = (Lsum > 0.f) ? (M + __log2f(Lsum)) * kLn2 : -kInf;
 }
 
+#ifndef SPOT_DECODE_TARGET_WGS
+#define SPOT_DECODE_TARGET_WGS 2048   // split workgroups per step (tuning knob)
+#endif
+
 int decode_num_splits(int batch, int hkv, int nk) {
   const int pairs = batch * hkv;
-  int ns = (2048 + pairs - 1) / pairs;
-  if (ns > 64) ns = 64;
-  const int cap = (nk + 3) / 4;
-  if (ns > cap) ns = cap;
+  int ns = (SPOT_DECODE_TARGET_WGS + pairs - 1) / pairs;
+  if (ns > kDecMaxSplits) ns = kDecMaxSplits;
+  if (ns > nk) ns = nk;
   return ns < 1 ? 1 : ns;
 }
 

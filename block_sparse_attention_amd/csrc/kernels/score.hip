@@ -183,52 +183,70 @@ hipError_t launch_meanpool_score(const MeanpoolScoreArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- ReLU indexer score
-// One wave per key block t at a time; each lane owns 4 consecutive elements
-// of the (h_idx x d_idx) row, lanes of one indexer head form a group of
-// d_idx/4 lanes.
+// A row (one key block: h_idx x d_idx bf16) is spread over LPR lanes, 8
+// elements (16 bytes) per lane; lanes of one indexer head sum their dot
+// products, the head leaders add w_h * ReLU(dot), and the row's lanes sum the
+// heads.  Each lane keeps kIdxUnroll rows in flight; one grid row per sequence.
 constexpr int kIdxUnroll = 4;
+constexpr int kIdxMaxBlocks = 64;   // workgroups per sequence
 
+template <int LPR>
 __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerScoreArgs a) {
+  constexpr int RPW = 64 / LPR;   // rows per wave per load
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / LPR, li = lane % LPR;
   const int R = a.h_idx * a.d_idx;
-  const int gs = a.d_idx / 4;  // lanes per indexer head
-  const int e0 = lane * 4;
-  const bool active = e0 < R;
-  const int head = active ? e0 / a.d_idx : 0;
-  uint2 qv = make_uint2(0u, 0u);
+  const int lph = a.d_idx / 8;    // lanes per indexer head
+  const int e0 = li * 8;
+  const bool act = e0 < R;
+  const int head = act ? e0 / a.d_idx : 0;
+  uint4 qv = make_uint4(0u, 0u, 0u, 0u);
   float w = 0.f;
-  if (active) {
-    qv = *reinterpret_cast<const uint2*>(a.idx_q + size_t(b) * R + e0);
+  if (act) {
+    qv = *reinterpret_cast<const uint4*>(a.idx_q + size_t(b) * R + e0);
     w = a.idx_w[size_t(b) * a.h_idx + head];
   }
-  const int waves_total = gridDim.x * 4;
   const uint16_t* kb = a.idx_k + size_t(b) * a.nk * R;
-  for (int t0 = (blockIdx.x * 4 + wave) * kIdxUnroll; t0 < a.nk; t0 += waves_total * kIdxUnroll) {
-    uint2 kv[kIdxUnroll];
+  const int step = gridDim.x * 4 * RPW * kIdxUnroll;
+  for (int t0 = (blockIdx.x * 4 + wave) * RPW * kIdxUnroll; t0 < a.nk; t0 += step) {
+    uint4 kv[kIdxUnroll];
 #pragma unroll
     for (int u = 0; u < kIdxUnroll; ++u) {
-      const int t = t0 + u;
-      kv[u] = (active && t < a.nk) ? *reinterpret_cast<const uint2*>(kb + size_t(t) * R + e0) : make_uint2(0u, 0u);
+      const int t = t0 + u * RPW + sub;
+      kv[u] = (act && t < a.nk) ? *reinterpret_cast<const uint4*>(kb + size_t(t) * R + e0)
+                                : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < kIdxUnroll; ++u) {
-      float dp = dot2_bf16(kv[u].x, qv.x, dot2_bf16(kv[u].y, qv.y, 0.f));
-      for (int o = gs >> 1; o > 0; o >>= 1) dp += __shfl_xor(dp, o);
-      float val = (active && (lane % gs) == 0) ? w * fmaxf(dp, 0.f) : 0.f;
-      val = wave_sum(val);
-      const int t = t0 + u;
-      if (lane == 0 && t < a.nk) a.scores[size_t(b) * a.nk + t] = val;
+      float dp = dot2_bf16(kv[u].x, qv.x, dot2_bf16(kv[u].y, qv.y, dot2_bf16(kv[u].z, qv.z,
+                           dot2_bf16(kv[u].w, qv.w, 0.f))));
+      for (int o = 1; o < lph; o <<= 1) dp += __shfl_xor(dp, o);
+      float val = (act && (li % lph) == 0) ? w * fmaxf(dp, 0.f) : 0.f;
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1)
+        if (o >= lph) val += __shfl_xor(val, o);
+      const int t = t0 + u * RPW + sub;
+      if (li == 0 && t < a.nk) a.scores[size_t(b) * a.nk + t] = val;
     }
   }
 }
 
-hipError_t launch_indexer_score(const IndexerScoreArgs& a, hipStream_t s) {
-  const int per_block = 4 * kIdxUnroll;
+template <int LPR>
+static void launch_idx(const IndexerScoreArgs& a, hipStream_t s) {
+  const int per_block = 4 * (64 / LPR) * kIdxUnroll;
   int blocks = (a.nk + per_block - 1) / per_block;
-  if (blocks > 1024) blocks = 1024;
-  dim3 grid(blocks, a.batch);
-  indexer_score_kernel<<<grid, 256, 0, s>>>(a);
+  if (blocks > kIdxMaxBlocks) blocks = kIdxMaxBlocks;
+  indexer_score_kernel<LPR><<<dim3(blocks, a.batch), 256, 0, s>>>(a);
+}
+
+hipError_t launch_indexer_score(const IndexerScoreArgs& a, hipStream_t s) {
+  const int lanes = (a.h_idx * a.d_idx) / 8;   // 16-byte chunks per row (R <= 256)
+  if (lanes <= 2) launch_idx<2>(a, s);
+  else if (lanes <= 4) launch_idx<4>(a, s);
+  else if (lanes <= 8) launch_idx<8>(a, s);
+  else if (lanes <= 16) launch_idx<16>(a, s);
+  else launch_idx<32>(a, s);
   return hipGetLastError();
 }
 

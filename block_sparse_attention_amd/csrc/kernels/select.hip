@@ -3,25 +3,26 @@
 // residual distribution until the cumulative mass reaches p, floor K_min.
 //
 // One workgroup per row; each thread owns a contiguous run of candidate ids.
-// Rows of at most 2048 candidates are ordered exactly: each residual
-// candidate's rank is the number of candidates ahead of it (higher score, or
-// equal score and lower id), the masses are prefix-summed in fp64 in rank
-// order and the first prefix reaching p ends the kept set.  Longer rows
-// (decode) search the cutoff instead of sorting: with
-// key(s) = order-preserving bits of the score, the kept residual set of the
-// rule (scores descending, ties to the lower block id, shortest prefix whose
-// mass reaches p) is {key > K} plus the first m candidates with key == K in
-// id order, where K is the largest key whose upper set {key >= K} still holds
-// mass >= p.  K is found by binary search over the 32-bit key space; every
-// mass is a fixed-order fp64 reduction (per-thread runs, then wave
-// butterflies, then waves in order), so the result is deterministic.
+// The residual candidates that can be kept are sorted exactly in LDS (bitonic
+// network on 64-bit keys: inverted order-preserving score bits above the id
+// rank, so ascending keys are score-descending with ties to the lower id),
+// their masses are prefix-summed in fp64 in that order and the first prefix
+// reaching p ends the kept set.  On rows longer than the sort buffer only the
+// candidates above a mass bound enter the sort: if the mass first reaches p
+// at the k-th sorted block, the blocks from k on carry more than (1-p)Z
+// between at most n_res of them, so every kept block has mass above
+// (1-p)Z/n_res.  If even that set is too large, the cutoff is searched
+// instead: with key = order-preserving score bits, the kept set is
+// {key > K} plus the first ties in id order, where K is the largest key whose
+// upper set still holds mass >= p (binary search over the key space).  Every
+// mass is a fixed-order fp64 reduction, so the result is deterministic.
 #include "../launch.h"
 #include "common.h"
 
 namespace spot {
 
 constexpr int kSelMaxPerThread = 16;   // candidates per thread (16384 / 1024)
-constexpr int kRankMax = 2048;         // rows up to this length are ranked exactly
+constexpr int kSortMax = 2048;         // candidates sorted exactly in LDS
 
 __device__ __forceinline__ uint32_t score_key(float s) {
   const uint32_t u = __float_as_uint(s);
@@ -128,9 +129,8 @@ __device__ void write_row(const SelectArgs& a, int row, uint32_t keepm, int c0, 
 
 __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
   __shared__ SelScratch sc;
-  __shared__ uint32_t s_key[kRankMax];
-  __shared__ uint16_t s_sorted[kRankMax];
-  __shared__ uint8_t s_flag[kRankMax];
+  __shared__ uint64_t s_sort[kSortMax];
+  __shared__ uint16_t s_rank[kSortMax];
   __shared__ int s_kstar;
   const int nk = a.nk;
   const int row = blockIdx.x;
@@ -166,50 +166,83 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
   }
   const int n_res = block_sum_i32(__popc(resid), sc);
 
-  if (n <= kRankMax) {
-    // ---- exact order by rank (rows up to kRankMax candidates)
+  if (a.top_p >= 1.0f) {   // every residual block
+    write_row(a, row, forcedm | resid, c0, sc);
+    return;
+  }
+  const int kfloor = min(a.k_min, n_res);
+  const bool by_mass = a.top_p > 0.0f && n_res > 0;
+  if (!by_mass && kfloor == 0) {   // forced blocks only
+    write_row(a, row, forcedm, c0, sc);
+    return;
+  }
+
+  // ---- exact sort of the candidates that can be kept
+  float gmax = 0.f;
+  double target = 0.0;
+  uint32_t candm = resid;
+  if (by_mass) {
+    gmax = block_max_f32(smax, sc);
+    double local = 0.0;
 #pragma unroll
-    for (int e = 0; e < kSelMaxPerThread; ++e) {
-      const int c = c0 + e;
-      if (e < per && c < n) {
-        s_key[c] = (resid & (1u << e)) ? key[e] : 0u;   // 0: not a residual candidate
-        s_flag[c] = (forcedm & (1u << e)) ? 1 : 0;
+    for (int e = 0; e < kSelMaxPerThread; ++e)
+      if (resid & (1u << e)) {
+        ex[e] = double(__expf(key_score(key[e]) - gmax));
+        local += ex[e];
+      }
+    const double z = block_sum_f64(local, sc);
+    target = double(a.top_p) * z;
+    if (n_res > kSortMax) {
+      const double bound = (1.0 - double(a.top_p)) * z / double(n_res) * (1.0 - 1e-6);
+      candm = 0;
+#pragma unroll
+      for (int e = 0; e < kSelMaxPerThread; ++e)
+        if ((resid & (1u << e)) && ex[e] > bound) candm |= 1u << e;
+    }
+  }
+  const bool filtered = candm != resid || n_res > kSortMax;
+  int ncand;
+  const int off = block_excl_scan_i32(__popc(candm), sc, ncand);
+  if (ncand <= kSortMax && ncand >= kfloor) {
+    int cap = 2;
+    while (cap < ncand) cap <<= 1;
+    int w = off;
+#pragma unroll
+    for (int e = 0; e < kSelMaxPerThread; ++e)
+      if (candm & (1u << e)) {
+        s_sort[w] = (uint64_t(~key[e]) << 32) | uint32_t(w);   // ascending: score desc, then id asc
+        ++w;
+      }
+    for (int k = ncand + tid; k < cap; k += nthr) s_sort[k] = ~0ull;
+    __syncthreads();
+    for (int k = 2; k <= cap; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int e = tid; e < cap; e += nthr) {
+          const int p = e ^ j;
+          if (p > e) {
+            const uint64_t x = s_sort[e], y = s_sort[p];
+            if ((x > y) == ((e & k) == 0)) {
+              s_sort[e] = y;
+              s_sort[p] = x;
+            }
+          }
+        }
+        __syncthreads();
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < kSelMaxPerThread; ++e) {
-      if (!(resid & (1u << e))) continue;
-      const int c = c0 + e;
-      const uint32_t k = key[e];
-      int rank = 0;
-      for (int o = 0; o < n; ++o) {
-        const uint32_t ko = s_key[o];
-        rank += (ko > k || (ko == k && o < c)) ? 1 : 0;
-      }
-      s_sorted[rank] = uint16_t(c);
-    }
-    __syncthreads();
-    int kstar;
-    if (a.top_p >= 1.0f) {
-      kstar = n_res;
-    } else if (a.top_p <= 0.0f || n_res == 0) {
-      kstar = 0;
-    } else {
-      const float gmax = block_max_f32(smax, sc);
-      const int rper = (n_res + nthr - 1) / nthr;
-      const int k0 = min(tid * rper, n_res), k1 = min(k0 + rper, n_res);
-      double local = 0.0;
-      for (int kk = k0; kk < k1; ++kk) local += double(__expf(srow[s_sorted[kk]] - gmax));
-      double z;
-      const double before = block_excl_scan_f64(local, sc, z);
-      if (tid == 0) s_kstar = n_res;
-      __syncthreads();
-      const double target = double(a.top_p) * z;
-      double cum = before;
+    for (int k = tid; k < ncand; k += nthr) s_rank[uint32_t(s_sort[k])] = uint16_t(k);
+    int kstar = 0;
+    if (by_mass) {
+      if (tid == 0) s_kstar = 0x7fffffff;
+      const int rper = (ncand + nthr - 1) / nthr;
+      const int k0 = min(tid * rper, ncand), k1 = min(k0 + rper, ncand);
+      double part = 0.0;
+      for (int kk = k0; kk < k1; ++kk) part += double(__expf(key_score(~uint32_t(s_sort[kk] >> 32)) - gmax));
+      double tot;
+      double cum = block_excl_scan_f64(part, sc, tot);
       for (int kk = k0; kk < k1; ++kk) {
         const double prev = cum;
-        cum += double(__expf(srow[s_sorted[kk]] - gmax));
+        cum += double(__expf(key_score(~uint32_t(s_sort[kk] >> 32)) - gmax));
         if (cum >= target && !(prev >= target)) {
           atomicMin(&s_kstar, kk + 1);
           break;
@@ -217,18 +250,23 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
       }
       __syncthreads();
       kstar = s_kstar;
+      if (kstar == 0x7fffffff) kstar = filtered ? -1 : ncand;   // rounding at p close to 1: keep all
+    } else {
+      __syncthreads();
     }
-    kstar = max(kstar, min(a.k_min, n_res));
-    for (int kk = tid; kk < kstar; kk += nthr) s_flag[s_sorted[kk]] = 1;
-    __syncthreads();
-    uint32_t keepm = 0;
+    if (kstar >= 0) {
+      const int kfinal = max(kstar, kfloor);
+      uint32_t keepm = forcedm;
+      int pidx = off;
 #pragma unroll
-    for (int e = 0; e < kSelMaxPerThread; ++e) {
-      const int c = c0 + e;
-      if (e < per && c < n && s_flag[c]) keepm |= 1u << e;
+      for (int e = 0; e < kSelMaxPerThread; ++e)
+        if (candm & (1u << e)) {
+          if (s_rank[pidx] < kfinal) keepm |= 1u << e;
+          ++pidx;
+        }
+      write_row(a, row, keepm, c0, sc);
+      return;
     }
-    write_row(a, row, keepm, c0, sc);
-    return;
   }
 
   // kept residual: key > kcut, plus the first mtie candidates with key == kcut
@@ -333,9 +371,10 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
 }
 
 hipError_t launch_select_topp(const SelectArgs& a, hipStream_t s) {
-  // enough threads that each owns at most kSelMaxPerThread candidates (and ~4 when possible)
+  // as few waves as keep every thread at kSelMaxPerThread candidates or fewer:
+  // the row is a chain of block-wide steps, and barriers over fewer waves are cheaper
   int threads = 64;
-  while (threads < 1024 && threads * 4 < a.nk) threads <<= 1;
+  while (threads < 1024 && threads * kSelMaxPerThread < a.nk) threads <<= 1;
   select_topp_kernel<<<a.rows, threads, 0, s>>>(a);
   return hipGetLastError();
 }
