@@ -18,11 +18,11 @@ LIB_PATH = os.path.join(_PKG, "libspot.so")
 SPOT_OK, SPOT_ERR_INVALID, SPOT_ERR_UNSUPPORTED, SPOT_ERR_WORKSPACE, SPOT_ERR_LAUNCH = 0, -1, -2, -3, -4
 SPOT_F32, SPOT_BF16 = 0, 1
 SPOT_SCORE_MEANPOOL, SPOT_SCORE_RELU_INDEXER = 0, 1
-SPOT_OP_BLOCK_SCORE, SPOT_OP_SELECT_TOPP, SPOT_OP_PREFILL, SPOT_OP_DECODE = 0, 1, 2, 3
+SPOT_OP_BLOCK_SCORE, SPOT_OP_SELECT_TOPP, SPOT_OP_PREFILL, SPOT_OP_DECODE, SPOT_OP_KEY_PERMUTATION = 0, 1, 2, 3, 4
 ABI_VERSION = 1
 
 EXPORTS = ("spot_version", "spot_status_string", "spot_last_error", "spot_workspace_size", "spot_block_score",
-           "spot_select_topp", "spot_sparse_attn_prefill", "spot_sparse_attn_decode")
+           "spot_select_topp", "spot_sparse_attn_prefill", "spot_sparse_attn_decode", "spot_key_permutation")
 
 
 class spot_desc(ctypes.Structure):
@@ -65,6 +65,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spot_select_topp.argtypes = [D, P, P, P, P, S, P]
     lib.spot_sparse_attn_prefill.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
     lib.spot_sparse_attn_decode.argtypes = [D, P, P, P, P, P, P, P, P, S, P]
+    lib.spot_key_permutation.argtypes = [D, P, P, P, P, P, S, P]
     for name in EXPORTS[3:]:
         getattr(lib, name).restype = I
     _lib = lib
@@ -128,6 +129,13 @@ def spot_sparse_attn_decode(desc, q, k_cache, v_cache, idx, cnt, o, lse=None, wo
                                                 _ptr(idx), _ptr(cnt), _ptr(o), _ptr(lse), _ptr(workspace),
                                                 ws_bytes, _stream() if stream is None else stream)
     _check("spot_sparse_attn_decode", st)
+
+
+def spot_key_permutation(desc, q, k, perm, importance=None, workspace=None, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load_library().spot_key_permutation(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(perm), _ptr(importance),
+                                             _ptr(workspace), ws_bytes, _stream() if stream is None else stream)
+    _check("spot_key_permutation", st)
 
 
 # ----------------------------------------------------------------- descriptors
@@ -211,6 +219,21 @@ def prefill(q, k, v, block: int, top_p: float, *, perm=None, segment: int = 0, n
     spot_select_topp(desc, bufs.scores, bufs.idx, bufs.cnt)
     spot_sparse_attn_prefill(desc, q, k, v, perm, bufs.idx, bufs.cnt, bufs.o, bufs.lse)
     return bufs
+
+
+def key_permutation(q, k, block: int, segment: int, *, sm_scale: float = 0.0, with_importance: bool = False):
+    """Intra-segment key permutation by last-query-block importance.
+
+    q (batch, hq, L, d), k (batch, hkv, L, d) bf16 device tensors.  Returns
+    perm (batch, hkv, L) int32 [and importance (batch, hkv, L) fp32]."""
+    _require(q, "q", dtype=torch.bfloat16)
+    _require(k, "k", dtype=torch.bfloat16)
+    desc = prefill_desc(q, k, block, 1.0, segment=segment, sm_scale=sm_scale)
+    ws = torch.empty(max(spot_workspace_size(desc, SPOT_OP_KEY_PERMUTATION), 1), dtype=torch.uint8, device=q.device)
+    perm = torch.empty(k.shape[0], k.shape[1], k.shape[2], dtype=torch.int32, device=q.device)
+    imp = torch.empty(perm.shape, dtype=torch.float32, device=q.device) if with_importance else None
+    spot_key_permutation(desc, q, k, perm, imp, ws)
+    return (perm, imp) if with_importance else perm
 
 
 @dataclass

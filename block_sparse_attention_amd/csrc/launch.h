@@ -78,4 +78,21 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 int decode_num_splits(int batch, int hkv, int nk);
 size_t decode_partials_bytes(int batch, int hq, int d, int nsplit);
 
+struct PermArgs {
+  const uint16_t* q;   // [batch, hq, L, d] bf16
+  const uint16_t* k;   // [batch, hkv, L, d] bf16
+  int32_t* perm;       // [batch, hkv, L]
+  float* importance;   // [batch, hkv, L] or nullptr
+  float* ws_lse;       // workspace: per-chunk (max, sum) of every last-block query row
+  float* ws_imp;       // workspace: per-row-group importance partials
+  int batch, hq, hkv, d, L, block, nb, segment, nchunks, ngroups;
+  float sm_scale;
+};
+hipError_t launch_key_permutation(const PermArgs& a, hipStream_t s);
+int perm_num_chunks(int L);
+int perm_num_groups(int G, int nr);
+size_t perm_workspace_bytes(int batch, int hkv, int L, int G, int nr);
+constexpr int kPermMaxSegment = 16384;
+constexpr int kPermRowsPerGroup = 256;   // query rows per workgroup in the permutation passes
+
 }  // namespace spot

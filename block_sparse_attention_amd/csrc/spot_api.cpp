@@ -135,6 +135,13 @@ int spot_workspace_size(const spot_desc* desc, int op, size_t* bytes) {
     case SPOT_OP_SELECT_TOPP:
     case SPOT_OP_PREFILL:
       break;
+    case SPOT_OP_KEY_PERMUTATION: {
+      if ((st = check_prefill_shape(desc))) return st;
+      const int nb = int(ceil_div64(desc->q_len, desc->block));
+      const int nr = int(desc->q_len - int64_t(nb - 1) * desc->block);
+      *bytes = spot::perm_workspace_bytes(desc->batch, desc->hkv, int(desc->q_len), desc->hq / desc->hkv, nr);
+      break;
+    }
     case SPOT_OP_DECODE: {
       const int nk = int(ceil_div64(desc->kv_len, desc->block));
       const int ns = spot::decode_num_splits(desc->batch, desc->hkv, nk);
@@ -254,6 +261,43 @@ int spot_sparse_attn_decode(const spot_desc* desc, const void* q, const void* k_
                      static_cast<float*>(workspace), desc->batch, desc->hq, desc->hkv, desc->d, int(desc->kv_len),
                      desc->block, nk, ns, effective_scale(desc)};
   return launched(spot::launch_decode(a, static_cast<hipStream_t>(stream)), "sparse_attn_decode");
+}
+
+int spot_key_permutation(const spot_desc* desc, const void* q, const void* k, int32_t* perm, float* importance,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_common(desc);
+  if (st) return st;
+  if ((st = check_prefill_shape(desc))) return st;
+  if (!q || !k || !perm) return fail(SPOT_ERR_INVALID, "q, k and perm are required");
+  if (desc->dtype != SPOT_BF16) return fail(SPOT_ERR_UNSUPPORTED, "key permutation supports bf16 only");
+  if (desc->segment <= 0) return fail(SPOT_ERR_INVALID, "segment must be > 0");
+  if (desc->segment > spot::kPermMaxSegment)
+    return fail(SPOT_ERR_UNSUPPORTED, "segment %d (max %d)", desc->segment, spot::kPermMaxSegment);
+  const int L = int(desc->q_len);
+  const int nb = int(ceil_div64(L, desc->block));
+  const int nr = L - (nb - 1) * desc->block;
+  const int G = desc->hq / desc->hkv;
+  const size_t need = spot::perm_workspace_bytes(desc->batch, desc->hkv, L, G, nr);
+  if ((st = check_workspace(need, workspace, workspace_bytes))) return st;
+  spot::PermArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.perm = perm;
+  a.importance = importance;
+  a.nchunks = spot::perm_num_chunks(L);
+  a.ngroups = spot::perm_num_groups(G, nr);
+  a.ws_lse = static_cast<float*>(workspace);
+  a.ws_imp = a.ws_lse + size_t(desc->batch) * desc->hkv * a.nchunks * a.ngroups * spot::kPermRowsPerGroup * 2;
+  a.batch = desc->batch;
+  a.hq = desc->hq;
+  a.hkv = desc->hkv;
+  a.d = desc->d;
+  a.L = L;
+  a.block = desc->block;
+  a.nb = nb;
+  a.segment = desc->segment;
+  a.sm_scale = effective_scale(desc);
+  return launched(spot::launch_key_permutation(a, static_cast<hipStream_t>(stream)), "key_permutation");
 }
 
 }  // extern "C"

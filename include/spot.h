@@ -2,12 +2,14 @@
  * spot.h - C ABI of the block-sparse causal attention library (libspot.so)
  * for AMD Instinct MI355X (gfx950).
  *
- * The library implements one hot path, in four calls:
+ * The library implements one hot path in four calls, plus the key permutation
+ * that feeds its permuted variant:
  *
  *   spot_block_score         score every (query block, key block) pair
  *   spot_select_topp         keep blocks by cumulative-mass top-p
  *   spot_sparse_attn_prefill online-softmax attention over the kept blocks (GQA prefill)
  *   spot_sparse_attn_decode  the same for one decode query per sequence
+ *   spot_key_permutation     the intra-segment key permutation the prefill gathers through
  *
  * Conventions shared by every call
  * --------------------------------
@@ -73,7 +75,8 @@ enum spot_op {
   SPOT_OP_BLOCK_SCORE = 0,
   SPOT_OP_SELECT_TOPP = 1,
   SPOT_OP_PREFILL = 2,
-  SPOT_OP_DECODE = 3
+  SPOT_OP_DECODE = 3,
+  SPOT_OP_KEY_PERMUTATION = 4
 };
 
 /* Problem descriptor.  `version` must be SPOT_ABI_VERSION. */
@@ -166,6 +169,22 @@ int spot_sparse_attn_prefill(const spot_desc* desc, const void* q, const void* k
 int spot_sparse_attn_decode(const spot_desc* desc, const void* q, const void* k_cache,
                             const void* v_cache, const int32_t* idx, const int32_t* cnt, void* o,
                             float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Key permutation by global importance ([PBS] §3; index arrays as in [S2O] §1).
+ * For KV head g, importance[t] = the causal softmax probability
+ * softmax_{t' <= r}(sm_scale * q_{h,r} . k_{t'})[t], averaged over the query
+ * rows r of the last query block and the G query heads h of the group (keys
+ * after r receive 0).  Inside each segment [sS, (s+1)S) the positions are
+ * sorted by importance descending, ties by position ascending:
+ * perm[b,g,sS + j] = the j-th of them (logical position -> physical row).
+ * q: [batch, hq, L, d] bf16; k: [batch, hkv, L, d] bf16; perm: int32
+ * [batch, hkv, L] (output); importance: float [batch, hkv, L] (nullable
+ * output).  Requires dtype bf16, segment > 0, a multiple of block and at most
+ * 16384.  Workspace: spot_workspace_size(SPOT_OP_KEY_PERMUTATION).
+ */
+int spot_key_permutation(const spot_desc* desc, const void* q, const void* k, int32_t* perm, float* importance,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -140,6 +140,21 @@ def test_indexer_and_decode_validation():
     assert call_decode(_decode(), o=None) == B.SPOT_ERR_INVALID
 
 
+def call_perm(d, q=FAKE, k=FAKE, perm=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return B.load_library().spot_key_permutation(ctypes.byref(d), q, k, perm, None, ws, ws_bytes, None)
+
+
+def test_key_permutation_validation():
+    assert call_perm(_prefill(segment=256, dtype=B.SPOT_F32)) == B.SPOT_ERR_UNSUPPORTED
+    assert call_perm(_prefill(segment=0)) == B.SPOT_ERR_INVALID
+    assert call_perm(_prefill(segment=96)) == B.SPOT_ERR_INVALID                 # not a multiple of the block
+    assert call_perm(_prefill(segment=32768, q_len=65536, kv_len=65536)) == B.SPOT_ERR_UNSUPPORTED
+    assert call_perm(_prefill(segment=256), perm=None) == B.SPOT_ERR_INVALID
+    assert call_perm(_prefill(segment=256), ws=None) == B.SPOT_ERR_WORKSPACE
+    assert call_perm(_prefill(segment=256), ws_bytes=64) == B.SPOT_ERR_WORKSPACE
+    assert B.spot_workspace_size(_prefill(segment=256), B.SPOT_OP_KEY_PERMUTATION) > 0
+
+
 def test_workspace_sizes():
     d = _prefill()
     assert B.spot_workspace_size(d, B.SPOT_OP_BLOCK_SCORE) == 3 * 1 * 2 * 16 * 128 * 4
