@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-sample-blocks", type=int, default=0, help="0: every query block")
+    ap.add_argument("--workload", default="gqa-bf16-L8192",
+                    help="prefill workload of the step: gqa-bf16-L8192 (default), heavy-perm-bf16-L32768 "
+                         "(permutation generated on the GPU inside the step), long-bf16-L131072, tiny-fp32-L256")
     return ap.parse_args()
 
 
@@ -83,23 +86,33 @@ def load_traffic(kernel_file: str, key: str):
 
 # ----------------------------------------------------------------- prefill
 def bench_prefill(args, torch, B, I):
-    cfg = I.C2
+    cfg = {c.name: c for c in (I.C1, I.C2, I.C3, I.C5)}[args.workload]
     dev = torch.device("cuda:0")
     q, k, v = I.prefill_inputs(cfg)
-    dq = torch.from_numpy(q).to(torch.bfloat16).to(dev)
-    dk = torch.from_numpy(k).to(torch.bfloat16).to(dev)
-    dv = torch.from_numpy(v).to(torch.bfloat16).to(dev)
-    desc = B.prefill_desc(dq, dk, cfg.block, cfg.top_p)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dq = torch.from_numpy(q).to(tdt).to(dev)
+    dk = torch.from_numpy(k).to(tdt).to(dev)
+    dv = torch.from_numpy(v).to(tdt).to(dev)
+    del v
+    desc = B.prefill_desc(dq, dk, cfg.block, cfg.top_p, segment=cfg.segment)
     bufs = B.alloc_prefill(desc, dev)
+    perm = perm_ws = None
+    if cfg.segment:
+        perm = torch.empty(dk.shape[0], dk.shape[1], dk.shape[2], dtype=torch.int32, device=dev)
+        perm_ws = torch.empty(B.spot_workspace_size(desc, B.SPOT_OP_KEY_PERMUTATION), dtype=torch.uint8, device=dev)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        B.spot_block_score(desc, dq, dk, None, None, None, None, bufs.scores, bufs.workspace)
+        if perm is not None:
+            B.spot_key_permutation(desc, dq, dk, perm, None, perm_ws)
+        if ev is not None:
+            ev[3].record()
+        B.spot_block_score(desc, dq, dk, perm, None, None, None, bufs.scores, bufs.workspace)
         B.spot_select_topp(desc, bufs.scores, bufs.idx, bufs.cnt)
         if ev is not None:
             ev[1].record()
-        B.spot_sparse_attn_prefill(desc, dq, dk, dv, None, bufs.idx, bufs.cnt, bufs.o, bufs.lse)
+        B.spot_sparse_attn_prefill(desc, dq, dk, dv, perm, bufs.idx, bufs.cnt, bufs.o, bufs.lse)
         if ev is not None:
             ev[2].record()
 
@@ -133,11 +146,12 @@ def bench_prefill(args, torch, B, I):
     ms_step = t0.elapsed_time(t1) / args.steps
 
     # per-kernel split with events on the launch stream (same work again)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for e in evs:
         step(e)
     torch.cuda.synchronize()
-    ms_sel = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_perm = float(np.mean([e[0].elapsed_time(e[3]) for e in evs])) if perm is not None else 0.0
+    ms_sel = float(np.mean([e[3].elapsed_time(e[1]) for e in evs]))
     ms_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
 
     idx = bufs.idx.cpu().numpy()
@@ -150,16 +164,19 @@ def bench_prefill(args, torch, B, I):
 
     attn_file = os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "kernels", "prefill.hip")
     achieved = flops / (ms_attn * 1e-3) / 1e12
+    if cfg.dtype == "bf16":
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                "traffic": load_traffic(attn_file, f"prefill_mfma_kernel@{cfg.name}"),
+                "kernel": "prefill_mfma_kernel<128,8>", "flop_per_launch": flops, "avg_launch_ms": round(ms_attn, 4)}
+    else:   # the fp32 row kernel on a 256-token input is launch-latency bound
+        roof = {"bound": "latency", "achieved": round(achieved, 4), "peak": None, "unit": "TFLOP/s", "frac": None,
+                "traffic": None, "kernel": "prefill_rows_kernel<float,64>", "flop_per_launch": flops,
+                "avg_launch_ms": round(ms_attn, 4)}
     res = dict(
-        cfg=cfg, ms_step=ms_step, ms_step_eager=ms_step_eager, ms_sel=ms_sel, ms_attn=ms_attn, flops=flops,
-        kept_fraction=kept_fraction,
-        value=flops / (ms_step * 1e-3) / 1e12,
-        roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                  "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                  "traffic": load_traffic(attn_file, "prefill_mfma_kernel@gqa-bf16-L8192"),
-                  "kernel": "prefill_mfma_kernel<128,8>", "flop_per_launch": flops,
-                  "avg_launch_ms": round(ms_attn, 4)},
-        host=(q, k, v), idx=idx, cnt=cnt,
+        cfg=cfg, ms_step=ms_step, ms_step_eager=ms_step_eager, ms_perm=ms_perm, ms_sel=ms_sel, ms_attn=ms_attn,
+        flops=flops, kept_fraction=kept_fraction, value=flops / (ms_step * 1e-3) / 1e12, roofline=roof,
+        host=(q, k, None), idx=idx, cnt=cnt,
     )
     return res
 
@@ -234,6 +251,10 @@ def bench_decode(args, torch, B, I):
 
 # ----------------------------------------------------------------- oracle on the host
 def cpu_baseline(res, I, sample_blocks: int):
+    """The float64 oracle on the host over the workload (or a seeded sample of
+    query blocks on the long ones): pool and score every block, select and
+    attend the sampled query blocks, permutation included when the workload
+    uses one."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -241,7 +262,9 @@ def cpu_baseline(res, I, sample_blocks: int):
     except Exception:
         threads = 1
     cfg = res["cfg"]
-    q, k, v = res["host"]
+    q, k, v = I.prefill_inputs(cfg)
+    if sample_blocks <= 0 and cfg.L > 16384:
+        sample_blocks = 8
     if sample_blocks <= 0 or sample_blocks >= cfg.nb:
         blocks = list(range(cfg.nb))
     else:
@@ -249,7 +272,10 @@ def cpu_baseline(res, I, sample_blocks: int):
         blocks = sorted({cfg.nb - 1} | set(rng.choice(cfg.nb, sample_blocks - 1, replace=False).tolist()))
     scale = 1 / math.sqrt(cfg.d)
     t0 = time.time()
-    out = oracle.prefill(q[0], k[0], v[0], cfg.block, cfg.top_p, qblocks=blocks)
+    perm = None
+    if cfg.segment:
+        perm, _ = oracle.key_permutation(q[0], k[0], cfg.block, cfg.segment, scale)
+    out = oracle.prefill(q[0], k[0], v[0], cfg.block, cfg.top_p, qblocks=blocks, segment=cfg.segment, perm=perm)
     dt = time.time() - t0
     G = cfg.hq // cfg.hkv
     nb = cfg.nb
@@ -262,10 +288,11 @@ def cpu_baseline(res, I, sample_blocks: int):
             sel[0, g, i] = True
     pairs = prefill_visible_pairs(idx, None, cfg.L, cfg.block, G)
     flops = 4.0 * cfg.d * float(pairs[sel].sum())
+    what = "every query block" if len(blocks) == nb else f"{len(blocks)} seeded query blocks"
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"float64 NumPy oracle, whole pipeline (pool and score every block, select and attend "
-                      f"{len(blocks)} seeded query blocks x {cfg.hkv} KV heads of {cfg.name})"}
+            "sample": f"float64 NumPy oracle, whole pipeline ({'permutation, ' if cfg.segment else ''}pool and "
+                      f"score every block, select and attend {what} x {cfg.hkv} KV heads of {cfg.name})"}
 
 
 def main():
@@ -298,12 +325,13 @@ def main():
     line = {
         "metric": METRIC, "value": round(pre["value"], 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(pre["ms_step"], 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.L, "hq": cfg.hq, "hkv": cfg.hkv,
                    "d": cfg.d, "block": cfg.block, "top_p": cfg.top_p, "n_sink": cfg.n_sink,
                    "n_recent": cfg.n_recent, "kept_fraction": round(pre["kept_fraction"], 4),
                    "ms_attention": round(pre["ms_attn"], 4), "ms_score_select": round(pre["ms_sel"], 4),
                    "ms_per_step_eager_launches": round(pre["ms_step_eager"], 4), "step_launch": "hip_graph_replay",
+                   "segment": cfg.segment, "ms_key_permutation": round(pre["ms_perm"], 4),
                    "flop_per_step": pre["flops"]},
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,

@@ -87,6 +87,9 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 #ifndef SPOT_PREFILL_WAVES
 #define SPOT_PREFILL_WAVES 8        // waves per workgroup (32 packed query rows each)
 #endif
+#ifndef SPOT_PREFILL_QG
+#define SPOT_PREFILL_QG 1           // groups of 32 query rows per wave (2: each LDS fragment feeds 2 MFMAs)
+#endif
 #ifndef SPOT_PREFILL_SCHED
 #define SPOT_PREFILL_SCHED 3        // 0: compiler default; 1, 2: iglp strategy 0 / 1; 3: raised wave priority over the MFMA block
 #endif
@@ -95,9 +98,11 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 #endif
 constexpr int kListCap = SPOT_PREFILL_LIST_CAP;
 
-template <int D, int NW, bool PERM>
-__global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a, int chunks, float scale_log2) {
+template <int D, int NW, int QG, bool PERM>
+__global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(PrefillArgs a, int chunks,
+                                                                               float scale_log2) {
   constexpr int NT = NW * 64;
+  constexpr int ROWS = NW * 32 * QG;                // packed query rows per workgroup
   // Row strides (elements): K rows start 4 banks apart (conflict-free 16-byte
   // fragment reads); V rows start 16 banks apart, so the four rows of a
   // transposing read cover all 64 banks.
@@ -119,20 +124,23 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int ql = lane & 31, hf = lane >> 5;
   const int GB = G * B;
-  const int pr = chunk * (NW * 32) + wv * 32 + ql;
-  const int prc = min(pr, GB - 1);
-  const int h = (pair % a.hkv) * G + prc / B;
-  const int r_raw = i * B + prc % B;
-  const bool qvalid = pr < GB && r_raw < L;
-  const int r = min(r_raw, L - 1);
 
-  // Q fragments (B operand of S^T = K Q^T): lane (query ql, half hf)
-  bf16x8_t qf[D / 16];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((size_t(b) * a.hq + h) * L + r) * D;
+  // each wave owns QG groups of 32 packed query rows; lane (query ql, half hf)
+  int hq_[QG], r_[QG];
+  bool qvalid[QG];
+  bf16x8_t qf[QG][D / 16];   // Q fragments (B operand of S^T = K Q^T)
+#pragma unroll
+  for (int gq = 0; gq < QG; ++gq) {
+    const int pr = chunk * ROWS + (wv * QG + gq) * 32 + ql;
+    const int prc = min(pr, GB - 1);
+    hq_[gq] = (pair % a.hkv) * G + prc / B;
+    const int r_raw = i * B + prc % B;
+    qvalid[gq] = pr < GB && r_raw < L;
+    r_[gq] = min(r_raw, L - 1);
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((size_t(b) * a.hq + hq_[gq]) * L + r_[gq]) * D;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + ks * 16 + hf * 8));
+      qf[gq][ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + ks * 16 + hf * 8));
   }
 
   const size_t row_id = size_t(pair) * a.nb + i;
@@ -202,26 +210,36 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
     }
   };
 
-  // S^T tile = K_tile Q^T (64 keys x 32 queries per wave)
-  auto qk = [&](const uint16_t* kt, f32x16_t (&s)[2]) {
+  // S^T tiles = K_tile Q^T (64 keys x 32 queries per group); each K fragment
+  // read from LDS feeds the QG groups
+  auto qk = [&](const uint16_t* kt, f32x16_t (&s)[QG][2]) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(&kt[(rt * 32 + ql) * KLD + hf * 8]);
-      s[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[0], f32x16_t{}, 0, 0, 0);
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq)
+        s[gq][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[gq][0], f32x16_t{}, 0, 0, 0);
     }
 #pragma unroll
     for (int ks = 1; ks < D / 16; ++ks)
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&kt[(rt * 32 + ql) * KLD + ks * 16 + hf * 8]);
-        s[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[rt], 0, 0, 0);
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq)
+          s[gq][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[gq][ks], s[gq][rt], 0, 0, 0);
       }
   };
 
-  f32x16_t oacc[D / 32];
+  f32x16_t oacc[QG][D / 32];
+  float m_run[QG], l_run[QG];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16_t{};
-  float m_run = -kInf, l_run = 0.f;
+  for (int gq = 0; gq < QG; ++gq) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) oacc[gq][dt] = f32x16_t{};
+    m_run[gq] = -kInf;
+    l_run[gq] = 0.f;
+  }
   const int jl = lane & 15, g16 = lane >> 4;
   const int vrow = 4 * (g16 >> 1) + (jl >> 2);          // key row within a 16-key step
   const int vcol = 16 * (g16 & 1) + 4 * (jl & 3);       // column within a 32-wide d tile
@@ -242,40 +260,44 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   put(Ks[1], KLD, kreg);
   put_kpos(kpos[1], mV);
   __syncthreads();
-  f32x16_t sa[2], sb[2];
+  f32x16_t sa[QG][2], sb[QG][2];
   qk(Ks[0], sa);
   __syncthreads();   // iteration 0 overwrites Ks[0]
 
   // One tile t: softmax of s_cur (scores of tile t) and PV(t); QK(t+1) -> s_nxt.
   // K runs one tile ahead of V: reads K(t+1) and V(t) from LDS, fetches
   // K(t+2) and V(t+1) from HBM, and maps tile t+3.
-  auto step = [&](int t, f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2]) {
+  auto step = [&](int t, f32x16_t (&s_cur)[QG][2], f32x16_t (&s_nxt)[QG][2]) {
     // (A) mask, max, rare rescale of the running state
-    if (t >= nfull) {
-      const int* kp = kpos[t % 3];
+    float msub[QG];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+    for (int gq = 0; gq < QG; ++gq) {
+      if (t >= nfull) {
+        const int* kp = kpos[t % 3];
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (kp[rt * 32 + 8 * (e >> 2) + 4 * hf + (e & 3)] > r) s_cur[rt][e] = -kInf;
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (kp[rt * 32 + 8 * (e >> 2) + 4 * hf + (e & 3)] > r_[gq]) s_cur[gq][rt][e] = -kInf;
+      }
+      float mx = __builtin_fmaxf(s_cur[gq][0][0], s_cur[gq][1][0]);
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s_cur[gq][0][e]), s_cur[gq][1][e]);
+      mx = xhalf_max(mx);
+      const float mcand = mx * scale_log2;
+      const bool need = mcand > m_run[gq] + kRescaleThreshold;
+      if (__ballot(need)) {
+        const float m_new = need ? mcand : m_run[gq];
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run[gq] - m_new) : 1.0f;
+        l_run[gq] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[gq][dt][e] *= alpha;
+        m_run[gq] = m_new;
+      }
+      msub[gq] = (m_run[gq] == -kInf) ? 0.f : m_run[gq];
     }
-    float mx = __builtin_fmaxf(s_cur[0][0], s_cur[1][0]);
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s_cur[0][e]), s_cur[1][e]);
-    mx = xhalf_max(mx);
-    const float mcand = mx * scale_log2;
-    const bool need = mcand > m_run + kRescaleThreshold;
-    if (__ballot(need)) {
-      const float m_new = need ? mcand : m_run;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
-      m_run = m_new;
-    }
-    const float msub = (m_run == -kInf) ? 0.f : m_run;
 
     // (B) straight-line: HBM fetches, next map, QK(t+1) on MFMA beside exp(t), PV(t)
     gather(rk, mK, kreg);
@@ -291,30 +313,40 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
     map_tile(t + 3, mN);
     qk(Ks[(t + 1) & 1], s_nxt);   // stale but in bounds on the last tile
     const uint16_t* vt = Vs[t & 1];
-    float rs = 0.f;   // row sum of the bf16-rounded P that enters the PV product
+    float rs[QG];   // row sums of the bf16-rounded P that enters the PV product
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq) rs[gq] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int rt = kk >> 1, hb = (kk & 1) * 8;
-      float pv[8];
+      bf16x8_t pf[QG];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(s_cur[rt][hb + e], scale_log2, -msub));
-      uint4 pp;
-      pp.x = pack_bf16x2(pv[0], pv[1]);
-      pp.y = pack_bf16x2(pv[2], pv[3]);
-      pp.z = pack_bf16x2(pv[4], pv[5]);
-      pp.w = pack_bf16x2(pv[6], pv[7]);
-      rs = dot2_bf16(pp.x, kOnes, dot2_bf16(pp.y, kOnes, dot2_bf16(pp.z, kOnes, dot2_bf16(pp.w, kOnes, rs))));
-      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pp);
+      for (int gq = 0; gq < QG; ++gq) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(s_cur[gq][rt][hb + e], scale_log2, -msub[gq]));
+        uint4 pp;
+        pp.x = pack_bf16x2(pv[0], pv[1]);
+        pp.y = pack_bf16x2(pv[2], pv[3]);
+        pp.z = pack_bf16x2(pv[4], pv[5]);
+        pp.w = pack_bf16x2(pv[6], pv[7]);
+        rs[gq] = dot2_bf16(pp.x, kOnes, dot2_bf16(pp.y, kOnes, dot2_bf16(pp.z, kOnes, dot2_bf16(pp.w, kOnes, rs[gq]))));
+        pf[gq] = __builtin_bit_cast(bf16x8_t, pp);
+      }
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const uint16_t* base = &vt[(kk * 16 + vrow) * VLD + dt * 32 + vcol];
         const uint2 lo = lds_read_tr16(base);              // keys kk*16 + 4*hf + 0..3
         const uint2 hi = lds_read_tr16(base + 8 * VLD);    // keys kk*16 + 8 + 4*hf + 0..3
         const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[dt], 0, 0, 0);
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq)
+          oacc[gq][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[gq], oacc[gq][dt], 0, 0, 0);
       }
     }
-    l_run += rs;
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq) l_run[gq] += rs[gq];
 #if SPOT_PREFILL_SCHED == 3
     __builtin_amdgcn_s_setprio(0);
 #endif
@@ -336,20 +368,24 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   }
   if (t < ntiles) step(t, sa, sb);
 
-  const float l_tot = xhalf_sum(l_run);
-  if (qvalid) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* orow = static_cast<uint16_t*>(a.o) + ((size_t(b) * a.hq + h) * L + r) * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+  for (int gq = 0; gq < QG; ++gq) {
+    const float l_tot = xhalf_sum(l_run[gq]);
+    if (qvalid[gq]) {
+      const float inv = 1.0f / l_tot;
+      uint16_t* orow = static_cast<uint16_t*>(a.o) + ((size_t(b) * a.hq + hq_[gq]) * L + r_[gq]) * D;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        uint2 w;
-        w.x = pack_bf16x2(oacc[dt][jj * 4 + 0] * inv, oacc[dt][jj * 4 + 1] * inv);
-        w.y = pack_bf16x2(oacc[dt][jj * 4 + 2] * inv, oacc[dt][jj * 4 + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * jj + 4 * hf) = w;
-      }
-    if (a.lse && hf == 0) a.lse[(size_t(b) * a.hq + h) * L + r] = (m_run + __log2f(l_tot)) * kLn2;
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          uint2 w;
+          w.x = pack_bf16x2(oacc[gq][dt][jj * 4 + 0] * inv, oacc[gq][dt][jj * 4 + 1] * inv);
+          w.y = pack_bf16x2(oacc[gq][dt][jj * 4 + 2] * inv, oacc[gq][dt][jj * 4 + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * jj + 4 * hf) = w;
+        }
+      if (a.lse && hf == 0)
+        a.lse[(size_t(b) * a.hq + hq_[gq]) * L + r_[gq]] = (m_run[gq] + __log2f(l_tot)) * kLn2;
+    }
   }
 }
 
@@ -442,13 +478,14 @@ __global__ __launch_bounds__(256) void prefill_rows_kernel(PrefillArgs a, float 
 template <int D>
 static hipError_t launch_mfma(const PrefillArgs& a, hipStream_t s, float scale_log2) {
   constexpr int NW = SPOT_PREFILL_WAVES;
+  constexpr int QG = SPOT_PREFILL_QG;
   const int G = a.hq / a.hkv;
-  const int chunks = (G * a.block + NW * 32 - 1) / (NW * 32);
+  const int chunks = (G * a.block + NW * 32 * QG - 1) / (NW * 32 * QG);
   const long long units = (long long)a.batch * a.hkv * a.nb * chunks;
   if (a.perm)
-    prefill_mfma_kernel<D, NW, true><<<dim3(unsigned(units)), NW * 64, 0, s>>>(a, chunks, scale_log2);
+    prefill_mfma_kernel<D, NW, QG, true><<<dim3(unsigned(units)), NW * 64, 0, s>>>(a, chunks, scale_log2);
   else
-    prefill_mfma_kernel<D, NW, false><<<dim3(unsigned(units)), NW * 64, 0, s>>>(a, chunks, scale_log2);
+    prefill_mfma_kernel<D, NW, QG, false><<<dim3(unsigned(units)), NW * 64, 0, s>>>(a, chunks, scale_log2);
   return hipGetLastError();
 }
 
