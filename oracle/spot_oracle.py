@@ -31,6 +31,11 @@ What each function follows:
                      the last position, softmax over the kept blocks
   key_permutation    [PBS] §3 (importance from the last query block by mean
                      pooling of attention, keys sorted descending per segment)
+  history_order      [S2O] §2 (candidate blocks visited in descending estimated
+                     importance)
+  attend_prefill_es  [S2O] §2 (monotone-gain early stopping) and §3 (dense
+                     causal pass over the own segment, then the permuted
+                     history in that order, resuming the same softmax state)
 
 Readings taken where the pages leave a step open (each is also listed with the
 design notes): the block distribution for top-p is the softmax of the block
@@ -40,6 +45,10 @@ crossing is inclusive; ties go to the lower block index; p >= 1 keeps every
 residual block and p <= 0 keeps none; history blocks (earlier segments) are
 read through the permutation and fully visible, blocks of the query's own
 segment are read in natural order under the positional causal mask.
+Early stopping: the stop rule is applied per query row; the marginal gain of a
+history block is the softmax mass its keys add and it is compared with the
+mass accumulated including that block (stop once gain < tau * accumulated);
+the block that triggers the stop is kept.
 """
 from __future__ import annotations
 
@@ -316,6 +325,115 @@ def key_permutation(q, k, block, segment, sm_scale):
             ts = np.arange(s0, min(s0 + segment, L))
             perm[g, ts] = ts[np.lexsort((ts, -imp[g, ts]))]
     return perm, imp
+
+
+# ----------------------------------------------------------------- early stopping
+def history_order(scores, block, segment, rows=None):
+    """[S2O] §2: the history blocks of query block i (those in segments
+    before i's segment) in descending block score, ties by block index.
+
+    scores: (Hkv, nB, nB).  Returns order[g][i] -> int array (empty for the
+    first segment); entries for query blocks outside `rows` are None.
+    """
+    hkv, nb, _ = scores.shape
+    rows = range(nb) if rows is None else rows
+    order = [[None] * nb for _ in range(hkv)]
+    for g in range(hkv):
+        for i in rows:
+            i = int(i)
+            n_hist = ((i * block) // segment) * segment // block
+            js = np.arange(n_hist)
+            order[g][i] = js[np.lexsort((js, -np.asarray(scores[g, i, :n_hist], dtype=np.float64)))]
+    return order
+
+
+def _es_blocks(q, k, i, g, h, order_gi, block, segment, sm_scale, perm):
+    """Masses of one query block's rows for head h, in one fixed frame.
+
+    Returns (e_own, own_phys, e_hist, hist_phys, shift): e_own (rows, n_own)
+    = exp(logit - shift) over the own-segment keys (0 where the causal mask
+    hides the key), e_hist (rows, n_hist_blocks, B) the same for the history
+    blocks in visiting order, shift (rows,) the row's largest visible logit.
+    """
+    L = q.shape[1]
+    rows = block_rows(i, block, L)
+    s0 = ((i * block) // segment) * segment
+    own = np.arange(s0, min(rows[-1] + 1, L))
+    hist = [perm[g, block_rows(int(j), block, L)] if perm is not None else block_rows(int(j), block, L)
+            for j in order_gi]
+    hist_phys = np.stack(hist) if hist else np.zeros((0, block), dtype=np.int64)
+    lo = sm_scale * (q[h, rows] @ k[g, own].T)
+    lo = np.where(own[None, :] <= rows[:, None], lo, -np.inf)
+    lh = sm_scale * np.einsum('rd,nbd->rnb', q[h, rows], k[g, hist_phys]) if hist else \
+        np.zeros((rows.shape[0], 0, block))
+    shift = lo.max(axis=1)
+    if hist:
+        shift = np.maximum(shift, lh.max(axis=(1, 2)))
+    return np.exp(lo - shift[:, None]), own, np.exp(lh - shift[:, None, None]), hist_phys, shift
+
+
+def es_gain_ratios(q, k, i, g, h, order_gi, block, segment, sm_scale, perm=None):
+    """[S2O] §2: for each row of query block i and head h, the marginal gain
+    of each visited history block relative to the mass accumulated including
+    it: ratio[r, n] = gain_n / (own mass + gain_1 + ... + gain_n)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    e_own, _, e_hist, _, _ = _es_blocks(q, k, i, g, h, order_gi, block, segment, sm_scale, perm)
+    gain = e_hist.sum(axis=2)
+    acc = e_own.sum(axis=1)[:, None] + np.cumsum(gain, axis=1)
+    return gain / acc
+
+
+def attend_prefill_es(q, k, v, order, block, segment, sm_scale, tau, perm=None, qblocks=None,
+                      nused=None):
+    """[S2O] §2-3 early-stopped attention for every query row.
+
+    Pass 1: the row's own segment in natural order under the causal mask.
+    Pass 2: the history blocks order[g][i] (rows through `perm`, all visible)
+    one at a time; after each, the row stops once the block's gain is below
+    tau times the mass accumulated so far (that block included).  The output
+    is the softmax attention over the own-segment keys and the visited blocks.
+
+    nused (Hq, L) int, optional: use these numbers of visited history blocks
+    instead of the rule (to evaluate the output at another implementation's
+    decisions).  Returns O (Hq, L, d), LSE (Hq, L) and the numbers of visited
+    history blocks (Hq, L); rows outside `qblocks` are NaN / -1.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    hq, L, d = q.shape
+    hkv = k.shape[0]
+    G = hq // hkv
+    nb = n_blocks(L, block)
+    qblocks = range(nb) if qblocks is None else qblocks
+    o = np.full((hq, L, d), np.nan)
+    lse = np.full((hq, L), np.nan)
+    used = np.full((hq, L), -1, dtype=np.int64)
+    for g in range(hkv):
+        for i in qblocks:
+            i = int(i)
+            rows = block_rows(i, block, L)
+            for h in range(g * G, (g + 1) * G):
+                e_own, own, e_hist, hist_phys, shift = _es_blocks(
+                    q, k, i, g, h, order[g][i], block, segment, sm_scale, perm)
+                n_h = e_hist.shape[1]
+                gain = e_hist.sum(axis=2)
+                acc = e_own.sum(axis=1)[:, None] + np.cumsum(gain, axis=1)
+                for ri, r in enumerate(rows):
+                    if nused is not None:
+                        n = int(nused[h, r])
+                    else:
+                        below = np.nonzero(gain[ri] < tau * acc[ri])[0]
+                        n = int(below[0]) + 1 if below.size else n_h
+                    z = e_own[ri].sum() + e_hist[ri, :n].sum()
+                    num = e_own[ri] @ v[g, own]
+                    if n:
+                        num = num + e_hist[ri, :n].reshape(-1) @ v[g, hist_phys[:n].reshape(-1)]
+                    o[h, r] = num / z
+                    lse[h, r] = shift[ri] + np.log(z)
+                    used[h, r] = n
+    return o, lse, used
 
 
 # ----------------------------------------------------------------- pipelines
