@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-early-stop", action="store_true", help="skip the early-stopping measurement")
+    ap.add_argument("--es-tau", type=float, default=0.01, help="early-stopping threshold tau")
     ap.add_argument("--cpu-sample-blocks", type=int, default=0, help="0: every query block")
     ap.add_argument("--workload", default="gqa-bf16-L8192",
                     help="prefill workload of the step: gqa-bf16-L8192 (default), heavy-perm-bf16-L32768 "
@@ -249,6 +251,95 @@ def bench_decode(args, torch, B, I):
     )
 
 
+# ----------------------------------------------------------------- early stopping
+def bench_early_stop(args, torch, B, I):
+    """Early-stopped prefill on the heavy-hitter workload (L=32768, segment
+    2048): key permutation, block scores, history visiting order and the
+    early-stopped attention, captured as one HIP graph."""
+    cfg = I.C3
+    dev = torch.device("cuda:0")
+    q, k, v = I.prefill_inputs(cfg)
+    dq = torch.from_numpy(q).to(torch.bfloat16).to(dev)
+    dk = torch.from_numpy(k).to(torch.bfloat16).to(dev)
+    dv = torch.from_numpy(v).to(torch.bfloat16).to(dev)
+    del q, k, v
+    tau = args.es_tau
+    desc = B.prefill_desc(dq, dk, cfg.block, 1.0, segment=cfg.segment)
+    bufs = B.alloc_prefill_early_stop(desc, dev)
+    perm = torch.empty(dk.shape[0], dk.shape[1], dk.shape[2], dtype=torch.int32, device=dev)
+    perm_ws = torch.empty(B.spot_workspace_size(desc, B.SPOT_OP_KEY_PERMUTATION), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        B.spot_key_permutation(desc, dq, dk, perm, None, perm_ws)
+        if ev is not None:
+            ev[1].record()
+        B.spot_block_score(desc, dq, dk, perm, None, None, None, bufs.scores, bufs.workspace)
+        B.spot_order_history(desc, bufs.scores, bufs.order, bufs.cnt)
+        if ev is not None:
+            ev[2].record()
+        B.spot_sparse_attn_prefill_early_stop(desc, tau, dq, dk, dv, perm, bufs.order, bufs.cnt, bufs.o, bufs.lse,
+                                              bufs.nused)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    ms_perm = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_front = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    # work: each row's own-segment keys (causal) plus the history blocks it took
+    nused = bufs.nused.cpu().numpy()[0].astype(np.int64)          # (hq, L)
+    L, Bk, S = cfg.L, cfg.block, cfg.segment
+    r = np.arange(L)
+    own = r - (r // S) * S + 1
+    pairs_row = own[None, :] + nused * Bk
+    flops = 4.0 * cfg.d * float(pairs_row.sum())
+    dense_pairs = cfg.hq * L * (L + 1) / 2
+    # keys the workgroups walked: a workgroup (256 packed rows of one KV head
+    # and query block) runs until its last row has stopped
+    G = cfg.hq // cfg.hkv
+    packed = nused.reshape(cfg.hkv, G, cfg.nb, Bk).transpose(0, 2, 1, 3).reshape(cfg.hkv, cfg.nb, G * Bk)
+    own_packed = np.tile(own.reshape(cfg.nb, Bk), (1, G))                 # (nb, G*Bk)
+    walked = 0.0
+    for c0 in range(0, G * Bk, 256):
+        part = packed[..., c0:c0 + 256]
+        walked += float((own_packed[None, :, c0:c0 + 256] + part.max(axis=-1, keepdims=True) * Bk).sum())
+    achieved = flops / (ms_attn * 1e-3) / 1e12
+    return dict(
+        workload=cfg.name, tau=tau, value=round(flops / (ms_step * 1e-3) / 1e12, 2), unit="TFLOP/s",
+        ms_per_step=round(ms_step, 4), ms_key_permutation=round(ms_perm, 4), ms_score_order=round(ms_front, 4),
+        ms_attention=round(ms_attn, 4), taken_fraction=round(float(pairs_row.sum()) / dense_pairs, 4),
+        walked_fraction=round(walked / dense_pairs, 4), mean_history_blocks=round(float(nused.mean()), 2),
+        flop_per_step=flops,
+        roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                  "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                  "kernel": "prefill_mfma_kernel<128,8,early stop>", "avg_launch_ms": round(ms_attn, 4),
+                  "walked_tflops": round(4.0 * cfg.d * walked / (ms_attn * 1e-3) / 1e12, 2)},
+    )
+
+
 # ----------------------------------------------------------------- oracle on the host
 def cpu_baseline(res, I, sample_blocks: int):
     """The float64 oracle on the host over the workload (or a seeded sample of
@@ -316,6 +407,10 @@ def main():
     if not args.no_decode:
         dec = bench_decode(args, torch, B, I)
         print(f"[bench] decode: {dec}", file=sys.stderr, flush=True)
+    es = None
+    if not args.no_early_stop:
+        es = bench_early_stop(args, torch, B, I)
+        print(f"[bench] early stop: {es}", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(pre, I, args.cpu_sample_blocks)
@@ -336,6 +431,7 @@ def main():
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,
         "decode": dec,
+        "early_stop": es,
     }
     print(json.dumps(line))
 

@@ -19,10 +19,12 @@ SPOT_OK, SPOT_ERR_INVALID, SPOT_ERR_UNSUPPORTED, SPOT_ERR_WORKSPACE, SPOT_ERR_LA
 SPOT_F32, SPOT_BF16 = 0, 1
 SPOT_SCORE_MEANPOOL, SPOT_SCORE_RELU_INDEXER = 0, 1
 SPOT_OP_BLOCK_SCORE, SPOT_OP_SELECT_TOPP, SPOT_OP_PREFILL, SPOT_OP_DECODE, SPOT_OP_KEY_PERMUTATION = 0, 1, 2, 3, 4
+SPOT_OP_ORDER_HISTORY, SPOT_OP_PREFILL_EARLY_STOP = 5, 6
 ABI_VERSION = 1
 
 EXPORTS = ("spot_version", "spot_status_string", "spot_last_error", "spot_workspace_size", "spot_block_score",
-           "spot_select_topp", "spot_sparse_attn_prefill", "spot_sparse_attn_decode", "spot_key_permutation")
+           "spot_select_topp", "spot_sparse_attn_prefill", "spot_sparse_attn_decode", "spot_key_permutation",
+           "spot_order_history", "spot_sparse_attn_prefill_early_stop")
 
 
 class spot_desc(ctypes.Structure):
@@ -66,6 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spot_sparse_attn_prefill.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
     lib.spot_sparse_attn_decode.argtypes = [D, P, P, P, P, P, P, P, P, S, P]
     lib.spot_key_permutation.argtypes = [D, P, P, P, P, P, S, P]
+    lib.spot_order_history.argtypes = [D, P, P, P, P, S, P]
+    lib.spot_sparse_attn_prefill_early_stop.argtypes = [D, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, S, P]
     for name in EXPORTS[3:]:
         getattr(lib, name).restype = I
     _lib = lib
@@ -136,6 +140,22 @@ def spot_key_permutation(desc, q, k, perm, importance=None, workspace=None, stre
     st = load_library().spot_key_permutation(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(perm), _ptr(importance),
                                              _ptr(workspace), ws_bytes, _stream() if stream is None else stream)
     _check("spot_key_permutation", st)
+
+
+def spot_order_history(desc, scores, order, cnt, workspace=None, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load_library().spot_order_history(ctypes.byref(desc), _ptr(scores), _ptr(order), _ptr(cnt), _ptr(workspace),
+                                           ws_bytes, _stream() if stream is None else stream)
+    _check("spot_order_history", st)
+
+
+def spot_sparse_attn_prefill_early_stop(desc, tau, q, k, v, perm, order, cnt, o, lse=None, nused=None,
+                                        workspace=None, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load_library().spot_sparse_attn_prefill_early_stop(
+        ctypes.byref(desc), float(tau), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(order), _ptr(cnt), _ptr(o),
+        _ptr(lse), _ptr(nused), _ptr(workspace), ws_bytes, _stream() if stream is None else stream)
+    _check("spot_sparse_attn_prefill_early_stop", st)
 
 
 # ----------------------------------------------------------------- descriptors
@@ -234,6 +254,54 @@ def key_permutation(q, k, block: int, segment: int, *, sm_scale: float = 0.0, wi
     imp = torch.empty(perm.shape, dtype=torch.float32, device=q.device) if with_importance else None
     spot_key_permutation(desc, q, k, perm, imp, ws)
     return (perm, imp) if with_importance else perm
+
+
+@dataclass
+class EarlyStopBuffers:
+    scores: torch.Tensor
+    order: torch.Tensor
+    cnt: torch.Tensor
+    o: torch.Tensor
+    lse: torch.Tensor
+    nused: torch.Tensor
+    workspace: torch.Tensor
+
+
+def alloc_prefill_early_stop(desc: spot_desc, device) -> EarlyStopBuffers:
+    nb = -(-desc.q_len // desc.block)
+    rows = (desc.batch, desc.hkv, nb)
+    ws = spot_workspace_size(desc, SPOT_OP_BLOCK_SCORE)
+    return EarlyStopBuffers(
+        scores=torch.empty(*rows, nb, dtype=torch.float32, device=device),
+        order=torch.empty(*rows, nb, dtype=torch.int32, device=device),
+        cnt=torch.empty(*rows, dtype=torch.int32, device=device),
+        o=torch.empty(desc.batch, desc.hq, desc.q_len, desc.d, dtype=torch.bfloat16, device=device),
+        lse=torch.empty(desc.batch, desc.hq, desc.q_len, dtype=torch.float32, device=device),
+        nused=torch.empty(desc.batch, desc.hq, desc.q_len, dtype=torch.int32, device=device),
+        workspace=torch.empty(max(ws, 1), dtype=torch.uint8, device=device),
+    )
+
+
+def prefill_early_stop(q, k, v, block: int, segment: int, tau: float, *, perm=None, sm_scale: float = 0.0,
+                       bufs: EarlyStopBuffers | None = None) -> EarlyStopBuffers:
+    """Early-stopped prefill: block scores -> history visiting order ->
+    attention that stops taking history blocks per row once their gain
+    falls below tau.
+
+    q (batch, hq, L, d), k/v (batch, hkv, L, d) bf16 device tensors;
+    perm (batch, hkv, L) int32 or None.
+    """
+    desc = prefill_desc(q, k, block, 1.0, segment=segment, sm_scale=sm_scale)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, dtype=torch.bfloat16)
+    if perm is not None:
+        _require(perm, "perm", dtype=torch.int32, shape=(k.shape[0], k.shape[1], k.shape[2]))
+    if bufs is None:
+        bufs = alloc_prefill_early_stop(desc, q.device)
+    spot_block_score(desc, q, k, perm, None, None, None, bufs.scores, bufs.workspace)
+    spot_order_history(desc, bufs.scores, bufs.order, bufs.cnt)
+    spot_sparse_attn_prefill_early_stop(desc, tau, q, k, v, perm, bufs.order, bufs.cnt, bufs.o, bufs.lse, bufs.nused)
+    return bufs
 
 
 @dataclass

@@ -98,7 +98,13 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 #endif
 constexpr int kListCap = SPOT_PREFILL_LIST_CAP;
 
-template <int D, int NW, int QG, bool PERM>
+// ES: early-stopped variant (S2O section 2 and 3).  The workgroup first walks
+// its own segment's blocks (causal), then the history blocks in the given
+// visiting order; after each history block every row compares the block's
+// softmax mass with the mass accumulated so far (that block included) and
+// stops taking further blocks once it is below tau.  A stopped row adds
+// nothing more; the workgroup leaves the loop when all its rows have stopped.
+template <int D, int NW, int QG, bool PERM, bool ES>
 __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(PrefillArgs a, int chunks,
                                                                                float scale_log2) {
   constexpr int NT = NW * 64;
@@ -114,6 +120,8 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKT * VLD];
   __shared__ int kpos[3][kKT];
   __shared__ int s_list[kListCap > 0 ? kListCap : 1];
+  __shared__ int s_act[2][NW];   // early stop: per-wave "a row is still taking blocks", by tile parity
+  static_assert(!ES || kListCap >= kEsMaxBlocks, "early stopping stages its visiting list in LDS");
 
   const int pairs = a.batch * a.hkv;
   int pair, i, chunk;
@@ -144,13 +152,25 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
   }
 
   const size_t row_id = size_t(pair) * a.nb + i;
-  const int nkept = a.cnt[row_id];
   const int32_t* glist = a.idx + row_id * a.nb;
-  if constexpr (kListCap > 0)
-    for (int k = tid; k < min(nkept, kListCap); k += NT) s_list[k] = glist[k];
-  const int* lst = (kListCap > 0 && nkept <= kListCap) ? s_list : glist;
   const int lgB = 31 - __builtin_clz(B);
-  const int seg_start = (PERM && a.segment > 0) ? ((i * B) / a.segment) * a.segment : 0;
+  const int seg_start = ((PERM || ES) && a.segment > 0) ? ((i * B) / a.segment) * a.segment : 0;
+  int nkept, own_tiles = 0;
+  const int* lst;
+  if constexpr (ES) {
+    // own segment's blocks ascending, then the history blocks in visiting order
+    const int sblk = seg_start >> lgB;
+    const int n_own = i - sblk + 1;
+    nkept = n_own + min(max(a.cnt[row_id], 0), sblk);   // at most the blocks before the segment
+    for (int k = tid; k < nkept; k += NT) s_list[k] = k < n_own ? sblk + k : glist[k - n_own];
+    lst = s_list;
+    own_tiles = (n_own * B) / kKT;
+  } else {
+    nkept = a.cnt[row_id];
+    if constexpr (kListCap > 0)
+      for (int k = tid; k < min(nkept, kListCap); k += NT) s_list[k] = glist[k];
+    lst = (kListCap > 0 && nkept <= kListCap) ? s_list : glist;
+  }
   const int32_t* permg = PERM ? a.perm + size_t(pair) * L : nullptr;
   const int ntiles = (nkept * B + kKT - 1) / kKT;
   // tiles before the last kept block need no mask (history and earlier own-segment blocks are visible)
@@ -179,7 +199,7 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
       const bool inl = bi < nkept && cid < kKT * CPR;
       const int base = lst[inl ? bi : 0] << lgB;
       const int pos = base + (s & (B - 1));
-      const bool valid = inl && pos < L;
+      const bool valid = inl && unsigned(pos) < unsigned(L);
       const bool hist = base < seg_start;
       int phys = pos;
       if constexpr (PERM) {
@@ -232,14 +252,21 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
   };
 
   f32x16_t oacc[QG][D / 32];
-  float m_run[QG], l_run[QG];
+  float m_run[QG], l_run[QG];   // ES: l_run is the whole row's sum (both lane halves); else this half's
+  float dsum[QG];               // ES: mass of the history block in progress
+  int nused[QG];                // ES: history blocks taken
+  bool active[QG];              // ES: the row still takes blocks
 #pragma unroll
   for (int gq = 0; gq < QG; ++gq) {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) oacc[gq][dt] = f32x16_t{};
     m_run[gq] = -kInf;
     l_run[gq] = 0.f;
+    dsum[gq] = 0.f;
+    nused[gq] = 0;
+    active[gq] = true;
   }
+  const int tpb = B / kKT;   // ES: tiles per block (block >= 64)
   const int jl = lane & 15, g16 = lane >> 4;
   const int vrow = 4 * (g16 >> 1) + (jl >> 2);          // key row within a 16-key step
   const int vcol = 16 * (g16 & 1) + 4 * (jl & 3);       // column within a 32-wide d tile
@@ -267,12 +294,12 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
   // One tile t: softmax of s_cur (scores of tile t) and PV(t); QK(t+1) -> s_nxt.
   // K runs one tile ahead of V: reads K(t+1) and V(t) from LDS, fetches
   // K(t+2) and V(t+1) from HBM, and maps tile t+3.
-  auto step = [&](int t, f32x16_t (&s_cur)[QG][2], f32x16_t (&s_nxt)[QG][2]) {
+  auto step = [&](int t, f32x16_t (&s_cur)[QG][2], f32x16_t (&s_nxt)[QG][2]) -> bool {
     // (A) mask, max, rare rescale of the running state
     float msub[QG];
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
-      if (t >= nfull) {
+      if (ES ? (t < own_tiles && t >= own_tiles - tpb) : (t >= nfull)) {
         const int* kp = kpos[t % 3];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -285,11 +312,12 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
       for (int e = 1; e < 16; ++e) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s_cur[gq][0][e]), s_cur[gq][1][e]);
       mx = xhalf_max(mx);
       const float mcand = mx * scale_log2;
-      const bool need = mcand > m_run[gq] + kRescaleThreshold;
+      const bool need = active[gq] && mcand > m_run[gq] + kRescaleThreshold;
       if (__ballot(need)) {
         const float m_new = need ? mcand : m_run[gq];
         const float alpha = need ? __builtin_amdgcn_exp2f(m_run[gq] - m_new) : 1.0f;
         l_run[gq] *= alpha;
+        if constexpr (ES) dsum[gq] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -297,6 +325,7 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
         m_run[gq] = m_new;
       }
       msub[gq] = (m_run[gq] == -kInf) ? 0.f : m_run[gq];
+      if constexpr (ES) msub[gq] = active[gq] ? msub[gq] : kInf;   // a stopped row's exponentials are 0
     }
 
     // (B) straight-line: HBM fetches, next map, QK(t+1) on MFMA beside exp(t), PV(t)
@@ -345,11 +374,35 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
           oacc[gq][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[gq], oacc[gq][dt], 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int gq = 0; gq < QG; ++gq) l_run[gq] += rs[gq];
 #if SPOT_PREFILL_SCHED == 3
     __builtin_amdgcn_s_setprio(0);
 #endif
+    bool block_end = false;
+    if constexpr (ES) {
+      block_end = t >= own_tiles && ((t - own_tiles + 1) % tpb) == 0;
+      bool any = false;
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq) {
+        const float rsum = xhalf_sum(rs[gq]);
+        l_run[gq] += rsum;
+        if (t >= own_tiles) dsum[gq] += rsum;
+        if (block_end) {
+          if (active[gq]) {
+            ++nused[gq];
+            if (dsum[gq] < a.tau * l_run[gq]) active[gq] = false;
+          }
+          dsum[gq] = 0.f;
+        }
+        any = any || active[gq];
+      }
+      if (block_end) {
+        const bool wave_any = __ballot(any) != 0;   // whole wave: block_end is uniform
+        if (lane == 0) s_act[t & 1][wv] = wave_any;
+      }
+    } else {
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq) l_run[gq] += rs[gq];
+    }
 
     // (C) stage K(t+2) and V(t+1)
     put(Ks[t & 1], KLD, kreg);
@@ -358,20 +411,31 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
     __syncthreads();
     mV = mK;
     mK = mN;
+    if constexpr (ES) {
+      if (block_end) {
+        int any = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) any |= s_act[t & 1][w];
+        return any != 0;
+      }
+    }
+    return true;
   };
 
   // unrolled by two so the score tiles alternate between register sets
   int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    step(t, sa, sb);
-    step(t + 1, sb, sa);
+  bool go = true;
+  for (; go && t + 1 < ntiles; t += 2) {
+    go = step(t, sa, sb);
+    if (go) go = step(t + 1, sb, sa);
   }
-  if (t < ntiles) step(t, sa, sb);
+  if (go && t < ntiles) step(t, sa, sb);
 
 #pragma unroll
   for (int gq = 0; gq < QG; ++gq) {
-    const float l_tot = xhalf_sum(l_run[gq]);
+    const float l_tot = ES ? l_run[gq] : xhalf_sum(l_run[gq]);
     if (qvalid[gq]) {
+      if (ES && a.nused && hf == 0) a.nused[(size_t(b) * a.hq + hq_[gq]) * L + r_[gq]] = nused[gq];
       const float inv = 1.0f / l_tot;
       uint16_t* orow = static_cast<uint16_t*>(a.o) + ((size_t(b) * a.hq + hq_[gq]) * L + r_[gq]) * D;
 #pragma unroll
@@ -482,10 +546,17 @@ static hipError_t launch_mfma(const PrefillArgs& a, hipStream_t s, float scale_l
   const int G = a.hq / a.hkv;
   const int chunks = (G * a.block + NW * 32 * QG - 1) / (NW * 32 * QG);
   const long long units = (long long)a.batch * a.hkv * a.nb * chunks;
-  if (a.perm)
-    prefill_mfma_kernel<D, NW, QG, true><<<dim3(unsigned(units)), NW * 64, 0, s>>>(a, chunks, scale_log2);
-  else
-    prefill_mfma_kernel<D, NW, QG, false><<<dim3(unsigned(units)), NW * 64, 0, s>>>(a, chunks, scale_log2);
+  const dim3 grid{unsigned(units)};
+  if (a.es) {
+    if (a.perm)
+      prefill_mfma_kernel<D, NW, QG, true, true><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
+    else
+      prefill_mfma_kernel<D, NW, QG, false, true><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
+  } else if (a.perm) {
+    prefill_mfma_kernel<D, NW, QG, true, false><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
+  } else {
+    prefill_mfma_kernel<D, NW, QG, false, false><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
+  }
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ constexpr int kSelMaxPerThread = 16;   // candidates per thread (16384 / 1024)
 constexpr int kSortMax = 2048;         // candidates sorted exactly in LDS
 
 __device__ __forceinline__ uint32_t score_key(float s) {
-  const uint32_t u = __float_as_uint(s);
+  const uint32_t u = __float_as_uint(s) == 0x80000000u ? 0u : __float_as_uint(s);   // -0 ties with +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 __device__ __forceinline__ float key_score(uint32_t k) {
@@ -368,6 +368,51 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
     if (k) keepm |= 1u << e;
   }
   write_row(a, row, keepm, c0, sc);
+}
+
+// Visiting order of the history blocks for early-stopped attention (S2O
+// section 2: candidates are processed in descending estimated importance).
+// One workgroup per (batch, KV head, query block) row: the blocks of earlier
+// segments are sorted in LDS by a bitonic network on 64-bit keys (inverted
+// order-preserving score bits above the block id: ascending keys are
+// score-descending with ties to the lower id).
+constexpr int kOrderThreads = 256;
+__global__ __launch_bounds__(kOrderThreads) void order_history_kernel(OrderArgs a) {
+  __shared__ uint64_t s_key[kOrderMaxBlocks];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int i = row % a.nb;
+  const int n = ((i * a.block) / a.segment) * a.segment / a.block;
+  const float* sc = a.scores + size_t(row) * a.nb;
+  int cap = 2;
+  while (cap < n) cap <<= 1;
+  for (int k = tid; k < cap; k += kOrderThreads)
+    s_key[k] = k < n ? ((uint64_t(~score_key(sc[k])) << 32) | uint32_t(k)) : ~0ull;
+  __syncthreads();
+  if (n > 1) {
+    for (int k = 2; k <= cap; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int e = tid; e < cap; e += kOrderThreads) {
+          const int p = e ^ j;
+          if (p > e) {
+            const uint64_t x = s_key[e], y = s_key[p];
+            if ((x > y) == ((e & k) == 0)) {
+              s_key[e] = y;
+              s_key[p] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  int32_t* out = a.order + size_t(row) * a.nb;
+  for (int k = tid; k < a.nb; k += kOrderThreads) out[k] = k < n ? int32_t(uint32_t(s_key[k])) : -1;
+  if (tid == 0) a.cnt[row] = n;
+}
+
+hipError_t launch_order_history(const OrderArgs& a, hipStream_t s) {
+  order_history_kernel<<<a.rows, kOrderThreads, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_select_topp(const SelectArgs& a, hipStream_t s) {

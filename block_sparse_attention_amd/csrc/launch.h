@@ -59,8 +59,23 @@ struct PrefillArgs {
   float* lse;           // nullable
   int bf16, batch, hq, hkv, d, L, block, segment, nb;
   float sm_scale;
+  // early stopping: idx holds the visiting order of the history blocks and
+  // cnt their number; the own segment is implied
+  int es;
+  float tau;
+  int32_t* nused;       // [batch, hq, L] history blocks taken per row, nullable
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+constexpr int kEsMaxBlocks = 2048;     // blocks per sequence for early stopping (visiting list staged in LDS)
+
+struct OrderArgs {
+  const float* scores;  // [rows, nb]
+  int32_t* order;       // [rows, nb]
+  int32_t* cnt;         // [rows]
+  int rows, nb, block, segment;
+};
+hipError_t launch_order_history(const OrderArgs& a, hipStream_t s);
+constexpr int kOrderMaxBlocks = 4096;
 
 struct DecodeArgs {
   const uint16_t* q;   // [batch, hq, d]

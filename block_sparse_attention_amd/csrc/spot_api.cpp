@@ -134,6 +134,8 @@ int spot_workspace_size(const spot_desc* desc, int op, size_t* bytes) {
       break;
     case SPOT_OP_SELECT_TOPP:
     case SPOT_OP_PREFILL:
+    case SPOT_OP_ORDER_HISTORY:
+    case SPOT_OP_PREFILL_EARLY_STOP:
       break;
     case SPOT_OP_KEY_PERMUTATION: {
       if ((st = check_prefill_shape(desc))) return st;
@@ -240,6 +242,48 @@ int spot_sparse_attn_prefill(const spot_desc* desc, const void* q, const void* k
   spot::PrefillArgs a{q, k, v, perm, idx, cnt, o, lse, desc->dtype == SPOT_BF16, desc->batch, desc->hq, desc->hkv,
                       desc->d, int(desc->q_len), desc->block, desc->segment, nb, effective_scale(desc)};
   return launched(spot::launch_prefill(a, static_cast<hipStream_t>(stream)), "sparse_attn_prefill");
+}
+
+int spot_order_history(const spot_desc* desc, const float* scores, int32_t* order, int32_t* cnt, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int st = check_common(desc);
+  if (st) return st;
+  if ((st = check_prefill_shape(desc))) return st;
+  if (!scores || !order || !cnt) return fail(SPOT_ERR_INVALID, "scores, order and cnt are required");
+  if (desc->segment <= 0) return fail(SPOT_ERR_INVALID, "segment must be > 0");
+  const int64_t nb = ceil_div64(desc->q_len, desc->block);
+  if (nb > spot::kOrderMaxBlocks)
+    return fail(SPOT_ERR_UNSUPPORTED, "%lld blocks per sequence (max %d)", (long long)nb, spot::kOrderMaxBlocks);
+  spot::OrderArgs a{scores, order, cnt, desc->batch * desc->hkv * int(nb), int(nb), desc->block, desc->segment};
+  return launched(spot::launch_order_history(a, static_cast<hipStream_t>(stream)), "order_history");
+}
+
+int spot_sparse_attn_prefill_early_stop(const spot_desc* desc, float tau, const void* q, const void* k, const void* v,
+                                        const int32_t* perm, const int32_t* order, const int32_t* cnt, void* o,
+                                        float* lse, int32_t* nused, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int st = check_common(desc);
+  if (st) return st;
+  if ((st = check_prefill_shape(desc))) return st;
+  if (!q || !k || !v || !order || !cnt || !o) return fail(SPOT_ERR_INVALID, "q, k, v, order, cnt and o are required");
+  if (!std::isfinite(tau) || tau < 0.f) return fail(SPOT_ERR_INVALID, "tau must be finite and >= 0");
+  if (desc->segment <= 0) return fail(SPOT_ERR_INVALID, "segment must be > 0");
+  if (desc->dtype != SPOT_BF16) return fail(SPOT_ERR_UNSUPPORTED, "early stopping supports bf16 only");
+  if (desc->block != 64 && desc->block != 128)
+    return fail(SPOT_ERR_UNSUPPORTED, "early stopping needs block 64 or 128 (got %d)", desc->block);
+  const int nb = int(ceil_div64(desc->q_len, desc->block));
+  if (nb > spot::kEsMaxBlocks)
+    return fail(SPOT_ERR_UNSUPPORTED, "%d blocks per sequence (max %d for early stopping)", nb, spot::kEsMaxBlocks);
+  spot::PrefillArgs a{q, k, v, perm, order, cnt, o, lse, 1, desc->batch, desc->hq, desc->hkv,
+                      desc->d, int(desc->q_len), desc->block, desc->segment, nb, effective_scale(desc)};
+  a.es = 1;
+  a.tau = tau;
+  a.nused = nused;
+  return launched(spot::launch_prefill(a, static_cast<hipStream_t>(stream)), "sparse_attn_prefill_early_stop");
 }
 
 int spot_sparse_attn_decode(const spot_desc* desc, const void* q, const void* k_cache, const void* v_cache,

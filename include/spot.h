@@ -11,6 +11,11 @@
  *   spot_sparse_attn_decode  the same for one decode query per sequence
  *   spot_key_permutation     the intra-segment key permutation the prefill gathers through
  *
+ * and an early-stopped variant of selection + prefill attention:
+ *
+ *   spot_order_history                  visiting order of each query block's history blocks
+ *   spot_sparse_attn_prefill_early_stop attention that stops taking history blocks per row
+ *
  * Conventions shared by every call
  * --------------------------------
  * Ownership.  Every tensor pointer is caller-owned DEVICE memory.  The library
@@ -76,7 +81,9 @@ enum spot_op {
   SPOT_OP_SELECT_TOPP = 1,
   SPOT_OP_PREFILL = 2,
   SPOT_OP_DECODE = 3,
-  SPOT_OP_KEY_PERMUTATION = 4
+  SPOT_OP_KEY_PERMUTATION = 4,
+  SPOT_OP_ORDER_HISTORY = 5,
+  SPOT_OP_PREFILL_EARLY_STOP = 6
 };
 
 /* Problem descriptor.  `version` must be SPOT_ABI_VERSION. */
@@ -185,6 +192,44 @@ int spot_sparse_attn_decode(const spot_desc* desc, const void* q, const void* k_
  */
 int spot_key_permutation(const spot_desc* desc, const void* q, const void* k, int32_t* perm, float* importance,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Visiting order for early stopping ([S2O] §2: candidate blocks are processed
+ * in descending estimated importance).  For each row (b, g, i) of the MEANPOOL
+ * scores [batch, hkv, nb, nb]: the history blocks of query block i, i.e. the
+ * blocks j of segments before i's segment (j < floor(i*B/S)*S/B), ordered by
+ * scores[b,g,i,j] descending, ties by j ascending.
+ * Output: order [batch, hkv, nb, nb] int32 (the ordered ids, -1 padded to nb)
+ * and cnt [batch, hkv, nb] int32 (the number of history blocks).
+ * Requires segment > 0 (a multiple of block) and nb <= 4096.  No workspace.
+ */
+int spot_order_history(const spot_desc* desc, const float* scores, int32_t* order, int32_t* cnt,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Early-stopped sparse prefill attention ([S2O] §2 early-stopping rule, §3
+ * two passes).  For query head h (group g) and row r of query block i, with
+ * s0 = floor(i*B/S)*S the start of i's segment:
+ *   pass 1: keys s0..r in natural order (dense causal own segment);
+ *   pass 2: the history blocks order[b,g,i,0..cnt) one at a time, their rows
+ *           taken through perm (natural rows when perm == NULL), all visible.
+ *   After each pass-2 block, gain = the softmax mass (sum of exp(logit - m))
+ *   its keys add and acc = the mass accumulated so far including them; the
+ *   row takes no further block once gain < tau * acc.
+ *   O[b,h,r] = softmax attention over the keys taken; lse (nullable) as in
+ *   spot_sparse_attn_prefill; nused (nullable) int32 [batch, hq, q_len]
+ *   receives the number of history blocks the row took.
+ * tau = 0 takes every history block (dense causal attention).  The
+ * comparison runs on the kernel's fp32 sums, so a row whose ratio lies
+ * within rounding of tau may stop one block earlier or later than an exact
+ * evaluation.  Requires dtype bf16, d in {64, 128}, block in {64, 128},
+ * segment > 0 (a multiple of block), nb <= 2048, tau finite and >= 0.
+ * No workspace.
+ */
+int spot_sparse_attn_prefill_early_stop(const spot_desc* desc, float tau, const void* q, const void* k,
+                                        const void* v, const int32_t* perm, const int32_t* order,
+                                        const int32_t* cnt, void* o, float* lse, int32_t* nused,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

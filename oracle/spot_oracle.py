@@ -364,8 +364,7 @@ def _es_blocks(q, k, i, g, h, order_gi, block, segment, sm_scale, perm):
     hist_phys = np.stack(hist) if hist else np.zeros((0, block), dtype=np.int64)
     lo = sm_scale * (q[h, rows] @ k[g, own].T)
     lo = np.where(own[None, :] <= rows[:, None], lo, -np.inf)
-    lh = sm_scale * np.einsum('rd,nbd->rnb', q[h, rows], k[g, hist_phys]) if hist else \
-        np.zeros((rows.shape[0], 0, block))
+    lh = (sm_scale * (q[h, rows] @ k[g, hist_phys.reshape(-1)].T)).reshape(rows.shape[0], -1, block)
     shift = lo.max(axis=1)
     if hist:
         shift = np.maximum(shift, lh.max(axis=(1, 2)))

@@ -155,6 +155,33 @@ def test_key_permutation_validation():
     assert B.spot_workspace_size(_prefill(segment=256), B.SPOT_OP_KEY_PERMUTATION) > 0
 
 
+def call_order(d, scores=FAKE, order=FAKE, cnt=FAKE):
+    return B.load_library().spot_order_history(ctypes.byref(d), scores, order, cnt, None, 0, None)
+
+
+def call_es(d, tau=0.01, q=FAKE, k=FAKE, v=FAKE, perm=None, order=FAKE, cnt=FAKE, o=FAKE):
+    return B.load_library().spot_sparse_attn_prefill_early_stop(ctypes.byref(d), tau, q, k, v, perm, order, cnt, o,
+                                                                 None, None, None, 0, None)
+
+
+def test_early_stop_validation():
+    assert call_order(_prefill(segment=0)) == B.SPOT_ERR_INVALID
+    assert call_order(_prefill(segment=96)) == B.SPOT_ERR_INVALID                 # not a multiple of the block
+    assert call_order(_prefill(segment=256), order=None) == B.SPOT_ERR_INVALID
+    assert call_order(_prefill(segment=256, q_len=64 * 5000, kv_len=64 * 5000)) == B.SPOT_ERR_UNSUPPORTED
+    assert call_es(_prefill(segment=0)) == B.SPOT_ERR_INVALID
+    assert call_es(_prefill(segment=256), tau=-0.5) == B.SPOT_ERR_INVALID
+    assert call_es(_prefill(segment=256), tau=float("nan")) == B.SPOT_ERR_INVALID
+    assert call_es(_prefill(segment=256), tau=float("inf")) == B.SPOT_ERR_INVALID
+    assert call_es(_prefill(segment=256), order=None) == B.SPOT_ERR_INVALID
+    assert call_es(_prefill(segment=256), o=None) == B.SPOT_ERR_INVALID
+    assert call_es(_prefill(segment=256, dtype=B.SPOT_F32)) == B.SPOT_ERR_UNSUPPORTED
+    assert call_es(_prefill(segment=256, block=32)) == B.SPOT_ERR_UNSUPPORTED
+    assert call_es(_prefill(segment=256, q_len=64 * 3000, kv_len=64 * 3000)) == B.SPOT_ERR_UNSUPPORTED
+    assert B.spot_workspace_size(_prefill(segment=256), B.SPOT_OP_ORDER_HISTORY) == 0
+    assert B.spot_workspace_size(_prefill(segment=256), B.SPOT_OP_PREFILL_EARLY_STOP) == 0
+
+
 def test_workspace_sizes():
     d = _prefill()
     assert B.spot_workspace_size(d, B.SPOT_OP_BLOCK_SCORE) == 3 * 1 * 2 * 16 * 128 * 4
