@@ -23,6 +23,9 @@ What each function follows:
                      nucleus on the residual distribution, stop once the mass
                      reaches p, floor K_min)
   indexer_scores     [Spot] §1 scoring equation (head-weighted ReLU of q.k)
+  key_block_variance [SPLA] §2.1 (block statistics: per-dimension variance,
+                     the diagonal of the block covariance)
+  taylor_scores      [SPLA] §2.1 second-order Taylor block score, as a log mass
   attend_prefill     [PBS] Problem + §2 (block-sparse attention, segment-local
                      causality), [S2O] §1 (index-array loads) and §3 (own
                      segment as a dense causal window, history through the
@@ -49,6 +52,10 @@ Early stopping: the stop rule is applied per query row; the marginal gain of a
 history block is the softmax mass its keys add and it is compared with the
 mass accumulated including that block (stop once gain < tau * accumulated);
 the block that triggers the stop is kept.
+Taylor score: the second-order expansion is taken for the scaled query
+(sm_scale * qbar) and enters the top-p rule as the log of the estimated block
+mass, so the softmax over blocks is the normalised mass estimate; variances
+are population variances (divide by the block's row count).
 """
 from __future__ import annotations
 
@@ -116,6 +123,49 @@ def meanpool_scores(qbar, kbar_nat, kbar_perm, block, segment, sm_scale):
             hist = np.array([is_history(j, i, block, segment) for j in js], dtype=bool)
             kb = np.where(hist[:, None], kbar_perm[g, :i + 1], kbar_nat[g, :i + 1])
             s[g, i, :i + 1] = sm_scale * (kb @ qbar[g, i])
+    return s
+
+
+def key_block_variance(k, block, perm=None):
+    """[SPLA] §2.1: per-dimension variance of the K rows of every block
+    (natural order, and through the permutation), divided by the row count.
+
+    k: (Hkv, L, d).  Returns var_nat, var_perm (Hkv, nB, d).
+    """
+    k = np.asarray(k, dtype=np.float64)
+    hkv, L, d = k.shape
+    nb = n_blocks(L, block)
+    vn = np.empty((hkv, nb, d))
+    vp = np.empty((hkv, nb, d))
+    for g in range(hkv):
+        for j in range(nb):
+            rows = block_rows(j, block, L)
+            x = k[g, rows]
+            vn[g, j] = ((x - x.mean(axis=0)) ** 2).mean(axis=0)
+            if perm is not None:
+                y = k[g, perm[g, rows]]
+                vp[g, j] = ((y - y.mean(axis=0)) ** 2).mean(axis=0)
+            else:
+                vp[g, j] = vn[g, j]
+    return vn, vp
+
+
+def taylor_scores(qbar, kbar_nat, kbar_perm, var_nat, var_perm, block, segment, sm_scale):
+    """[SPLA] §2.1: the block mass E_t[exp(x . k_t)] of the scaled pooled query
+    x = sm_scale * qbar, expanded to second order around the block mean with a
+    diagonal covariance: exp(x . kbar) * (1 + 1/2 * sum_d x_d^2 var_d).
+    Returned as its logarithm for j <= i (-inf for j > i); history blocks use
+    the permuted statistics as in meanpool_scores."""
+    hkv, nb, _ = qbar.shape
+    s = np.full((hkv, nb, nb), -np.inf)
+    for g in range(hkv):
+        for i in range(nb):
+            js = np.arange(i + 1)
+            hist = np.array([is_history(j, i, block, segment) for j in js], dtype=bool)
+            kb = np.where(hist[:, None], kbar_perm[g, :i + 1], kbar_nat[g, :i + 1])
+            vb = np.where(hist[:, None], var_perm[g, :i + 1], var_nat[g, :i + 1])
+            x = sm_scale * qbar[g, i]
+            s[g, i, :i + 1] = kb @ x + np.log(1.0 + 0.5 * (vb @ (x * x)))
     return s
 
 
@@ -437,7 +487,7 @@ def attend_prefill_es(q, k, v, order, block, segment, sm_scale, tau, perm=None, 
 
 # ----------------------------------------------------------------- pipelines
 def prefill(q, k, v, block, top_p, n_sink=1, n_recent=1, k_min=0, sm_scale=None,
-            segment=0, perm=None, qblocks=None):
+            segment=0, perm=None, qblocks=None, score="meanpool"):
     """Whole prefill path for one sequence: pool -> score -> select -> attend.
 
     q: (Hq, L, d), k/v: (Hkv, L, d).  Returns dict with scores, kept lists,
@@ -446,7 +496,11 @@ def prefill(q, k, v, block, top_p, n_sink=1, n_recent=1, k_min=0, sm_scale=None,
     d = q.shape[-1]
     sm_scale = 1.0 / np.sqrt(d) if not sm_scale else sm_scale
     qbar, kn, kp = pool_blocks(q, k, block, perm)
-    s = meanpool_scores(qbar, kn, kp, block, segment, sm_scale)
+    if score == "taylor":
+        vn, vp = key_block_variance(k, block, perm)
+        s = taylor_scores(qbar, kn, kp, vn, vp, block, segment, sm_scale)
+    else:
+        s = meanpool_scores(qbar, kn, kp, block, segment, sm_scale)
     kept = select_prefill(s, n_sink, n_recent, top_p, k_min, rows=qblocks)
     o, lse = attend_prefill(q, k, v, kept, block, sm_scale, segment, perm, qblocks)
     return dict(scores=s, kept=kept, o=o, lse=lse, qbar=qbar, kbar_nat=kn, kbar_perm=kp)
