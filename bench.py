@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-early-stop", action="store_true", help="skip the early-stopping measurement")
     ap.add_argument("--es-tau", type=float, default=0.01, help="early-stopping threshold tau")
+    ap.add_argument("--no-taylor", action="store_true", help="skip the Taylor-score measurement")
     ap.add_argument("--cpu-sample-blocks", type=int, default=0, help="0: every query block")
     ap.add_argument("--workload", default="gqa-bf16-L8192",
                     help="prefill workload of the step: gqa-bf16-L8192 (default), heavy-perm-bf16-L32768 "
@@ -87,8 +88,9 @@ def load_traffic(kernel_file: str, key: str):
 
 
 # ----------------------------------------------------------------- prefill
-def bench_prefill(args, torch, B, I):
+def bench_prefill(args, torch, B, I, score_kind=None):
     cfg = {c.name: c for c in (I.C1, I.C2, I.C3, I.C5)}[args.workload]
+    score_kind = B.SPOT_SCORE_MEANPOOL if score_kind is None else score_kind
     dev = torch.device("cuda:0")
     q, k, v = I.prefill_inputs(cfg)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -96,7 +98,7 @@ def bench_prefill(args, torch, B, I):
     dk = torch.from_numpy(k).to(tdt).to(dev)
     dv = torch.from_numpy(v).to(tdt).to(dev)
     del v
-    desc = B.prefill_desc(dq, dk, cfg.block, cfg.top_p, segment=cfg.segment)
+    desc = B.prefill_desc(dq, dk, cfg.block, cfg.top_p, segment=cfg.segment, score_kind=score_kind)
     bufs = B.alloc_prefill(desc, dev)
     perm = perm_ws = None
     if cfg.segment:
@@ -407,6 +409,15 @@ def main():
     if not args.no_decode:
         dec = bench_decode(args, torch, B, I)
         print(f"[bench] decode: {dec}", file=sys.stderr, flush=True)
+    tay = None
+    if not args.no_taylor:
+        t = bench_prefill(args, torch, B, I, score_kind=B.SPOT_SCORE_TAYLOR)
+        tay = {"workload": t["cfg"].name, "score": "second-order Taylor", "value": round(t["value"], 2),
+               "unit": "TFLOP/s", "ms_per_step": round(t["ms_step"], 4), "ms_score_select": round(t["ms_sel"], 4),
+               "ms_attention": round(t["ms_attn"], 4), "kept_fraction": round(t["kept_fraction"], 4),
+               "flop_per_step": t["flops"]}
+        del t
+        print(f"[bench] taylor: {tay}", file=sys.stderr, flush=True)
     es = None
     if not args.no_early_stop:
         es = bench_early_stop(args, torch, B, I)
@@ -431,6 +442,7 @@ def main():
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,
         "decode": dec,
+        "taylor_score": tay,
         "early_stop": es,
     }
     print(json.dumps(line))

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libspot.so")
 
 SPOT_OK, SPOT_ERR_INVALID, SPOT_ERR_UNSUPPORTED, SPOT_ERR_WORKSPACE, SPOT_ERR_LAUNCH = 0, -1, -2, -3, -4
 SPOT_F32, SPOT_BF16 = 0, 1
-SPOT_SCORE_MEANPOOL, SPOT_SCORE_RELU_INDEXER = 0, 1
+SPOT_SCORE_MEANPOOL, SPOT_SCORE_RELU_INDEXER, SPOT_SCORE_TAYLOR = 0, 1, 2
 SPOT_OP_BLOCK_SCORE, SPOT_OP_SELECT_TOPP, SPOT_OP_PREFILL, SPOT_OP_DECODE, SPOT_OP_KEY_PERMUTATION = 0, 1, 2, 3, 4
 SPOT_OP_ORDER_HISTORY, SPOT_OP_PREFILL_EARLY_STOP = 5, 6
 ABI_VERSION = 1
@@ -198,11 +198,12 @@ class PrefillBuffers:
 
 
 def prefill_desc(q: torch.Tensor, k: torch.Tensor, block: int, top_p: float, *, segment: int = 0, n_sink: int = 1,
-                 n_recent: int = 1, k_min: int = 0, sm_scale: float = 0.0) -> spot_desc:
+                 n_recent: int = 1, k_min: int = 0, sm_scale: float = 0.0,
+                 score_kind: int = SPOT_SCORE_MEANPOOL) -> spot_desc:
     b, hq, L, d = q.shape
     return make_desc(dtype=torch_dtype_code(q), batch=b, hq=hq, hkv=k.shape[1], d=d, q_len=L, kv_len=L, block=block,
                      segment=segment, n_sink=n_sink, n_recent=n_recent, k_min=k_min, top_p=top_p, sm_scale=sm_scale,
-                     score_kind=SPOT_SCORE_MEANPOOL)
+                     score_kind=score_kind)
 
 
 def alloc_prefill(desc: spot_desc, device) -> PrefillBuffers:
@@ -221,14 +222,15 @@ def alloc_prefill(desc: spot_desc, device) -> PrefillBuffers:
 
 
 def prefill(q, k, v, block: int, top_p: float, *, perm=None, segment: int = 0, n_sink: int = 1, n_recent: int = 1,
-            k_min: int = 0, sm_scale: float = 0.0, bufs: PrefillBuffers | None = None) -> PrefillBuffers:
+            k_min: int = 0, sm_scale: float = 0.0, score_kind: int = SPOT_SCORE_MEANPOOL,
+            bufs: PrefillBuffers | None = None) -> PrefillBuffers:
     """Whole prefill path: block scores -> top-p selection -> sparse attention.
 
     q (batch, hq, L, d), k/v (batch, hkv, L, d) bf16 or fp32 device tensors;
-    perm (batch, hkv, L) int32 or None.
+    perm (batch, hkv, L) int32 or None; score_kind MEANPOOL or TAYLOR.
     """
     desc = prefill_desc(q, k, block, top_p, segment=segment, n_sink=n_sink, n_recent=n_recent, k_min=k_min,
-                        sm_scale=sm_scale)
+                        sm_scale=sm_scale, score_kind=score_kind)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _require(t, name, dtype=q.dtype)
     if perm is not None:

@@ -4,9 +4,15 @@
 //                  rows of the block) and of K (natural, and through the key
 //                  permutation): mean pooling for block selection as in PBS-Attn
 //                  section 4 ("Implementatie", block selection on permuted keys).
+//                  With variance outputs it also writes the per-dimension
+//                  variance of each block's K rows (SPLA section 2.1 block
+//                  statistics), from a second pass over the rows.
 // meanpool_score   sm_scale * <qbar_i, kbar_j> for every key block j <= i
 //                  (SpotAttention section 1: all previous blocks are scored in
-//                  one contraction); j > i is -inf.
+//                  one contraction); j > i is -inf.  Taylor variant (SPLA
+//                  section 2.1): x . kbar_j + log(1 + 1/2 sum_d x_d^2 var_jd)
+//                  with x = sm_scale * qbar_i, the log of the second-order
+//                  estimate of the block's attention mass.
 // indexer_score    SpotAttention section 1 scoring equation:
 //                  sum_h w_h ReLU(q^I_h . k^I_{h,t}), one streaming pass over the
 //                  indexer key cache.
@@ -36,8 +42,9 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
 
 // Reduce per-thread column partials (rows_par row slots x d columns) through
 // LDS and store sum * inv_count for the d columns.
+// With `keep`, the result is also left in LDS for a following pass.
 __device__ __forceinline__ void reduce_cols_store(float (&acc)[8], float* red, int lr, int rp, int rows_par,
-                                                  int d, float inv_count, float* out) {
+                                                  int d, float inv_count, float* out, float* keep = nullptr) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[rp * d + lr * 8 + e] = acc[e];
   __syncthreads();
@@ -45,13 +52,40 @@ __device__ __forceinline__ void reduce_cols_store(float (&acc)[8], float* red, i
     float s = 0.f;
     for (int r = 0; r < rows_par; ++r) s += red[r * d + c];
     out[c] = s * inv_count;
+    if (keep) keep[c] = s * inv_count;
   }
   __syncthreads();
+}
+
+// Second pass over a block's K rows: sum of squared deviations from the mean
+// kept in LDS, stored divided by the row count.
+template <typename T, bool PERM>
+__device__ __forceinline__ void block_variance(const PoolArgs& a, const T* K, size_t kv_row0, int r0, int nr,
+                                               int lr, int rp, int rows_par, float* red, const float* mean,
+                                               float* out) {
+  float acc[8];
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  float mu[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mu[e] = mean[lr * 8 + e];
+#pragma unroll 4
+  for (int rr = rp; rr < nr; rr += rows_par) {
+    const int row = PERM ? a.perm[kv_row0 + r0 + rr] : r0 + rr;
+    float x[8];
+    load8<T>(K + (kv_row0 + row) * a.d + lr * 8, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float dx = x[e] - mu[e];
+      acc[e] = fmaf(dx, dx, acc[e]);
+    }
+  }
+  reduce_cols_store(acc, red, lr, rp, rows_par, a.d, 1.0f / float(nr), out);
 }
 
 template <typename T>
 __global__ __launch_bounds__(256) void pool_blocks_kernel(PoolArgs a) {
   __shared__ float red[256 * 8];
+  __shared__ float mean_s[128];
   const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int d = a.d, L = a.L, B = a.block;
   const int G = a.hq / a.hkv;
@@ -86,7 +120,9 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(PoolArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += x[e];
   }
-  reduce_cols_store(acc, red, lr, rp, rows_par, d, 1.0f / float(nr), a.kbar_nat + out_off);
+  reduce_cols_store(acc, red, lr, rp, rows_par, d, 1.0f / float(nr), a.kbar_nat + out_off, mean_s);
+  if (a.kvar_nat)
+    block_variance<T, false>(a, K, kv_row0, r0, nr, lr, rp, rows_par, red, mean_s, a.kvar_nat + out_off);
 
   if (a.perm) {
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
@@ -98,7 +134,9 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(PoolArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += x[e];
     }
-    reduce_cols_store(acc, red, lr, rp, rows_par, d, 1.0f / float(nr), a.kbar_perm + out_off);
+    reduce_cols_store(acc, red, lr, rp, rows_par, d, 1.0f / float(nr), a.kbar_perm + out_off, mean_s);
+    if (a.kvar_nat)
+      block_variance<T, true>(a, K, kv_row0, r0, nr, lr, rp, rows_par, red, mean_s, a.kvar_perm + out_off);
   }
 }
 
@@ -114,6 +152,7 @@ hipError_t launch_pool_blocks(const PoolArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------- mean-pool score
 constexpr int kST = 32;  // score tile (query blocks x key blocks)
 
+template <bool TAYLOR>
 __global__ __launch_bounds__(256) void meanpool_score_kernel(MeanpoolScoreArgs a) {
   extern __shared__ float sm[];
   const int d = a.d, nb = a.nb;
@@ -121,6 +160,8 @@ __global__ __launch_bounds__(256) void meanpool_score_kernel(MeanpoolScoreArgs a
   float* qs = sm;
   float* kn = qs + kST * ld;
   float* kp = kn + kST * ld;
+  float* vns = kp + kST * ld;   // TAYLOR: block variances (natural, permuted)
+  float* vps = vns + kST * ld;
   const int i0 = blockIdx.y * kST, j0 = blockIdx.x * kST;
   const size_t bg = blockIdx.z;
   float* out = a.scores + bg * size_t(nb) * nb;
@@ -136,6 +177,8 @@ __global__ __launch_bounds__(256) void meanpool_score_kernel(MeanpoolScoreArgs a
   const float* qb = a.qbar + bg * size_t(nb) * d;
   const float* knb = a.kbar_nat + bg * size_t(nb) * d;
   const float* kpb = a.kbar_perm ? a.kbar_perm + bg * size_t(nb) * d : nullptr;
+  const float* vnb = TAYLOR ? a.var_nat + bg * size_t(nb) * d : nullptr;
+  const float* vpb = TAYLOR && kpb ? a.var_perm + bg * size_t(nb) * d : nullptr;
   for (int e = threadIdx.x; e < kST * d / 4; e += 256) {
     const int r = e / (d / 4), c = (e % (d / 4)) * 4;
     const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -147,9 +190,18 @@ __global__ __launch_bounds__(256) void meanpool_score_kernel(MeanpoolScoreArgs a
       const float4 vp = (j0 + r < nb) ? *reinterpret_cast<const float4*>(kpb + size_t(j0 + r) * d + c) : zero;
       kp[r * ld + c] = vp.x; kp[r * ld + c + 1] = vp.y; kp[r * ld + c + 2] = vp.z; kp[r * ld + c + 3] = vp.w;
     }
+    if constexpr (TAYLOR) {
+      const float4 wn = (j0 + r < nb) ? *reinterpret_cast<const float4*>(vnb + size_t(j0 + r) * d + c) : zero;
+      vns[r * ld + c] = wn.x; vns[r * ld + c + 1] = wn.y; vns[r * ld + c + 2] = wn.z; vns[r * ld + c + 3] = wn.w;
+      if (vpb) {
+        const float4 wp = (j0 + r < nb) ? *reinterpret_cast<const float4*>(vpb + size_t(j0 + r) * d + c) : zero;
+        vps[r * ld + c] = wp.x; vps[r * ld + c + 1] = wp.y; vps[r * ld + c + 2] = wp.z; vps[r * ld + c + 3] = wp.w;
+      }
+    }
   }
   __syncthreads();
   float sn[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, sp[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  float tn[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, tp[2][2] = {{0.f, 0.f}, {0.f, 0.f}};   // TAYLOR: sum qbar_c^2 var_c
   for (int c = 0; c < d; ++c) {
     const float q0 = qs[(ty * 2) * ld + c], q1 = qs[(ty * 2 + 1) * ld + c];
     const float k0 = kn[(tx * 2) * ld + c], k1 = kn[(tx * 2 + 1) * ld + c];
@@ -160,6 +212,17 @@ __global__ __launch_bounds__(256) void meanpool_score_kernel(MeanpoolScoreArgs a
       sp[0][0] = fmaf(q0, p0, sp[0][0]); sp[0][1] = fmaf(q0, p1, sp[0][1]);
       sp[1][0] = fmaf(q1, p0, sp[1][0]); sp[1][1] = fmaf(q1, p1, sp[1][1]);
     }
+    if constexpr (TAYLOR) {
+      const float qq0 = q0 * q0, qq1 = q1 * q1;
+      const float w0 = vns[(tx * 2) * ld + c], w1 = vns[(tx * 2 + 1) * ld + c];
+      tn[0][0] = fmaf(qq0, w0, tn[0][0]); tn[0][1] = fmaf(qq0, w1, tn[0][1]);
+      tn[1][0] = fmaf(qq1, w0, tn[1][0]); tn[1][1] = fmaf(qq1, w1, tn[1][1]);
+      if (vpb) {
+        const float u0 = vps[(tx * 2) * ld + c], u1 = vps[(tx * 2 + 1) * ld + c];
+        tp[0][0] = fmaf(qq0, u0, tp[0][0]); tp[0][1] = fmaf(qq0, u1, tp[0][1]);
+        tp[1][0] = fmaf(qq1, u0, tp[1][0]); tp[1][1] = fmaf(qq1, u1, tp[1][1]);
+      }
+    }
   }
   for (int u = 0; u < 2; ++u)
     for (int w = 0; w < 2; ++w) {
@@ -169,6 +232,7 @@ __global__ __launch_bounds__(256) void meanpool_score_kernel(MeanpoolScoreArgs a
       if (j <= i) {
         const bool hist = kpb && a.segment > 0 && (j * a.block) / a.segment < (i * a.block) / a.segment;
         v = a.scale * (hist ? sp[u][w] : sn[u][w]);
+        if constexpr (TAYLOR) v += log1pf(0.5f * a.scale * a.scale * (hist ? tp[u][w] : tn[u][w]));
       }
       out[size_t(i) * nb + j] = v;
     }
@@ -177,8 +241,13 @@ __global__ __launch_bounds__(256) void meanpool_score_kernel(MeanpoolScoreArgs a
 hipError_t launch_meanpool_score(const MeanpoolScoreArgs& a, hipStream_t s) {
   const int nt = (a.nb + kST - 1) / kST;
   dim3 grid(nt, nt, a.batch * a.hkv);
-  size_t lds = size_t(3) * kST * (a.d + 1) * sizeof(float);
-  meanpool_score_kernel<<<grid, 256, lds, s>>>(a);
+  if (a.var_nat) {
+    const size_t lds = size_t(5) * kST * (a.d + 1) * sizeof(float);
+    meanpool_score_kernel<true><<<grid, 256, lds, s>>>(a);
+  } else {
+    const size_t lds = size_t(3) * kST * (a.d + 1) * sizeof(float);
+    meanpool_score_kernel<false><<<grid, 256, lds, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -15,6 +15,8 @@ struct PoolArgs {
   float* kbar_nat;
   float* kbar_perm;      // written only when perm != nullptr
   int bf16, batch, hq, hkv, d, L, block, nb;
+  float* kvar_nat;       // nullable: per-dimension block variances of K (natural)
+  float* kvar_perm;      // and through perm (written only when perm != nullptr)
 };
 hipError_t launch_pool_blocks(const PoolArgs& a, hipStream_t s);
 
@@ -25,6 +27,8 @@ struct MeanpoolScoreArgs {
   float* scores;           // [batch, hkv, nb, nb]
   int batch, hkv, d, nb, block, segment;
   float scale;
+  const float* var_nat;    // nullable: Taylor score with these block variances
+  const float* var_perm;
 };
 hipError_t launch_meanpool_score(const MeanpoolScoreArgs& a, hipStream_t s);
 

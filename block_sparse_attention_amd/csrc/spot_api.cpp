@@ -81,9 +81,15 @@ float effective_scale(const spot_desc* d) {
   return d->sm_scale > 0.f ? d->sm_scale : 1.0f / std::sqrt(float(d->d));
 }
 
+bool is_pooled(const spot_desc* d) {
+  return d->score_kind == SPOT_SCORE_MEANPOOL || d->score_kind == SPOT_SCORE_TAYLOR;
+}
+
+// pooled statistics: qbar, kbar natural, kbar permuted (+ K variances natural and permuted for TAYLOR)
 size_t meanpool_ws_bytes(const spot_desc* d) {
   const size_t nb = size_t(ceil_div64(d->q_len, d->block));
-  return size_t(3) * d->batch * d->hkv * nb * d->d * sizeof(float);
+  const size_t slabs = d->score_kind == SPOT_SCORE_TAYLOR ? 5 : 3;
+  return slabs * d->batch * d->hkv * nb * d->d * sizeof(float);
 }
 
 int check_workspace(size_t need, const void* ws, size_t have) {
@@ -125,7 +131,7 @@ int spot_workspace_size(const spot_desc* desc, int op, size_t* bytes) {
   if (st) return st;
   switch (op) {
     case SPOT_OP_BLOCK_SCORE:
-      if (desc->score_kind == SPOT_SCORE_MEANPOOL) {
+      if (is_pooled(desc)) {
         if ((st = check_prefill_shape(desc))) return st;
         *bytes = meanpool_ws_bytes(desc);
       } else if (desc->score_kind != SPOT_SCORE_RELU_INDEXER) {
@@ -164,21 +170,30 @@ int spot_block_score(const spot_desc* desc, const void* q, const void* k, const 
   if (st) return st;
   if (!scores) return fail(SPOT_ERR_INVALID, "scores is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (desc->score_kind == SPOT_SCORE_MEANPOOL) {
+  if (is_pooled(desc)) {
     if ((st = check_prefill_shape(desc))) return st;
-    if (!q || !k) return fail(SPOT_ERR_INVALID, "q and k are required for MEANPOOL");
+    if (!q || !k) return fail(SPOT_ERR_INVALID, "q and k are required for MEANPOOL and TAYLOR");
     if (perm && desc->segment <= 0) return fail(SPOT_ERR_INVALID, "perm given but segment is 0");
     const size_t need = meanpool_ws_bytes(desc);
     if ((st = check_workspace(need, workspace, workspace_bytes))) return st;
     const int nb = int(ceil_div64(desc->q_len, desc->block));
     const size_t slab = size_t(desc->batch) * desc->hkv * nb * desc->d;
     float* ws = static_cast<float*>(workspace);
+    const bool taylor = desc->score_kind == SPOT_SCORE_TAYLOR;
     spot::PoolArgs pa{q, k, perm, ws, ws + slab, ws + 2 * slab, desc->dtype == SPOT_BF16, desc->batch, desc->hq,
                       desc->hkv, desc->d, int(desc->q_len), desc->block, nb};
+    if (taylor) {
+      pa.kvar_nat = ws + 3 * slab;
+      pa.kvar_perm = ws + 4 * slab;
+    }
     hipError_t e = spot::launch_pool_blocks(pa, s);
     if (e != hipSuccess) return launched(e, "pool_blocks");
     spot::MeanpoolScoreArgs sa{ws, ws + slab, perm ? ws + 2 * slab : nullptr, scores, desc->batch, desc->hkv,
                                desc->d, nb, desc->block, desc->segment, effective_scale(desc)};
+    if (taylor) {
+      sa.var_nat = ws + 3 * slab;
+      sa.var_perm = perm ? ws + 4 * slab : nullptr;
+    }
     return launched(spot::launch_meanpool_score(sa, s), "meanpool_score");
   }
   if (desc->score_kind == SPOT_SCORE_RELU_INDEXER) {

@@ -48,6 +48,7 @@
  *          Long-Context Transformers
  *   [PBS]  PBS-Attn, "Sparsere Blok-Sparse Attention via Tokenpermutatie"
  *   [S2O]  "S2O - Vroege Stoppering voor Sparse Attention via Online Permutatie"
+ *   [SPLA] "SPLA - Block Sparse Plus Linear Attention voor Long Context Modeling"
  */
 #ifndef SPOT_H
 #define SPOT_H
@@ -73,7 +74,8 @@ enum spot_dtype { SPOT_F32 = 0, SPOT_BF16 = 1 };
 
 enum spot_score_kind {
   SPOT_SCORE_MEANPOOL = 0,     /* prefill: sm_scale * <mean q, mean k>           ([PBS] §4) */
-  SPOT_SCORE_RELU_INDEXER = 1  /* decode: sum_h w_h ReLU(q^I_h . k^I_{h,t})       ([Spot] §1) */
+  SPOT_SCORE_RELU_INDEXER = 1, /* decode: sum_h w_h ReLU(q^I_h . k^I_{h,t})       ([Spot] §1) */
+  SPOT_SCORE_TAYLOR = 2        /* prefill: log of the second-order block mass      ([SPLA] §2.1) */
 };
 
 enum spot_op {
@@ -126,6 +128,15 @@ int spot_workspace_size(const spot_desc* desc, int op, size_t* bytes);
  *   earlier segment than block i, else in natural order.  j > i gets -inf.
  *   Uses q, k, perm (nullable); idx_q, idx_w, idx_k must be NULL or are ignored.
  *   Workspace: the pooled means (spot_workspace_size).
+ *
+ * TAYLOR (prefill, [SPLA] §2.1 second-order Taylor block selection with a
+ * diagonal covariance): with x = sm_scale * qbar[g,i],
+ *     scores[b,g,i,j] = < x, kbar[g,j] > + ln(1 + 1/2 * sum_c x_c^2 var[g,j,c])
+ *   the logarithm of the estimated attention mass of block j, so the softmax
+ *   over blocks is the normalised estimate.  var[g,j,c] is the population
+ *   variance of coordinate c over the block's K rows (the same rows as kbar:
+ *   through perm for history blocks).  Same inputs as MEANPOOL; workspace:
+ *   five pooled slabs instead of three (spot_workspace_size).
  *
  * RELU_INDEXER (decode, [Spot] §1 scoring equation): for sequence b and key
  * block t < nk

@@ -202,3 +202,11 @@ def test_error_message_is_thread_local_and_cleared():
     assert lib.spot_last_error() == b"desc is NULL"
     B.spot_workspace_size(_prefill(), B.SPOT_OP_PREFILL)
     assert lib.spot_last_error() == b""
+
+
+def test_taylor_score_workspace_and_validation():
+    d = _prefill(score_kind=B.SPOT_SCORE_TAYLOR)
+    assert B.spot_workspace_size(d, B.SPOT_OP_BLOCK_SCORE) == 5 * 1 * 2 * 16 * 128 * 4
+    need = B.spot_workspace_size(d, B.SPOT_OP_BLOCK_SCORE)
+    assert call_score(d, ws_bytes=need - 1) == B.SPOT_ERR_WORKSPACE
+    assert call_score(d, q=None) == B.SPOT_ERR_INVALID

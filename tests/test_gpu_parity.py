@@ -34,20 +34,22 @@ def upload_prefill(cfg, device, perm=None):
     return (q, k, v), (dq, dk, dv, dp)
 
 
-def gpu_prefill(cfg, dev_inputs, perm_dev=None, top_p=None, **kw):
+def gpu_prefill(cfg, dev_inputs, perm_dev=None, top_p=None, score_kind=B.SPOT_SCORE_MEANPOOL, **kw):
     dq, dk, dv, _ = dev_inputs
     bufs = B.prefill(dq, dk, dv, cfg.block, cfg.top_p if top_p is None else top_p, perm=perm_dev,
                      segment=cfg.segment if perm_dev is not None else 0, n_sink=kw.get("n_sink", cfg.n_sink),
-                     n_recent=kw.get("n_recent", cfg.n_recent), k_min=kw.get("k_min", cfg.k_min))
+                     n_recent=kw.get("n_recent", cfg.n_recent), k_min=kw.get("k_min", cfg.k_min),
+                     score_kind=score_kind)
     torch.cuda.synchronize()
     return bufs
 
 
 def pipeline_check(cfg, host, bufs, perm=None, pairs=None, top_p=None, n_sink=None, n_recent=None, k_min=None,
-                   check_scores=True):
+                   check_scores=True, score="meanpool"):
     """Scores, selection and output of a GPU prefill against the oracle.
 
-    pairs: list of (b, g, i) rows to check (default: all)."""
+    pairs: list of (b, g, i) rows to check (default: all); score: "meanpool"
+    or "taylor" (the block score the GPU used)."""
     q, k, v = host
     top_p = cfg.top_p if top_p is None else top_p
     n_sink = cfg.n_sink if n_sink is None else n_sink
@@ -69,7 +71,11 @@ def pipeline_check(cfg, host, bufs, perm=None, pairs=None, top_p=None, n_sink=No
     for b in range(cfg.batch):
         pb = None if perm is None else perm[b]
         qbar, kn, kp = oracle.pool_blocks(q[b], k[b], cfg.block, pb)
-        s = oracle.meanpool_scores(qbar, kn, kp, cfg.block, seg, scale)
+        if score == "taylor":
+            vn, vp = oracle.key_block_variance(k[b], cfg.block, pb)
+            s = oracle.taylor_scores(qbar, kn, kp, vn, vp, cfg.block, seg, scale)
+        else:
+            s = oracle.meanpool_scores(qbar, kn, kp, cfg.block, seg, scale)
         if check_scores:
             fin = np.isfinite(s)
             assert np.array_equal(fin, np.isfinite(gs[b]))
