@@ -23,6 +23,10 @@ What each function follows:
                      nucleus on the residual distribution, stop once the mass
                      reaches p, floor K_min)
   indexer_scores     [Spot] §1 scoring equation (head-weighted ReLU of q.k)
+  mxfp4_quantize,    [Spot] §4 (selector K-cache in FP4 microscaling); the
+  mxfp4_dequantize   format is the OCP Microscaling (MX) v1.0 MXFP4 element
+                     and scale encoding: FP4 E2M1 elements, one E8M0
+                     power-of-two scale per 32 elements
   key_block_variance [SPLA] §2.1 (block statistics: per-dimension variance,
                      the diagonal of the block covariance)
   taylor_scores      [SPLA] §2.1 second-order Taylor block score, as a log mass
@@ -52,6 +56,10 @@ Early stopping: the stop rule is applied per query row; the marginal gain of a
 history block is the softmax mass its keys add and it is compared with the
 mass accumulated including that block (stop once gain < tau * accumulated);
 the block that triggers the stop is kept.
+MXFP4: the shared exponent is floor(log2(max |x|)) - 2 (the largest E2M1
+exponent), clamped to the E8M0 range, -127 for an all-zero group; elements
+are rounded to the nearest E2M1 value, ties to the even code, and saturate at
+6; the sign bit is the input's sign bit (so -0 keeps its sign).
 Taylor score: the second-order expansion is taken for the scaled query
 (sm_scale * qbar) and enters the top-p rule as the log of the estimated block
 mass, so the softmax over blocks is the normalised mass estimate; variances
@@ -167,6 +175,70 @@ def taylor_scores(qbar, kbar_nat, kbar_perm, var_nat, var_perm, block, segment, 
             x = sm_scale * qbar[g, i]
             s[g, i, :i + 1] = kb @ x + np.log(1.0 + 0.5 * (vb @ (x * x)))
     return s
+
+
+# ----------------------------------------------------------------- MXFP4 indexer keys
+E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)   # codes 0..7; bit 3 is the sign
+MX_GROUP = 32
+
+
+def mxfp4_quantize(x):
+    """[Spot] §4 FP4 microscaling of the selector keys.
+
+    x: (..., n) with n a multiple of 32, groups of 32 consecutive elements.
+    Returns codes uint8 (..., n), one 4-bit code per element (sign << 3 |
+    magnitude index into E2M1_MAGNITUDES), and scale bytes uint8
+    (..., n // 32): the group scale is 2 ** (byte - 127).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    shape = x.shape
+    g = x.reshape(-1, MX_GROUP)
+    grid = np.array(E2M1_MAGNITUDES)
+    codes = np.zeros(g.shape, dtype=np.uint8)
+    scales = np.zeros(g.shape[0], dtype=np.uint8)
+    for r in range(g.shape[0]):
+        amax = np.abs(g[r]).max()
+        if amax == 0:
+            e = -127
+        else:
+            _, ex = np.frexp(amax)          # amax = m * 2**ex, 0.5 <= m < 1
+            e = int(ex) - 1 - 2             # floor(log2(amax)) - 2
+            e = max(-127, min(127, e))
+        scales[r] = e + 127
+        y = g[r] / 2.0 ** e
+        for c in range(MX_GROUP):
+            a = abs(y[c])
+            if a >= grid[-1]:
+                m = len(grid) - 1
+            else:
+                dist = np.abs(grid - a)
+                best = np.nonzero(dist == dist.min())[0]
+                m = int(best[0]) if best.size == 1 else int(best[best % 2 == 0][0])
+            codes[r, c] = (8 if np.signbit(y[c]) else 0) | m
+    return codes.reshape(shape), scales.reshape(shape[:-1] + (shape[-1] // MX_GROUP,))
+
+
+def mxfp4_dequantize(codes, scales):
+    """Values of MXFP4 codes: (-1)^sign * E2M1 magnitude * 2 ** (scale - 127)."""
+    codes = np.asarray(codes)
+    mag = np.array(E2M1_MAGNITUDES)[codes & 7]
+    sign = np.where(codes & 8, -1.0, 1.0)
+    sc = 2.0 ** (np.repeat(np.asarray(scales, dtype=np.float64), MX_GROUP, axis=-1) - 127.0)
+    return sign * mag * sc
+
+
+def mxfp4_pack(codes):
+    """Two codes per byte: element 2k in the low nibble, 2k+1 in the high one."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
+def mxfp4_unpack(packed):
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = packed & 15
+    out[..., 1::2] = packed >> 4
+    return out
 
 
 # ----------------------------------------------------------------- D1 indexer score
@@ -507,10 +579,15 @@ def prefill(q, k, v, block, top_p, n_sink=1, n_recent=1, k_min=0, sm_scale=None,
 
 
 def decode(q, k_cache, v_cache, idx_q, idx_w, idx_k, block, T, top_p, n_sink=1, n_recent=1,
-           k_min=0, sm_scale=None):
-    """Whole decode step for one sequence: indexer score -> select -> attend."""
+           k_min=0, sm_scale=None, idx_format="bf16"):
+    """Whole decode step for one sequence: indexer score -> select -> attend.
+    idx_format "mxfp4": the indexer keys are scored from their MXFP4 encoding."""
     d = q.shape[-1]
     sm_scale = 1.0 / np.sqrt(d) if not sm_scale else sm_scale
+    if idx_format == "mxfp4":
+        nt, h_idx, d_idx = idx_k.shape
+        codes, scales = mxfp4_quantize(np.asarray(idx_k, dtype=np.float64).reshape(nt, h_idx * d_idx))
+        idx_k = mxfp4_dequantize(codes, scales).reshape(nt, h_idx, d_idx)
     s = indexer_scores(idx_q, idx_w, idx_k)
     kept = select_decode(s, n_sink, n_recent, top_p, k_min)
     o, lse = attend_decode(q, k_cache, v_cache, kept, block, T, sm_scale)
