@@ -186,7 +186,7 @@ def bench_prefill(args, torch, B, I, score_kind=None):
 
 
 # ----------------------------------------------------------------- decode
-def bench_decode(args, torch, B, I):
+def bench_decode(args, torch, B, I, mxfp4=False):
     cfg = I.C4
     dev = torch.device("cuda:0")
     D = I.decode_inputs(cfg)
@@ -198,30 +198,42 @@ def bench_decode(args, torch, B, I):
     desc = B.decode_desc(q, kc, cfg.block, cfg.top_p, cfg.h_idx, cfg.d_idx)
     bufs = B.alloc_decode(desc, dev)
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    if mxfp4:   # the cache is encoded once, when keys are appended (outside the step)
+        kcodes, kscales = B.quantize_indexer_keys(ik, cfg.block, cfg.T)
+        torch.cuda.synchronize()
+        del ik
+
+    def score():
+        if mxfp4:
+            B.spot_indexer_score_mxfp4(desc, iq, iw, kcodes, kscales, bufs.scores)
+        else:
+            B.spot_block_score(desc, None, None, None, iq, iw, ik, bufs.scores)
 
     def step(ev):
         ev[0].record()
-        B.spot_block_score(desc, None, None, None, iq, iw, ik, bufs.scores)
+        score()
+        ev[3].record()
         B.spot_select_topp(desc, bufs.scores, bufs.idx, bufs.cnt)
         ev[1].record()
         B.spot_sparse_attn_decode(desc, q, kc, vc, bufs.idx, bufs.cnt, bufs.o, bufs.lse, bufs.workspace)
         ev[2].record()
 
     for _ in range(args.warmup):
-        step([torch.cuda.Event(enable_timing=True) for _ in range(3)])
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for e in evs:
         flush.fill_(1.0)          # evict the 256 MB last-level cache between steps (outside the events)
         step(e)
     torch.cuda.synchronize()
     ms_front = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_scan = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
     ms_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     ms_step_eager = ms_front + ms_attn
 
     # the step's four launches as one HIP graph, replayed with a cold cache each time
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        B.spot_block_score(desc, None, None, None, iq, iw, ik, bufs.scores)
+        score()
         B.spot_select_topp(desc, bufs.scores, bufs.idx, bufs.cnt)
         B.spot_sparse_attn_decode(desc, q, kc, vc, bufs.idx, bufs.cnt, bufs.o, bufs.lse, bufs.workspace)
     graph.replay()
@@ -238,14 +250,17 @@ def bench_decode(args, torch, B, I):
     bs = np.minimum(cfg.block, cfg.T - np.arange(cfg.nt) * cfg.block)
     kept_keys = np.array([bs[idx[b, :cnt[b]]].sum() for b in range(cfg.batch)], dtype=np.float64)
     kv_bytes = float(kept_keys.sum()) * cfg.hkv * cfg.d * 2 * 2
-    scan_bytes = cfg.batch * cfg.nt * cfg.h_idx * cfg.d_idx * 2.0
+    scan_bytes = cfg.batch * cfg.nt * cfg.h_idx * cfg.d_idx * (0.5 + 1.0 / 32 if mxfp4 else 2.0)
     qo_bytes = cfg.batch * cfg.hq * cfg.d * 2 * 2.0 + cfg.batch * cfg.h_idx * (cfg.d_idx * 2 + 4)
     step_bytes = kv_bytes + scan_bytes + qo_bytes
     attn_gbs = (kv_bytes + qo_bytes) / (ms_attn * 1e-3) / 1e9
     return dict(
-        workload=cfg.name, value=round(step_bytes / (ms_step * 1e-3) / 1e9, 1), unit="GB/s",
+        workload=cfg.name, indexer_cache="mxfp4" if mxfp4 else "bf16",
+        value=round(step_bytes / (ms_step * 1e-3) / 1e9, 1), unit="GB/s",
         ms_per_step=round(ms_step, 4), ms_per_step_eager_launches=round(ms_step_eager, 4),
-        ms_score_select=round(ms_front, 4), ms_attention=round(ms_attn, 4),
+        ms_score_select=round(ms_front, 4), ms_indexer_scan=round(ms_scan, 4),
+        indexer_scan_gbs=round(scan_bytes / (ms_scan * 1e-3) / 1e9, 1), indexer_scan_bytes=scan_bytes,
+        ms_attention=round(ms_attn, 4),
         kept_fraction=round(float(kept_keys.sum()) / (cfg.batch * cfg.T), 4), bytes_per_step=step_bytes,
         roofline={"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "kernel": "decode_split_kernel<128,4>+combine",
@@ -405,10 +420,12 @@ def main():
     print(f"[bench] prefill {pre['cfg'].name}: {pre['ms_step']:.4f} ms/step (graph), "
           f"{pre['ms_step_eager']:.4f} ms/step (eager), attention {pre['ms_attn']:.4f} ms, "
           f"score+select {pre['ms_sel']:.4f} ms, kept {pre['kept_fraction']:.4f}", file=sys.stderr, flush=True)
-    dec = None
+    dec = dec_mx = None
     if not args.no_decode:
         dec = bench_decode(args, torch, B, I)
         print(f"[bench] decode: {dec}", file=sys.stderr, flush=True)
+        dec_mx = bench_decode(args, torch, B, I, mxfp4=True)
+        print(f"[bench] decode mxfp4: {dec_mx}", file=sys.stderr, flush=True)
     tay = None
     if not args.no_taylor:
         t = bench_prefill(args, torch, B, I, score_kind=B.SPOT_SCORE_TAYLOR)
@@ -442,6 +459,7 @@ def main():
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,
         "decode": dec,
+        "decode_mxfp4_indexer": dec_mx,
         "taylor_score": tay,
         "early_stop": es,
     }

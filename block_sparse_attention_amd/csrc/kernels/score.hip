@@ -17,7 +17,15 @@
 //                  sum_h w_h ReLU(q^I_h . k^I_{h,t}), one streaming pass over the
 //                  indexer key cache.
 //
-// All three are HBM- or latency-bound; they use plain fp32 VALU arithmetic.
+// quantize_mxfp4   SpotAttention section 4: the selector's key cache in FP4
+//                  microscaling (OCP MX MXFP4: E2M1 elements, one E8M0
+//                  power-of-two scale per 32 elements).
+// indexer_score_mxfp4  the ReLU indexer score over that cache: the E2M1 pairs
+//                  are widened to bf16 by the gfx950 conversion instruction and
+//                  multiplied with the bf16 query by v_dot2; the group sum is
+//                  scaled by its power of two.
+//
+// All of them are HBM- or latency-bound; they use plain fp32 VALU arithmetic.
 #include "../launch.h"
 #include "common.h"
 
@@ -316,6 +324,144 @@ hipError_t launch_indexer_score(const IndexerScoreArgs& a, hipStream_t s) {
   else if (lanes <= 8) launch_idx<8>(a, s);
   else if (lanes <= 16) launch_idx<16>(a, s);
   else launch_idx<32>(a, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- MXFP4 indexer keys
+// Magnitude code of |y| on the E2M1 grid (0, 0.5, 1, 1.5, 2, 3, 4, 6), rounded
+// to nearest with ties to the even code and saturating at 6: every midpoint
+// below an even code counts with >=, every midpoint below an odd code with >.
+__device__ __forceinline__ uint32_t e2m1_code(uint16_t bits, float inv_scale) {
+  const float a = fabsf(bf16_to_f32(bits) * inv_scale);
+  const uint32_t m = uint32_t(a > 0.25f) + uint32_t(a >= 0.75f) + uint32_t(a > 1.25f) + uint32_t(a >= 1.75f) +
+                     uint32_t(a > 2.5f) + uint32_t(a >= 3.5f) + uint32_t(a > 5.0f);
+  return ((uint32_t(bits) >> 12) & 8u) | m;
+}
+
+// One thread per group of 32 consecutive elements: shared exponent from the
+// largest magnitude (compared as bit patterns), then 16 packed code bytes
+// (element 2k in the low nibble) and one scale byte.
+__global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales, long long ngroups) {
+  const long long gi = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gi >= ngroups) return;
+  const uint4* src = reinterpret_cast<const uint4*>(x + gi * 32);
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = src[i];
+    w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+  }
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = max(amax, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+  int e = -127;
+  if (amax) {
+    const int ef = int(amax >> 7);
+    const int fl = ef > 0 ? ef - 127 : (31 - __builtin_clz(amax & 0x7fu)) - 133;   // floor(log2 max)
+    e = min(max(fl - 2, -127), 127);
+  }
+  scales[gi] = uint8_t(e + 127);
+  const float inv = __uint_as_float(uint32_t(127 - e) << 23);   // 2^-e, a normal float for finite inputs
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t word = w[4 * i + j];
+      const uint32_t byte = e2m1_code(uint16_t(word & 0xffffu), inv) | (e2m1_code(uint16_t(word >> 16), inv) << 4);
+      r |= byte << (8 * j);
+    }
+    out[i] = r;
+  }
+  *reinterpret_cast<uint4*>(codes + gi * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+hipError_t launch_quantize_mxfp4(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long ngroups,
+                                 hipStream_t s) {
+  const long long blocks = (ngroups + 255) / 256;
+  quantize_mxfp4_kernel<<<dim3(unsigned(blocks)), 256, 0, s>>>(x, codes, scales, ngroups);
+  return hipGetLastError();
+}
+
+// A row (one key block: h_idx x d_idx codes) is spread over LPR lanes, one
+// 32-element group (16 code bytes + its scale byte) per lane.
+template <int LPR>
+__global__ __launch_bounds__(256) void indexer_score_mxfp4_kernel(IndexerFp4Args a) {
+  constexpr int RPW = 64 / LPR;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / LPR, li = lane % LPR;
+  const int R = a.h_idx * a.d_idx;
+  const int lph = a.d_idx / 32;   // lanes per indexer head
+  const int e0 = li * 32;
+  const int head = e0 / a.d_idx;
+  uint32_t qw[16];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(a.idx_q + size_t(b) * R + e0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = qp[i];
+      qw[4 * i] = v.x; qw[4 * i + 1] = v.y; qw[4 * i + 2] = v.z; qw[4 * i + 3] = v.w;
+    }
+  }
+  const float w = a.idx_w[size_t(b) * a.h_idx + head];
+  const uint8_t* cb = a.codes + size_t(b) * a.nk * (R / 2);
+  const uint8_t* sb = a.scales + size_t(b) * a.nk * (R / 32);
+  const int step = gridDim.x * 4 * RPW * kIdxUnroll;
+  for (int t0 = (blockIdx.x * 4 + wave) * RPW * kIdxUnroll; t0 < a.nk; t0 += step) {
+    uint4 cv[kIdxUnroll];
+    int ex[kIdxUnroll];
+#pragma unroll
+    for (int u = 0; u < kIdxUnroll; ++u) {
+      const int t = t0 + u * RPW + sub;
+      const bool in = t < a.nk;
+      cv[u] = in ? *reinterpret_cast<const uint4*>(cb + size_t(t) * (R / 2) + li * 16) : make_uint4(0u, 0u, 0u, 0u);
+      ex[u] = in ? int(sb[size_t(t) * (R / 32) + li]) - 127 : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kIdxUnroll; ++u) {
+      const uint32_t cw[4] = {cv[u].x, cv[u].y, cv[u].z, cv[u].w};
+      float dp = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // byte j of word i holds elements 8i+2j (low nibble) and 8i+2j+1
+        dp = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[i], 1.0f, 0)),
+                       qw[4 * i + 0], dp);
+        dp = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[i], 1.0f, 1)),
+                       qw[4 * i + 1], dp);
+        dp = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[i], 1.0f, 2)),
+                       qw[4 * i + 2], dp);
+        dp = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[i], 1.0f, 3)),
+                       qw[4 * i + 3], dp);
+      }
+      dp = ldexpf(dp, ex[u]);
+      for (int o = 1; o < lph; o <<= 1) dp += __shfl_xor(dp, o);
+      float val = (li % lph) == 0 ? w * fmaxf(dp, 0.f) : 0.f;
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1)
+        if (o >= lph) val += __shfl_xor(val, o);
+      const int t = t0 + u * RPW + sub;
+      if (li == 0 && t < a.nk) a.scores[size_t(b) * a.nk + t] = val;
+    }
+  }
+}
+
+template <int LPR>
+static void launch_idx_fp4(const IndexerFp4Args& a, hipStream_t s) {
+  const int per_block = 4 * (64 / LPR) * kIdxUnroll;
+  int blocks = (a.nk + per_block - 1) / per_block;
+  if (blocks > kIdxMaxBlocks) blocks = kIdxMaxBlocks;
+  indexer_score_mxfp4_kernel<LPR><<<dim3(blocks, a.batch), 256, 0, s>>>(a);
+}
+
+hipError_t launch_indexer_score_mxfp4(const IndexerFp4Args& a, hipStream_t s) {
+  const int lanes = (a.h_idx * a.d_idx) / 32;   // one 32-element group per lane (R <= 256)
+  if (lanes <= 1) launch_idx_fp4<1>(a, s);
+  else if (lanes <= 2) launch_idx_fp4<2>(a, s);
+  else if (lanes <= 4) launch_idx_fp4<4>(a, s);
+  else launch_idx_fp4<8>(a, s);
   return hipGetLastError();
 }
 

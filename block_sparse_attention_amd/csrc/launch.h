@@ -41,6 +41,18 @@ struct IndexerScoreArgs {
 };
 hipError_t launch_indexer_score(const IndexerScoreArgs& a, hipStream_t s);
 
+struct IndexerFp4Args {
+  const uint16_t* idx_q;  // [batch, h_idx, d_idx] bf16
+  const float* idx_w;     // [batch, h_idx]
+  const uint8_t* codes;   // [batch, nk, h_idx * d_idx / 2] packed E2M1 pairs
+  const uint8_t* scales;  // [batch, nk, h_idx * d_idx / 32] E8M0
+  float* scores;          // [batch, nk]
+  int batch, nk, h_idx, d_idx;
+};
+hipError_t launch_indexer_score_mxfp4(const IndexerFp4Args& a, hipStream_t s);
+hipError_t launch_quantize_mxfp4(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long ngroups,
+                                 hipStream_t s);
+
 struct SelectArgs {
   const float* scores;  // [rows, nk]
   int32_t* idx;         // [rows, nk]

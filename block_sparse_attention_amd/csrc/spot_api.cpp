@@ -259,6 +259,38 @@ int spot_sparse_attn_prefill(const spot_desc* desc, const void* q, const void* k
   return launched(spot::launch_prefill(a, static_cast<hipStream_t>(stream)), "sparse_attn_prefill");
 }
 
+static int check_mxfp4_indexer(const spot_desc* desc) {
+  int st = check_common(desc);
+  if (st) return st;
+  if (desc->score_kind != SPOT_SCORE_RELU_INDEXER) return fail(SPOT_ERR_INVALID, "score_kind must be RELU_INDEXER");
+  if ((st = check_indexer(desc))) return st;
+  if (desc->d_idx % 32) return fail(SPOT_ERR_UNSUPPORTED, "MXFP4 needs d_idx a multiple of 32 (got %d)", desc->d_idx);
+  return SPOT_OK;
+}
+
+int spot_quantize_indexer_keys(const spot_desc* desc, const void* idx_k, uint8_t* k_codes, uint8_t* k_scales,
+                               void* stream) {
+  int st = check_mxfp4_indexer(desc);
+  if (st) return st;
+  if (!idx_k || !k_codes || !k_scales) return fail(SPOT_ERR_INVALID, "idx_k, k_codes and k_scales are required");
+  const long long nk = ceil_div64(desc->kv_len, desc->block);
+  const long long groups = (long long)desc->batch * nk * (desc->h_idx * desc->d_idx / 32);
+  return launched(spot::launch_quantize_mxfp4(static_cast<const uint16_t*>(idx_k), k_codes, k_scales, groups,
+                                              static_cast<hipStream_t>(stream)),
+                  "quantize_indexer_keys");
+}
+
+int spot_indexer_score_mxfp4(const spot_desc* desc, const void* idx_q, const float* idx_w, const uint8_t* k_codes,
+                             const uint8_t* k_scales, float* scores, void* stream) {
+  int st = check_mxfp4_indexer(desc);
+  if (st) return st;
+  if (!idx_q || !idx_w || !k_codes || !k_scales || !scores)
+    return fail(SPOT_ERR_INVALID, "idx_q, idx_w, k_codes, k_scales and scores are required");
+  spot::IndexerFp4Args a{static_cast<const uint16_t*>(idx_q), idx_w, k_codes, k_scales, scores, desc->batch,
+                         int(ceil_div64(desc->kv_len, desc->block)), desc->h_idx, desc->d_idx};
+  return launched(spot::launch_indexer_score_mxfp4(a, static_cast<hipStream_t>(stream)), "indexer_score_mxfp4");
+}
+
 int spot_order_history(const spot_desc* desc, const float* scores, int32_t* order, int32_t* cnt, void* workspace,
                        size_t workspace_bytes, void* stream) {
   (void)workspace;

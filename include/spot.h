@@ -11,6 +11,11 @@
  *   spot_sparse_attn_decode  the same for one decode query per sequence
  *   spot_key_permutation     the intra-segment key permutation the prefill gathers through
  *
+ * the selector key cache in FP4 microscaling for the decode scan:
+ *
+ *   spot_quantize_indexer_keys  encode the indexer keys as MXFP4
+ *   spot_indexer_score_mxfp4    the RELU_INDEXER scores from that encoding
+ *
  * and an early-stopped variant of selection + prefill attention:
  *
  *   spot_order_history                  visiting order of each query block's history blocks
@@ -203,6 +208,33 @@ int spot_sparse_attn_decode(const spot_desc* desc, const void* q, const void* k_
  */
 int spot_key_permutation(const spot_desc* desc, const void* q, const void* k, int32_t* perm, float* importance,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Selector key cache in FP4 microscaling ([Spot] §4 quantisation: the
+ * selector's K-cache held as INT4/FP4 microscale).  The format is OCP
+ * Microscaling (MX) v1.0 MXFP4: every 32 consecutive elements of an indexer
+ * key row (h_idx * d_idx elements, so d_idx must be a multiple of 32) share
+ * one E8M0 scale byte e (scale 2^(e-127)); each element is a 4-bit E2M1 code
+ * (bit 3 sign, bits 0-2 index into 0, 0.5, 1, 1.5, 2, 3, 4, 6), two codes per
+ * byte with the even element in the low nibble.
+ * Layouts: k_codes uint8 [batch, nk, h_idx*d_idx/2]; k_scales uint8
+ * [batch, nk, h_idx*d_idx/32]; nk = ceil(kv_len / block).
+ *
+ * spot_quantize_indexer_keys: idx_k bf16 [batch, nk, h_idx, d_idx] (finite)
+ *   -> codes and scales.  Per group: e = floor(log2(max |x|)) - 2 clamped to
+ *   [-127, 127] (-127 for an all-zero group); each x / 2^e is rounded to the
+ *   nearest E2M1 value, ties to the even code, saturating at 6; the sign bit
+ *   is the input's.  Deterministic and exact (scales are powers of two).
+ * spot_indexer_score_mxfp4: as spot_block_score with RELU_INDEXER, with the
+ *   keys read from the encoding (decoded value = E2M1 value * 2^(e-127)):
+ *     scores[b,0,0,t] = sum_h idx_w[b,h] * max(0, < idx_q[b,h], key[b,t,h] >)
+ * Both need score_kind RELU_INDEXER and the indexer limits of
+ * spot_block_score; no workspace.
+ */
+int spot_quantize_indexer_keys(const spot_desc* desc, const void* idx_k, uint8_t* k_codes, uint8_t* k_scales,
+                               void* stream);
+int spot_indexer_score_mxfp4(const spot_desc* desc, const void* idx_q, const float* idx_w, const uint8_t* k_codes,
+                             const uint8_t* k_scales, float* scores, void* stream);
 
 /*
  * Visiting order for early stopping ([S2O] §2: candidate blocks are processed

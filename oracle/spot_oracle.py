@@ -194,27 +194,23 @@ def mxfp4_quantize(x):
     shape = x.shape
     g = x.reshape(-1, MX_GROUP)
     grid = np.array(E2M1_MAGNITUDES)
+    even = (np.arange(len(grid)) % 2 == 0)
     codes = np.zeros(g.shape, dtype=np.uint8)
     scales = np.zeros(g.shape[0], dtype=np.uint8)
-    for r in range(g.shape[0]):
-        amax = np.abs(g[r]).max()
-        if amax == 0:
-            e = -127
-        else:
-            _, ex = np.frexp(amax)          # amax = m * 2**ex, 0.5 <= m < 1
-            e = int(ex) - 1 - 2             # floor(log2(amax)) - 2
-            e = max(-127, min(127, e))
-        scales[r] = e + 127
-        y = g[r] / 2.0 ** e
-        for c in range(MX_GROUP):
-            a = abs(y[c])
-            if a >= grid[-1]:
-                m = len(grid) - 1
-            else:
-                dist = np.abs(grid - a)
-                best = np.nonzero(dist == dist.min())[0]
-                m = int(best[0]) if best.size == 1 else int(best[best % 2 == 0][0])
-            codes[r, c] = (8 if np.signbit(y[c]) else 0) | m
+    for r0 in range(0, g.shape[0], 1 << 14):          # groups in chunks (memory only)
+        gc = g[r0:r0 + (1 << 14)]
+        amax = np.abs(gc).max(axis=1)
+        _, ex = np.frexp(amax)                           # amax = m * 2**ex, 0.5 <= m < 1
+        e = np.where(amax == 0, -127, np.clip(ex.astype(np.int64) - 1 - 2, -127, 127))   # floor(log2) - 2
+        scales[r0:r0 + len(gc)] = (e + 127).astype(np.uint8)
+        y = gc / np.exp2(e.astype(np.float64))[:, None]
+        a = np.abs(y)
+        dist = np.abs(grid[None, None, :] - a[..., None])
+        nearest = dist == dist.min(axis=-1, keepdims=True)
+        # the nearest value; of two equally near, the one with the even code
+        m = np.where((nearest & even).any(axis=-1), np.argmax(nearest & even, axis=-1), np.argmax(nearest, axis=-1))
+        m = np.where(a >= grid[-1], len(grid) - 1, m)
+        codes[r0:r0 + len(gc)] = (np.where(np.signbit(y), 8, 0) | m).astype(np.uint8)
     return codes.reshape(shape), scales.reshape(shape[:-1] + (shape[-1] // MX_GROUP,))
 
 
