@@ -172,7 +172,8 @@ def bench_prefill(args, torch, B, I, score_kind=None):
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
                 "traffic": load_traffic(attn_file, f"prefill_mfma_kernel@{cfg.name}"),
-                "kernel": "prefill_mfma_kernel<128,8>", "flop_per_launch": flops, "avg_launch_ms": round(ms_attn, 4)}
+                "kernel": f"prefill_mfma_kernel<{cfg.d},8,1,{'true' if cfg.segment else 'false'},false>",
+                "flop_per_launch": flops, "avg_launch_ms": round(ms_attn, 4)}
     else:   # the fp32 row kernel on a 256-token input is launch-latency bound
         roof = {"bound": "latency", "achieved": round(achieved, 4), "peak": None, "unit": "TFLOP/s", "frac": None,
                 "traffic": None, "kernel": "prefill_rows_kernel<float,64>", "flop_per_launch": flops,
@@ -197,7 +198,7 @@ def bench_decode(args, torch, B, I, mxfp4=False):
     del D
     desc = B.decode_desc(q, kc, cfg.block, cfg.top_p, cfg.h_idx, cfg.d_idx)
     bufs = B.alloc_decode(desc, dev)
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     if mxfp4:   # the cache is encoded once, when keys are appended (outside the step)
         kcodes, kscales = B.quantize_indexer_keys(ik, cfg.block, cfg.T)
         torch.cuda.synchronize()
@@ -222,7 +223,7 @@ def bench_decode(args, torch, B, I, mxfp4=False):
         step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for e in evs:
-        flush.fill_(1.0)          # evict the 256 MB last-level cache between steps (outside the events)
+        flush.sum()               # read 512 MB between steps (outside the events): evicts the 256 MB last-level cache
         step(e)
     torch.cuda.synchronize()
     ms_front = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
@@ -239,7 +240,7 @@ def bench_decode(args, torch, B, I, mxfp4=False):
     graph.replay()
     gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for e in gev:
-        flush.fill_(1.0)
+        flush.sum()
         e[0].record()
         graph.replay()
         e[1].record()
@@ -264,6 +265,8 @@ def bench_decode(args, torch, B, I, mxfp4=False):
         kept_fraction=round(float(kept_keys.sum()) / (cfg.batch * cfg.T), 4), bytes_per_step=step_bytes,
         roofline={"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "kernel": "decode_split_kernel<128,4>+combine",
+                  "traffic": load_traffic(os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "kernels",
+                                                       "decode.hip"), f"decode_split_kernel@{cfg.name}"),
                   "bytes_per_launch": kv_bytes + qo_bytes},
     )
 
@@ -352,7 +355,10 @@ def bench_early_stop(args, torch, B, I):
         flop_per_step=flops,
         roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                   "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                  "kernel": "prefill_mfma_kernel<128,8,early stop>", "avg_launch_ms": round(ms_attn, 4),
+                  "kernel": "prefill_mfma_kernel<128,8,1,true,true> (early stop)", "avg_launch_ms": round(ms_attn, 4),
+                  "traffic": load_traffic(os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "kernels",
+                                                       "prefill.hip"),
+                                          f"prefill_mfma_kernel_early_stop@{cfg.name}"),
                   "walked_tflops": round(4.0 * cfg.d * walked / (ms_attn * 1e-3) / 1e12, 2)},
     )
 

@@ -23,12 +23,19 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 KDIR = os.path.join(PKG, "csrc", "kernels")
 COPY_BYTES = 1 << 30
 
-# kernel-name fragment -> (source file, workload key)
+# kernel-name fragment -> (source file, workload key, launches used).  The
+# profiling workload runs its parts in a fixed order (GQA prefill, decode with
+# the bf16 indexer cache, decode with the MXFP4 cache, early-stopped
+# heavy-hitter prefill), so "first" takes the first `--steps` launches of a
+# kernel that several parts use, "all" every launch.
 TRACKED = {
-    "prefill_mfma_kernel<128, 8, false>": ("prefill.hip", "prefill_mfma_kernel@gqa-bf16-L8192"),
-    "decode_split_kernel<128, 4>": ("decode.hip", "decode_split_kernel@decode-b16-T131072"),
-    "indexer_score_kernel": ("score.hip", "indexer_score_kernel@decode-b16-T131072"),
-    "pool_blocks_kernel<unsigned short>": ("score.hip", "pool_blocks_kernel@gqa-bf16-L8192"),
+    "prefill_mfma_kernel<128, 8, 1, false, false>": ("prefill.hip", "prefill_mfma_kernel@gqa-bf16-L8192", "all"),
+    "prefill_mfma_kernel<128, 8, 1, true, true>": ("prefill.hip",
+                                                   "prefill_mfma_kernel_early_stop@heavy-perm-bf16-L32768", "all"),
+    "decode_split_kernel<128, 4>": ("decode.hip", "decode_split_kernel@decode-b16-T131072", "first"),
+    "indexer_score_kernel<": ("score.hip", "indexer_score_kernel@decode-b16-T131072", "all"),
+    "indexer_score_mxfp4_kernel": ("score.hip", "indexer_score_mxfp4_kernel@decode-b16-T131072", "all"),
+    "pool_blocks_kernel<unsigned short>": ("score.hip", "pool_blocks_kernel@gqa-bf16-L8192", "first"),
 }
 
 
@@ -83,6 +90,7 @@ def main():
     ap.add_argument("--cmd-pmc", default="")
     ap.add_argument("--out", default="profiles")
     ap.add_argument("--name", default="kernels")
+    ap.add_argument("--steps", type=int, default=3, help="--steps of the profiling workload")
     args = ap.parse_args()
     os.makedirs(args.out, exist_ok=True)
 
@@ -101,14 +109,17 @@ def main():
                   "", f"Calibration on a 1 GiB device copy: FETCH_SIZE reads {ff:.4f} x the bytes moved, "
                   f"WRITE_SIZE {wf:.4f} x; measured values below are divided by these factors.", "",
                   "| kernel | launches | fetch MB | write MB | total MB |", "|---|---:|---:|---:|---:|"]
-        for frag, (src, key) in TRACKED.items():
+        for frag, (src, key, use) in TRACKED.items():
             fk = [k for k in fv if frag in k]
             wk = [k for k in wv if frag in k]
             if not fk or not wk:
                 continue
-            fetch = statistics.median(fv[fk[0]]) * 1024 / ff
-            write = statistics.median(wv[wk[0]]) * 1024 / wf
-            lines.append(f"| `{frag}` | {len(fv[fk[0]])} | {fetch / 1e6:.2f} | {write / 1e6:.2f} | "
+            fl, wl = fv[fk[0]], wv[wk[0]]
+            if use == "first":
+                fl, wl = fl[:args.steps], wl[:args.steps]
+            fetch = statistics.median(fl) * 1024 / ff
+            write = statistics.median(wl) * 1024 / wf
+            lines.append(f"| `{frag}` ({key.split('@')[1]}) | {len(fl)} | {fetch / 1e6:.2f} | {write / 1e6:.2f} | "
                          f"{(fetch + write) / 1e6:.2f} |")
             traffic[key] = {"bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch),
                             "write_bytes": round(write), "source_sha256_16": digest(os.path.join(KDIR, src)),

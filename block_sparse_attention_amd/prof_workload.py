@@ -2,9 +2,11 @@
 
 Runs, on cuda:0: `--steps` prefill steps of the GQA workload (L=8192, 32/8
 heads, d=128, bf16, block 64, top-p 0.9), `--steps` decode steps of the sparse
-decode workload (batch 16, context 131072), and `--steps` plain device copies
-of 1 GiB, whose counter readings calibrate FETCH_SIZE / WRITE_SIZE against a
-known byte count.
+decode workload (batch 16, context 131072) with the bf16 and with the MXFP4
+indexer cache, `--steps` early-stopped prefill steps of the heavy-hitter
+workload (L=32768, segment 2048, tau 0.01, permutation on the GPU), and
+`--steps` plain device copies of 1 GiB, whose counter readings calibrate
+FETCH_SIZE / WRITE_SIZE against a known byte count.
 
   rocprofv3 --kernel-trace --stats -d OUT -o run -- python -m block_sparse_attention_amd.prof_workload
   rocprofv3 --pmc FETCH_SIZE -d OUT -o fetch -- python -m block_sparse_attention_amd.prof_workload
@@ -27,6 +29,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-early-stop", action="store_true")
     args = ap.parse_args()
     B.load_library()
     dev = torch.device("cuda:0")
@@ -53,6 +56,26 @@ def main():
                              dc.top_p, bufs=dbufs)
         torch.cuda.synchronize()
         print(f"decode steps done: {args.steps}", flush=True)
+        codes, scales = B.quantize_indexer_keys(t["idx_k"], dc.block, dc.T)
+        for _ in range(args.steps):
+            dbufs = B.decode(t["q"], t["k_cache"], t["v_cache"], t["idx_q"], t["idx_w"], (codes, scales),
+                             dc.block, dc.top_p, bufs=dbufs)
+        torch.cuda.synchronize()
+        print(f"decode steps with the MXFP4 indexer cache done: {args.steps}", flush=True)
+        del t, codes, scales, dbufs
+
+    if not args.no_early_stop:
+        ec = I.C3
+        q, k, v = I.prefill_inputs(ec)
+        eq, ek, ev = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q, k, v))
+        del q, k, v
+        perm = B.key_permutation(eq, ek, ec.block, ec.segment)
+        ebufs = None
+        for _ in range(args.steps):
+            ebufs = B.prefill_early_stop(eq, ek, ev, ec.block, ec.segment, 0.01, perm=perm, bufs=ebufs)
+        torch.cuda.synchronize()
+        print(f"early-stopped prefill steps done: {args.steps}", flush=True)
+        del eq, ek, ev, perm, ebufs
 
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
