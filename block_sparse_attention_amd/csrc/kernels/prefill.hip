@@ -14,8 +14,9 @@
 //   head g, query block i); packed row p is head g*G + p/B, row i*B + p%B,
 //   so the G query heads of a group share every K/V tile (GQA packing).
 //   Key tiles of 64 slots walk the concatenated kept blocks; each slot is
-//   gathered (natural or permuted row) from HBM into registers one tile ahead
-//   and written to LDS: K row-major, V transposed (Vt[d][key]).
+//   gathered (natural or permuted row) from HBM into registers ahead of use
+//   (K two tiles, V one tile) and written to LDS row-major; the V^T operand
+//   of the PV product is read with the transposing LDS load.
 //   S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16, so every
 //   lane owns one query column: row max/sum stay in-lane plus one exchange
 //   between the two lane halves.  P is rounded to bf16 for the PV product.
