@@ -363,6 +363,37 @@ def bench_early_stop(args, torch, B, I):
     )
 
 
+# ----------------------------------------------------------------- measured ceilings
+def measured_ceilings(torch):
+    """Context for the rooflines: a dense bf16 GEMM (8192^3, the vendor BLAS
+    through torch) and a 1 GiB device-to-device copy on the same GPU."""
+    dev = torch.device("cuda:0")
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    gemm = 2.0 * 8192 ** 3 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
+    del a, b, c
+    src = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy = 2.0 * (1 << 30) / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e9
+    return {"bf16_gemm_8192_tflops": round(gemm, 1), "device_copy_1gib_gbs": round(copy, 1)}
+
+
 # ----------------------------------------------------------------- oracle on the host
 def cpu_baseline(res, I, sample_blocks: int):
     """The float64 oracle on the host over the workload (or a seeded sample of
@@ -441,6 +472,8 @@ def main():
                "flop_per_step": t["flops"]}
         del t
         print(f"[bench] taylor: {tay}", file=sys.stderr, flush=True)
+    ceil = measured_ceilings(torch)
+    print(f"[bench] measured ceilings: {ceil}", file=sys.stderr, flush=True)
     es = None
     if not args.no_early_stop:
         es = bench_early_stop(args, torch, B, I)
@@ -462,7 +495,7 @@ def main():
                    "ms_per_step_eager_launches": round(pre["ms_step_eager"], 4), "step_launch": "hip_graph_replay",
                    "segment": cfg.segment, "ms_key_permutation": round(pre["ms_perm"], 4),
                    "flop_per_step": pre["flops"]},
-        "roofline": pre["roofline"],
+        "roofline": dict(pre["roofline"], measured_ceilings=ceil),
         "cpu_baseline": cpu,
         "decode": dec,
         "decode_mxfp4_indexer": dec_mx,
