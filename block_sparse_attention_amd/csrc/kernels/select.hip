@@ -23,6 +23,9 @@ namespace spot {
 
 constexpr int kSelMaxPerThread = 16;   // candidates per thread (16384 / 1024)
 constexpr int kSortMax = 2048;         // candidates sorted exactly in LDS
+constexpr int kRefineMin = 128;        // long rows: above this many candidates, narrow them by a score histogram
+constexpr int kHistBins = 64;          // histogram bins of width 1/kHistScale in score units below the row max
+constexpr float kHistScale = 4.0f;
 
 __device__ __forceinline__ uint32_t score_key(float s) {
   const uint32_t u = __float_as_uint(s) == 0x80000000u ? 0u : __float_as_uint(s);   // -0 ties with +0
@@ -132,6 +135,9 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
   __shared__ uint64_t s_sort[kSortMax];
   __shared__ uint16_t s_rank[kSortMax];
   __shared__ int s_kstar;
+  __shared__ int s_hcnt[kHistBins];
+  __shared__ float s_hmass[kHistBins];
+  __shared__ int s_bcut;
   const int nk = a.nk;
   const int row = blockIdx.x;
   const int tid = threadIdx.x, nthr = blockDim.x;
@@ -164,7 +170,8 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
       }
     }
   }
-  const int n_res = block_sum_i32(__popc(resid), sc);
+  // forced blocks: the first n_sink and the last n_recent of the n candidates (they may overlap)
+  const int n_res = n - min(n, min(n, max(a.n_sink, 0)) + min(n, max(a.n_recent, 0)));
 
   if (a.top_p >= 1.0f) {   // every residual block
     write_row(a, row, forcedm | resid, c0, sc);
@@ -200,9 +207,57 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
         if ((resid & (1u << e)) && ex[e] > bound) candm |= 1u << e;
     }
   }
-  const bool filtered = candm != resid || n_res > kSortMax;
+  bool filtered = candm != resid || n_res > kSortMax;
   int ncand;
-  const int off = block_excl_scan_i32(__popc(candm), sc, ncand);
+  int off = block_excl_scan_i32(__popc(candm), sc, ncand);
+  if (by_mass && ncand > kRefineMin) {
+    // Narrow the candidates with a histogram of their masses over score bins
+    // below the row max: keep the bins down to one past the bin where the
+    // (fp32, any-order) cumulative mass first reaches the target.  The kept
+    // set is still decided by the exact scan below over a prefix of the
+    // sorted order; if the narrowed set falls short of the target, that scan
+    // finds no crossing and the cutoff search runs instead.
+    if (tid < kHistBins) {
+      s_hcnt[tid] = 0;
+      s_hmass[tid] = 0.f;
+    }
+    __syncthreads();
+    uint8_t bin[kSelMaxPerThread];
+#pragma unroll
+    for (int e = 0; e < kSelMaxPerThread; ++e) {
+      bin[e] = 0;
+      if (candm & (1u << e)) {
+        const float dsc = (gmax - key_score(key[e])) * kHistScale;
+        const int bi = dsc < float(kHistBins - 1) ? int(dsc) : kHistBins - 1;
+        bin[e] = uint8_t(bi);
+        atomicAdd(&s_hcnt[bi], 1);
+        atomicAdd(&s_hmass[bi], float(ex[e]));
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      const float goal = float(target) * 1.001f;
+      float cum = 0.f;
+      int cnt = 0, b = 0;
+      for (; b < kHistBins; ++b) {
+        cum += s_hmass[b];
+        cnt += s_hcnt[b];
+        if (cum >= goal) break;
+      }
+      int bcut = min(b + 1, kHistBins - 1);
+      if (b + 1 < kHistBins) cnt += s_hcnt[b + 1];
+      s_bcut = (b < kHistBins && cnt < ncand && cnt >= kfloor) ? bcut : kHistBins;   // kHistBins: keep all
+    }
+    __syncthreads();
+    const int bcut = s_bcut;
+    if (bcut < kHistBins) {
+#pragma unroll
+      for (int e = 0; e < kSelMaxPerThread; ++e)
+        if ((candm & (1u << e)) && int(bin[e]) > bcut) candm &= ~(1u << e);
+      filtered = true;
+      off = block_excl_scan_i32(__popc(candm), sc, ncand);
+    }
+  }
   if (ncand <= kSortMax && ncand >= kfloor) {
     int cap = 2;
     while (cap < ncand) cap <<= 1;
