@@ -130,6 +130,36 @@ __device__ void write_row(const SelectArgs& a, int row, uint32_t keepm, int c0, 
   if (threadIdx.x == 0) a.cnt[row] = total_kept;
 }
 
+// Bitonic sort of the 128 keys s[0..128) ascending by one wave: key i lives in
+// lane i % 64, register i / 64; partners 64 apart meet in one lane, closer
+// ones across lanes through a shuffle.  No workgroup barrier is needed.
+constexpr int kWaveSort = 128;
+__device__ void wave_sort128(uint64_t* s, int lane) {
+  uint64_t x[2] = {s[lane], s[lane + 64]};
+#pragma unroll
+  for (int k = 2; k <= 128; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j == 64) {   // only k == 128: ascending across the two registers
+        const uint64_t lo = x[0] < x[1] ? x[0] : x[1], hi = x[0] < x[1] ? x[1] : x[0];
+        x[0] = lo;
+        x[1] = hi;
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int i = lane + 64 * h;
+          const uint64_t y = __shfl_xor(x[h], j);
+          const bool asc = (i & k) == 0, lower = (i & j) == 0;
+          const bool take_min = asc == lower;
+          x[h] = take_min ? (x[h] < y ? x[h] : y) : (x[h] < y ? y : x[h]);
+        }
+      }
+    }
+  }
+  s[lane] = x[0];
+  s[lane + 64] = x[1];
+}
+
 __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
   __shared__ SelScratch sc;
   __shared__ uint64_t s_sort[kSortMax];
@@ -261,6 +291,7 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
   if (ncand <= kSortMax && ncand >= kfloor) {
     int cap = 2;
     while (cap < ncand) cap <<= 1;
+    if (cap <= kWaveSort) cap = kWaveSort;   // small sets: one wave sorts 128 keys in registers
     int w = off;
 #pragma unroll
     for (int e = 0; e < kSelMaxPerThread; ++e)
@@ -270,6 +301,10 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
       }
     for (int k = ncand + tid; k < cap; k += nthr) s_sort[k] = ~0ull;
     __syncthreads();
+    if (cap == kWaveSort) {
+      if (tid < 64) wave_sort128(s_sort, tid);
+      __syncthreads();
+    } else
     for (int k = 2; k <= cap; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
         for (int e = tid; e < cap; e += nthr) {
