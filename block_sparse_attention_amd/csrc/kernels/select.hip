@@ -22,6 +22,11 @@
 namespace spot {
 
 constexpr int kSelMaxPerThread = 16;   // candidates per thread (16384 / 1024)
+#ifndef SPOT_SELECT_PER_THREAD
+#define SPOT_SELECT_PER_THREAD 16
+#endif
+constexpr int kSelTargetPerThread = SPOT_SELECT_PER_THREAD;   // launch as few threads as keep at most this many per thread
+static_assert(kSelTargetPerThread <= kSelMaxPerThread, "per-thread runs are register arrays");
 constexpr int kSortMax = 2048;         // candidates sorted exactly in LDS
 constexpr int kRefineMin = 128;        // long rows: above this many candidates, narrow them by a score histogram
 constexpr int kHistBins = 64;          // histogram bins of width 1/kHistScale in score units below the row max
@@ -509,7 +514,7 @@ hipError_t launch_select_topp(const SelectArgs& a, hipStream_t s) {
   // as few waves as keep every thread at kSelMaxPerThread candidates or fewer:
   // the row is a chain of block-wide steps, and barriers over fewer waves are cheaper
   int threads = 64;
-  while (threads < 1024 && threads * kSelMaxPerThread < a.nk) threads <<= 1;
+  while (threads < 1024 && threads * kSelTargetPerThread < a.nk) threads <<= 1;
   select_topp_kernel<<<a.rows, threads, 0, s>>>(a);
   return hipGetLastError();
 }

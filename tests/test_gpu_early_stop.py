@@ -127,6 +127,7 @@ ES_CASES = [
     dict(L=1280, block=128, segment=256, tau=0.0, perm=True),           # dense causal
     dict(L=1280, block=64, segment=128, tau=2.0, perm=True, hq=16, hkv=2),  # one history block per row
     dict(L=900, block=64, segment=64, tau=0.003, perm=False, hq=6, hkv=3, d=64),
+    dict(L=1100, block=64, segment=256, tau=0.01, perm=True, batch=2),     # two sequences, ragged
 ]
 
 

@@ -21,6 +21,7 @@ CASES = [
     dict(L=513, hq=4, hkv=4, d=128, block=16, top_p=0.7),
     dict(L=2048, hq=16, hkv=2, d=128, block=128, top_p=0.95, heavy_hitters=True),
     dict(L=300, hq=2, hkv=2, d=64, block=16, top_p=0.9, dtype="f32"),
+    dict(L=900, hq=8, hkv=2, d=128, block=64, top_p=0.9, batch=2),
 ]
 
 
