@@ -40,6 +40,10 @@ What each function follows:
                      pooling of attention, keys sorted descending per segment)
   history_order      [S2O] §2 (candidate blocks visited in descending estimated
                      importance)
+  representative_queries, history_map
+                     [S2O] §1 (historical keys scored against a representative
+                     query of the segment, prefix only; the sorted positions
+                     form the segment's logical map of its history)
   attend_prefill_es  [S2O] §2 (monotone-gain early stopping) and §3 (dense
                      causal pass over the own segment, then the permuted
                      history in that order, resuming the same softmax state)
@@ -60,6 +64,10 @@ MXFP4: the shared exponent is floor(log2(max |x|)) - 2 (the largest E2M1
 exponent), clamped to the E8M0 range, -127 for an all-zero group; elements
 are rounded to the nearest E2M1 value, ties to the even code, and saturate at
 6; the sign bit is the input's sign bit (so -0 keeps its sign).
+Representative query: the mean of Q over the group's heads and the segment's
+rows; the history map sorts the prefix by sm_scale * <representative, key>
+descending, ties by position; early-stopped attention on the map visits its
+consecutive runs of B positions in order.
 Taylor score: the second-order expansion is taken for the scaled query
 (sm_scale * qbar) and enters the top-p rule as the log of the estimated block
 mass, so the softmax over blocks is the normalised mass estimate; variances
@@ -465,20 +473,26 @@ def history_order(scores, block, segment, rows=None):
     return order
 
 
-def _es_blocks(q, k, i, g, h, order_gi, block, segment, sm_scale, perm):
+def _es_blocks(q, k, i, g, h, order_gi, block, segment, sm_scale, perm, hmap=None):
     """Masses of one query block's rows for head h, in one fixed frame.
 
     Returns (e_own, own_phys, e_hist, hist_phys, shift): e_own (rows, n_own)
     = exp(logit - shift) over the own-segment keys (0 where the causal mask
     hides the key), e_hist (rows, n_hist_blocks, B) the same for the history
     blocks in visiting order, shift (rows,) the row's largest visible logit.
+    With `hmap` (the history maps of history_map), the history blocks are the
+    consecutive runs of B positions of the segment's map, in map order, and
+    `order_gi` and `perm` are not used.
     """
     L = q.shape[1]
     rows = block_rows(i, block, L)
     s0 = ((i * block) // segment) * segment
     own = np.arange(s0, min(rows[-1] + 1, L))
-    hist = [perm[g, block_rows(int(j), block, L)] if perm is not None else block_rows(int(j), block, L)
-            for j in order_gi]
+    if hmap is not None:
+        hist = list(np.asarray(hmap[g, s0 // segment, :s0], dtype=np.int64).reshape(-1, block))
+    else:
+        hist = [perm[g, block_rows(int(j), block, L)] if perm is not None else block_rows(int(j), block, L)
+                for j in order_gi]
     hist_phys = np.stack(hist) if hist else np.zeros((0, block), dtype=np.int64)
     lo = sm_scale * (q[h, rows] @ k[g, own].T)
     lo = np.where(own[None, :] <= rows[:, None], lo, -np.inf)
@@ -489,20 +503,20 @@ def _es_blocks(q, k, i, g, h, order_gi, block, segment, sm_scale, perm):
     return np.exp(lo - shift[:, None]), own, np.exp(lh - shift[:, None, None]), hist_phys, shift
 
 
-def es_gain_ratios(q, k, i, g, h, order_gi, block, segment, sm_scale, perm=None):
+def es_gain_ratios(q, k, i, g, h, order_gi, block, segment, sm_scale, perm=None, hmap=None):
     """[S2O] §2: for each row of query block i and head h, the marginal gain
     of each visited history block relative to the mass accumulated including
     it: ratio[r, n] = gain_n / (own mass + gain_1 + ... + gain_n)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
-    e_own, _, e_hist, _, _ = _es_blocks(q, k, i, g, h, order_gi, block, segment, sm_scale, perm)
+    e_own, _, e_hist, _, _ = _es_blocks(q, k, i, g, h, order_gi, block, segment, sm_scale, perm, hmap)
     gain = e_hist.sum(axis=2)
     acc = e_own.sum(axis=1)[:, None] + np.cumsum(gain, axis=1)
     return gain / acc
 
 
 def attend_prefill_es(q, k, v, order, block, segment, sm_scale, tau, perm=None, qblocks=None,
-                      nused=None):
+                      nused=None, hmap=None):
     """[S2O] §2-3 early-stopped attention for every query row.
 
     Pass 1: the row's own segment in natural order under the causal mask.
@@ -513,8 +527,10 @@ def attend_prefill_es(q, k, v, order, block, segment, sm_scale, tau, perm=None, 
 
     nused (Hq, L) int, optional: use these numbers of visited history blocks
     instead of the rule (to evaluate the output at another implementation's
-    decisions).  Returns O (Hq, L, d), LSE (Hq, L) and the numbers of visited
-    history blocks (Hq, L); rows outside `qblocks` are NaN / -1.
+    decisions).  With `hmap`, pass 2 visits the runs of B positions of the
+    segment's history map (history_map) in order instead.  Returns O
+    (Hq, L, d), LSE (Hq, L) and the numbers of visited history blocks
+    (Hq, L); rows outside `qblocks` are NaN / -1.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -533,7 +549,7 @@ def attend_prefill_es(q, k, v, order, block, segment, sm_scale, tau, perm=None, 
             rows = block_rows(i, block, L)
             for h in range(g * G, (g + 1) * G):
                 e_own, own, e_hist, hist_phys, shift = _es_blocks(
-                    q, k, i, g, h, order[g][i], block, segment, sm_scale, perm)
+                    q, k, i, g, h, None if order is None else order[g][i], block, segment, sm_scale, perm, hmap)
                 n_h = e_hist.shape[1]
                 gain = e_hist.sum(axis=2)
                 acc = e_own.sum(axis=1)[:, None] + np.cumsum(gain, axis=1)
@@ -551,6 +567,43 @@ def attend_prefill_es(q, k, v, order, block, segment, sm_scale, tau, perm=None, 
                     lse[h, r] = shift[ri] + np.log(z)
                     used[h, r] = n
     return o, lse, used
+
+
+def representative_queries(q, hkv, segment):
+    """[S2O] §1: per KV head g and segment s, the mean of Q over the G heads
+    of the group and the rows of the segment.  q: (Hq, L, d) -> (Hkv, nseg, d)."""
+    q = np.asarray(q, dtype=np.float64)
+    hq, L, d = q.shape
+    G = hq // hkv
+    nseg = n_blocks(L, segment)
+    rep_q = np.empty((hkv, nseg, d))
+    for g in range(hkv):
+        for sg in range(nseg):
+            rep_q[g, sg] = q[g * G:(g + 1) * G, sg * segment:min((sg + 1) * segment, L)].mean(axis=(0, 1))
+    return rep_q
+
+
+def history_map(q, k, segment, sm_scale):
+    """[S2O] §1: for KV head g and segment s >= 1, the prefix positions
+    t < s*S sorted by sm_scale * <representative query of s, k_t> descending,
+    ties by position ascending.
+
+    Returns hmap (Hkv, nseg, L) int64 (entries t >= s*S are -1) and the
+    scores (Hkv, nseg, L) (NaN outside the prefix)."""
+    k = np.asarray(k, dtype=np.float64)
+    hkv, L, _ = k.shape
+    rep_q = representative_queries(q, hkv, segment)
+    nseg = rep_q.shape[1]
+    hmap = np.full((hkv, nseg, L), -1, dtype=np.int64)
+    score = np.full((hkv, nseg, L), np.nan)
+    for g in range(hkv):
+        for sg in range(1, nseg):
+            n = sg * segment
+            c = sm_scale * (k[g, :n] @ rep_q[g, sg])
+            ts = np.arange(n)
+            hmap[g, sg, :n] = ts[np.lexsort((ts, -c))]
+            score[g, sg, :n] = c
+    return hmap, score
 
 
 # ----------------------------------------------------------------- pipelines
