@@ -363,6 +363,74 @@ def bench_early_stop(args, torch, B, I):
     )
 
 
+def bench_history_map(args, torch, B, I):
+    """Early-stopped prefill on representative-query history maps on the
+    heavy-hitter workload: maps of every segment, then the attention walking
+    them, captured as one HIP graph."""
+    cfg = I.C3
+    dev = torch.device("cuda:0")
+    q, k, v = I.prefill_inputs(cfg)
+    dq = torch.from_numpy(q).to(torch.bfloat16).to(dev)
+    dk = torch.from_numpy(k).to(torch.bfloat16).to(dev)
+    dv = torch.from_numpy(v).to(torch.bfloat16).to(dev)
+    del q, k, v
+    tau = args.es_tau
+    desc = B.prefill_desc(dq, dk, cfg.block, 1.0, segment=cfg.segment)
+    bufs = B.alloc_prefill_early_stop(desc, dev)
+    nseg = -(-cfg.L // cfg.segment)
+    hmap = torch.empty(dk.shape[0], dk.shape[1], nseg, cfg.L, dtype=torch.int32, device=dev)
+    ws = torch.empty(B.spot_workspace_size(desc, B.SPOT_OP_HISTORY_MAP), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        B.spot_history_map(desc, dq, dk, hmap, ws)
+        if ev is not None:
+            ev[1].record()
+        B.spot_sparse_attn_prefill_history_map(desc, tau, dq, dk, dv, hmap, bufs.o, bufs.lse, bufs.nused)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    ms_map = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    nused = bufs.nused.cpu().numpy()[0].astype(np.int64)
+    r = np.arange(cfg.L)
+    own = r - (r // cfg.segment) * cfg.segment + 1
+    flops = 4.0 * cfg.d * float((own[None, :] + nused * cfg.block).sum())
+    dense_pairs = cfg.hq * cfg.L * (cfg.L + 1) / 2
+    achieved = flops / (ms_attn * 1e-3) / 1e12
+    return dict(
+        workload=cfg.name, tau=tau, value=round(flops / (ms_step * 1e-3) / 1e12, 2), unit="TFLOP/s",
+        ms_per_step=round(ms_step, 4), ms_history_map=round(ms_map, 4), ms_attention=round(ms_attn, 4),
+        taken_fraction=round(flops / (4.0 * cfg.d) / dense_pairs, 4), mean_history_runs=round(float(nused.mean()), 2),
+        flop_per_step=flops,
+        roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                  "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                  "kernel": "prefill_mfma_kernel<128,8,1,true,true> (early stop, history maps)",
+                  "avg_launch_ms": round(ms_attn, 4)},
+    )
+
+
 # ----------------------------------------------------------------- measured ceilings
 def measured_ceilings(torch):
     """Context for the rooflines: a dense bf16 GEMM (8192^3, the vendor BLAS
@@ -474,10 +542,12 @@ def main():
         print(f"[bench] taylor: {tay}", file=sys.stderr, flush=True)
     ceil = measured_ceilings(torch)
     print(f"[bench] measured ceilings: {ceil}", file=sys.stderr, flush=True)
-    es = None
+    es = es_map = None
     if not args.no_early_stop:
         es = bench_early_stop(args, torch, B, I)
         print(f"[bench] early stop: {es}", file=sys.stderr, flush=True)
+        es_map = bench_history_map(args, torch, B, I)
+        print(f"[bench] early stop on history maps: {es_map}", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(pre, I, args.cpu_sample_blocks)
@@ -501,6 +571,7 @@ def main():
         "decode_mxfp4_indexer": dec_mx,
         "taylor_score": tay,
         "early_stop": es,
+        "early_stop_history_map": es_map,
     }
     print(json.dumps(line))
 

@@ -19,13 +19,13 @@ SPOT_OK, SPOT_ERR_INVALID, SPOT_ERR_UNSUPPORTED, SPOT_ERR_WORKSPACE, SPOT_ERR_LA
 SPOT_F32, SPOT_BF16 = 0, 1
 SPOT_SCORE_MEANPOOL, SPOT_SCORE_RELU_INDEXER, SPOT_SCORE_TAYLOR = 0, 1, 2
 SPOT_OP_BLOCK_SCORE, SPOT_OP_SELECT_TOPP, SPOT_OP_PREFILL, SPOT_OP_DECODE, SPOT_OP_KEY_PERMUTATION = 0, 1, 2, 3, 4
-SPOT_OP_ORDER_HISTORY, SPOT_OP_PREFILL_EARLY_STOP = 5, 6
+SPOT_OP_ORDER_HISTORY, SPOT_OP_PREFILL_EARLY_STOP, SPOT_OP_HISTORY_MAP = 5, 6, 7
 ABI_VERSION = 1
 
 EXPORTS = ("spot_version", "spot_status_string", "spot_last_error", "spot_workspace_size", "spot_block_score",
            "spot_select_topp", "spot_sparse_attn_prefill", "spot_sparse_attn_decode", "spot_key_permutation",
            "spot_order_history", "spot_sparse_attn_prefill_early_stop", "spot_quantize_indexer_keys",
-           "spot_indexer_score_mxfp4")
+           "spot_indexer_score_mxfp4", "spot_history_map", "spot_sparse_attn_prefill_history_map")
 
 
 class spot_desc(ctypes.Structure):
@@ -72,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spot_order_history.argtypes = [D, P, P, P, P, S, P]
     lib.spot_quantize_indexer_keys.argtypes = [D, P, P, P, P]
     lib.spot_indexer_score_mxfp4.argtypes = [D, P, P, P, P, P, P]
+    lib.spot_history_map.argtypes = [D, P, P, P, P, S, P]
+    lib.spot_sparse_attn_prefill_history_map.argtypes = [D, ctypes.c_float, P, P, P, P, P, P, P, P, S, P]
     lib.spot_sparse_attn_prefill_early_stop.argtypes = [D, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, S, P]
     for name in EXPORTS[3:]:
         getattr(lib, name).restype = I
@@ -155,6 +157,22 @@ def spot_indexer_score_mxfp4(desc, idx_q, idx_w, k_codes, k_scales, scores, stre
     st = load_library().spot_indexer_score_mxfp4(ctypes.byref(desc), _ptr(idx_q), _ptr(idx_w), _ptr(k_codes),
                                                  _ptr(k_scales), _ptr(scores), _stream() if stream is None else stream)
     _check("spot_indexer_score_mxfp4", st)
+
+
+def spot_history_map(desc, q, k, hmap, workspace=None, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load_library().spot_history_map(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(hmap), _ptr(workspace), ws_bytes,
+                                         _stream() if stream is None else stream)
+    _check("spot_history_map", st)
+
+
+def spot_sparse_attn_prefill_history_map(desc, tau, q, k, v, hmap, o, lse=None, nused=None, workspace=None,
+                                         stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load_library().spot_sparse_attn_prefill_history_map(
+        ctypes.byref(desc), float(tau), _ptr(q), _ptr(k), _ptr(v), _ptr(hmap), _ptr(o), _ptr(lse), _ptr(nused),
+        _ptr(workspace), ws_bytes, _stream() if stream is None else stream)
+    _check("spot_sparse_attn_prefill_history_map", st)
 
 
 def spot_order_history(desc, scores, order, cnt, workspace=None, stream=None):
@@ -318,6 +336,40 @@ def prefill_early_stop(q, k, v, block: int, segment: int, tau: float, *, perm=No
     spot_block_score(desc, q, k, perm, None, None, None, bufs.scores, bufs.workspace)
     spot_order_history(desc, bufs.scores, bufs.order, bufs.cnt)
     spot_sparse_attn_prefill_early_stop(desc, tau, q, k, v, perm, bufs.order, bufs.cnt, bufs.o, bufs.lse, bufs.nused)
+    return bufs
+
+
+def history_map(q, k, segment: int, *, sm_scale: float = 0.0, workspace=None):
+    """Per-segment history maps by the segment's mean query.
+
+    q (batch, hq, L, d), k (batch, hkv, L, d) bf16 device tensors.  Returns
+    hmap (batch, hkv, nseg, L) int32."""
+    _require(q, "q", dtype=torch.bfloat16)
+    _require(k, "k", dtype=torch.bfloat16)
+    desc = prefill_desc(q, k, segment, 1.0, segment=segment, sm_scale=sm_scale)
+    desc.block = 16   # the map does not depend on the block size
+    nseg = -(-q.shape[2] // segment)
+    hmap = torch.empty(k.shape[0], k.shape[1], nseg, k.shape[2], dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(spot_workspace_size(desc, SPOT_OP_HISTORY_MAP), 1), dtype=torch.uint8,
+                                device=q.device)
+    spot_history_map(desc, q, k, hmap, workspace)
+    return hmap
+
+
+def prefill_history_map(q, k, v, block: int, segment: int, tau: float, *, hmap=None, sm_scale: float = 0.0,
+                        bufs: EarlyStopBuffers | None = None) -> EarlyStopBuffers:
+    """Early-stopped prefill on per-segment history maps (computed here when
+    `hmap` is None).  Returns buffers with o, lse and nused (scores, order and
+    cnt are not used)."""
+    desc = prefill_desc(q, k, block, 1.0, segment=segment, sm_scale=sm_scale)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, dtype=torch.bfloat16)
+    if hmap is None:
+        hmap = history_map(q, k, segment, sm_scale=sm_scale)
+    if bufs is None:
+        bufs = alloc_prefill_early_stop(desc, q.device)
+    spot_sparse_attn_prefill_history_map(desc, tau, q, k, v, hmap, bufs.o, bufs.lse, bufs.nused)
     return bufs
 
 

@@ -159,11 +159,13 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
   int nkept, own_tiles = 0;
   const int* lst;
   if constexpr (ES) {
-    // own segment's blocks ascending, then the history blocks in visiting order
+    // own segment's blocks ascending, then the history blocks in visiting
+    // order (with history maps: the runs of the map in order, all of them)
     const int sblk = seg_start >> lgB;
     const int n_own = i - sblk + 1;
-    nkept = n_own + min(max(a.cnt[row_id], 0), sblk);   // at most the blocks before the segment
-    for (int k = tid; k < nkept; k += NT) s_list[k] = k < n_own ? sblk + k : glist[k - n_own];
+    nkept = n_own + (a.es_hmap ? sblk : min(max(a.cnt[row_id], 0), sblk));   // at most the blocks before the segment
+    for (int k = tid; k < nkept; k += NT)
+      s_list[k] = k < n_own ? sblk + k : (a.es_hmap ? k - n_own : glist[k - n_own]);
     lst = s_list;
     own_tiles = (n_own * B) / kKT;
   } else {
@@ -172,7 +174,9 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
       for (int k = tid; k < min(nkept, kListCap); k += NT) s_list[k] = glist[k];
     lst = (kListCap > 0 && nkept <= kListCap) ? s_list : glist;
   }
-  const int32_t* permg = PERM ? a.perm + size_t(pair) * L : nullptr;
+  const int32_t* permg =
+      PERM ? a.perm + (ES && a.es_hmap ? size_t(pair) * a.nseg + seg_start / max(a.segment, 1) : size_t(pair)) * L
+           : nullptr;
   const int ntiles = (nkept * B + kKT - 1) / kKT;
   // tiles before the last kept block need no mask (history and earlier own-segment blocks are visible)
   const int nfull = min(ntiles, ((nkept - 1) * B) / kKT);

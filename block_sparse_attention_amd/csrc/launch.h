@@ -80,9 +80,28 @@ struct PrefillArgs {
   int es;
   float tau;
   int32_t* nused;       // [batch, hq, L] history blocks taken per row, nullable
+  // early stopping on per-segment history maps: perm points at maps
+  // [batch, hkv, nseg, L] and the history is visited in map order
+  int es_hmap;
+  int nseg;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 constexpr int kEsMaxBlocks = 2048;     // blocks per sequence for early stopping (visiting list staged in LDS)
+
+struct HistMapArgs {
+  const uint16_t* q;   // [batch, hq, L, d] bf16
+  const uint16_t* k;   // [batch, hkv, L, d] bf16
+  int32_t* hmap;       // [batch, hkv, nseg, L]
+  float* qrep;         // workspace: [batch, hkv, nseg, d] representative queries
+  uint64_t* keys;      // workspace: [batch, hkv, nseg, kcap] sort keys
+  int batch, hq, hkv, d, L, segment, nseg, kcap;
+  float sm_scale;
+};
+hipError_t launch_history_map(const HistMapArgs& a, hipStream_t s);
+int hist_key_cap(int nseg, int segment);
+size_t hist_workspace_bytes(int batch, int hkv, int nseg, int segment, int d);
+constexpr int kHistMaxPrefix = 32768;   // history positions per segment map
+constexpr int kHistMaxSegments = 64;    // representative queries held in LDS by the key pass
 
 struct OrderArgs {
   const float* scores;  // [rows, nb]

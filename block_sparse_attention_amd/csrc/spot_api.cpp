@@ -143,6 +143,13 @@ int spot_workspace_size(const spot_desc* desc, int op, size_t* bytes) {
     case SPOT_OP_ORDER_HISTORY:
     case SPOT_OP_PREFILL_EARLY_STOP:
       break;
+    case SPOT_OP_HISTORY_MAP: {
+      if ((st = check_prefill_shape(desc))) return st;
+      if (desc->segment <= 0) return fail(SPOT_ERR_INVALID, "segment must be > 0");
+      const int nseg = int(ceil_div64(desc->q_len, desc->segment));
+      *bytes = spot::hist_workspace_bytes(desc->batch, desc->hkv, nseg, desc->segment, desc->d);
+      break;
+    }
     case SPOT_OP_KEY_PERMUTATION: {
       if ((st = check_prefill_shape(desc))) return st;
       const int nb = int(ceil_div64(desc->q_len, desc->block));
@@ -289,6 +296,69 @@ int spot_indexer_score_mxfp4(const spot_desc* desc, const void* idx_q, const flo
   spot::IndexerFp4Args a{static_cast<const uint16_t*>(idx_q), idx_w, k_codes, k_scales, scores, desc->batch,
                          int(ceil_div64(desc->kv_len, desc->block)), desc->h_idx, desc->d_idx};
   return launched(spot::launch_indexer_score_mxfp4(a, static_cast<hipStream_t>(stream)), "indexer_score_mxfp4");
+}
+
+int spot_history_map(const spot_desc* desc, const void* q, const void* k, int32_t* hmap, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_common(desc);
+  if (st) return st;
+  if ((st = check_prefill_shape(desc))) return st;
+  if (!q || !k || !hmap) return fail(SPOT_ERR_INVALID, "q, k and hmap are required");
+  if (desc->dtype != SPOT_BF16) return fail(SPOT_ERR_UNSUPPORTED, "history maps support bf16 only");
+  if (desc->segment <= 0) return fail(SPOT_ERR_INVALID, "segment must be > 0");
+  const int L = int(desc->q_len);
+  const int nseg = int(ceil_div64(L, desc->segment));
+  if (nseg > spot::kHistMaxSegments)
+    return fail(SPOT_ERR_UNSUPPORTED, "%d segments (max %d)", nseg, spot::kHistMaxSegments);
+  if (int64_t(nseg - 1) * desc->segment > spot::kHistMaxPrefix)
+    return fail(SPOT_ERR_UNSUPPORTED, "history of %lld positions (max %d)", (long long)(nseg - 1) * desc->segment,
+                spot::kHistMaxPrefix);
+  const size_t need = spot::hist_workspace_bytes(desc->batch, desc->hkv, nseg, desc->segment, desc->d);
+  if ((st = check_workspace(need, workspace, workspace_bytes))) return st;
+  const size_t qrep_bytes = size_t(desc->batch) * desc->hkv * nseg * desc->d * sizeof(float);
+  spot::HistMapArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.hmap = hmap;
+  a.qrep = static_cast<float*>(workspace);
+  a.keys = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + ((qrep_bytes + 255) / 256) * 256);
+  a.batch = desc->batch;
+  a.hq = desc->hq;
+  a.hkv = desc->hkv;
+  a.d = desc->d;
+  a.L = L;
+  a.segment = desc->segment;
+  a.nseg = nseg;
+  a.kcap = spot::hist_key_cap(nseg, desc->segment);
+  a.sm_scale = effective_scale(desc);
+  return launched(spot::launch_history_map(a, static_cast<hipStream_t>(stream)), "history_map");
+}
+
+int spot_sparse_attn_prefill_history_map(const spot_desc* desc, float tau, const void* q, const void* k,
+                                         const void* v, const int32_t* hmap, void* o, float* lse, int32_t* nused,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int st = check_common(desc);
+  if (st) return st;
+  if ((st = check_prefill_shape(desc))) return st;
+  if (!q || !k || !v || !hmap || !o) return fail(SPOT_ERR_INVALID, "q, k, v, hmap and o are required");
+  if (!std::isfinite(tau) || tau < 0.f) return fail(SPOT_ERR_INVALID, "tau must be finite and >= 0");
+  if (desc->segment <= 0) return fail(SPOT_ERR_INVALID, "segment must be > 0");
+  if (desc->dtype != SPOT_BF16) return fail(SPOT_ERR_UNSUPPORTED, "early stopping supports bf16 only");
+  if (desc->block != 64 && desc->block != 128)
+    return fail(SPOT_ERR_UNSUPPORTED, "early stopping needs block 64 or 128 (got %d)", desc->block);
+  const int nb = int(ceil_div64(desc->q_len, desc->block));
+  if (nb > spot::kEsMaxBlocks)
+    return fail(SPOT_ERR_UNSUPPORTED, "%d blocks per sequence (max %d for early stopping)", nb, spot::kEsMaxBlocks);
+  spot::PrefillArgs a{q, k, v, hmap, nullptr, nullptr, o, lse, 1, desc->batch, desc->hq, desc->hkv,
+                      desc->d, int(desc->q_len), desc->block, desc->segment, nb, effective_scale(desc)};
+  a.es = 1;
+  a.tau = tau;
+  a.nused = nused;
+  a.es_hmap = 1;
+  a.nseg = int(ceil_div64(desc->q_len, desc->segment));
+  return launched(spot::launch_prefill(a, static_cast<hipStream_t>(stream)), "sparse_attn_prefill_history_map");
 }
 
 int spot_order_history(const spot_desc* desc, const float* scores, int32_t* order, int32_t* cnt, void* workspace,

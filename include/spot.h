@@ -20,6 +20,8 @@
  *
  *   spot_order_history                  visiting order of each query block's history blocks
  *   spot_sparse_attn_prefill_early_stop attention that stops taking history blocks per row
+ *   spot_history_map                    per-segment maps of the history by a representative query
+ *   spot_sparse_attn_prefill_history_map the early-stopped attention walking those maps
  *
  * Conventions shared by every call
  * --------------------------------
@@ -90,7 +92,8 @@ enum spot_op {
   SPOT_OP_DECODE = 3,
   SPOT_OP_KEY_PERMUTATION = 4,
   SPOT_OP_ORDER_HISTORY = 5,
-  SPOT_OP_PREFILL_EARLY_STOP = 6
+  SPOT_OP_PREFILL_EARLY_STOP = 6,
+  SPOT_OP_HISTORY_MAP = 7
 };
 
 /* Problem descriptor.  `version` must be SPOT_ABI_VERSION. */
@@ -273,6 +276,39 @@ int spot_sparse_attn_prefill_early_stop(const spot_desc* desc, float tau, const 
                                         const void* v, const int32_t* perm, const int32_t* order,
                                         const int32_t* cnt, void* o, float* lse, int32_t* nused,
                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * History maps by a representative query ([S2O] §1 historical KV
+ * permutation: the historical keys are scored against a representative
+ * query of the segment, prefix tokens only, and the sorted indices form a
+ * logical map).  For KV head g and segment s >= 1 (segments of S positions,
+ * the last one possibly partial):
+ *   qrep = mean of Q over the G query heads of the group and the rows of s;
+ *   hmap[b,g,s,j], j < s*S = the positions t < s*S sorted by
+ *     sm_scale * < qrep, k_t > descending, ties by t ascending;
+ *   hmap[b,g,s,j] = -1 for j >= s*S, and all of segment 0.
+ * q: [batch, hq, L, d] bf16; k: [batch, hkv, L, d] bf16; hmap: int32
+ * [batch, hkv, nseg, L] (output), nseg = ceil(L / S).  Requires segment > 0,
+ * nseg <= 64 and (nseg - 1) * S <= 32768.  Workspace:
+ * spot_workspace_size(SPOT_OP_HISTORY_MAP).  Scores are fp32, so keys whose
+ * scores agree to fp32 rounding may be ordered differently from an exact
+ * evaluation.
+ */
+int spot_history_map(const spot_desc* desc, const void* q, const void* k, int32_t* hmap, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * Early-stopped prefill on history maps ([S2O] §1-3): as
+ * spot_sparse_attn_prefill_early_stop, with pass 2 visiting, for a query in
+ * segment s, the history blocks hmap[b,g,s, jB .. (j+1)B) for j = 0, 1, ...
+ * (all visible) instead of ordered key blocks; the same per-row stopping
+ * rule with threshold tau; nused counts the runs taken.  Same requirements
+ * as spot_sparse_attn_prefill_early_stop plus segment > 0 (a multiple of
+ * block).  No workspace.
+ */
+int spot_sparse_attn_prefill_history_map(const spot_desc* desc, float tau, const void* q, const void* k,
+                                         const void* v, const int32_t* hmap, void* o, float* lse, int32_t* nused,
+                                         void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

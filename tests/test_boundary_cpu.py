@@ -228,3 +228,27 @@ def test_mxfp4_indexer_validation():
     assert q(_decode(), x=None) == B.SPOT_ERR_INVALID
     assert sc(_decode(), s=None) == B.SPOT_ERR_INVALID
     assert sc(_decode(), out=None) == B.SPOT_ERR_INVALID
+
+
+def test_history_map_validation():
+    lib = B.load_library()
+
+    def hm(d, q=FAKE, k=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        return lib.spot_history_map(ctypes.byref(d), q, k, out, ws, ws_bytes, None)
+
+    def att(d, tau=0.01, hmap=FAKE, o=FAKE):
+        return lib.spot_sparse_attn_prefill_history_map(ctypes.byref(d), tau, FAKE, FAKE, FAKE, hmap, o, None, None,
+                                                         None, 0, None)
+
+    assert hm(_prefill(segment=0)) == B.SPOT_ERR_INVALID
+    assert hm(_prefill(segment=256, dtype=B.SPOT_F32)) == B.SPOT_ERR_UNSUPPORTED
+    assert hm(_prefill(segment=256), out=None) == B.SPOT_ERR_INVALID
+    assert hm(_prefill(segment=256), ws=None) == B.SPOT_ERR_WORKSPACE
+    assert hm(_prefill(segment=256), ws_bytes=16) == B.SPOT_ERR_WORKSPACE
+    assert hm(_prefill(segment=64, q_len=64 * 65, kv_len=64 * 65)) == B.SPOT_ERR_UNSUPPORTED        # 65 segments
+    assert hm(_prefill(segment=8192, q_len=8192 * 6, kv_len=8192 * 6)) == B.SPOT_ERR_UNSUPPORTED    # prefix 40960
+    assert B.spot_workspace_size(_prefill(segment=256), B.SPOT_OP_HISTORY_MAP) > 0
+    assert att(_prefill(segment=0)) == B.SPOT_ERR_INVALID
+    assert att(_prefill(segment=256), hmap=None) == B.SPOT_ERR_INVALID
+    assert att(_prefill(segment=256), tau=-1.0) == B.SPOT_ERR_INVALID
+    assert att(_prefill(segment=256, block=16)) == B.SPOT_ERR_UNSUPPORTED

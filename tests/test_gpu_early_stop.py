@@ -29,10 +29,11 @@ def order_nested(order_np, cnt_np, b, hkv, blocks):
     return out
 
 
-def es_check(cfg, host, order_np, cnt_np, bufs, tau, perm=None, pairs=None):
+def es_check(cfg, host, order_np, cnt_np, bufs, tau, perm=None, pairs=None, hmap=None):
     """Stop points and outputs of an early-stopped GPU prefill against the oracle.
 
-    pairs: (b, g, i) query blocks to check (default: all)."""
+    pairs: (b, g, i) query blocks to check (default: all); hmap (batch, hkv,
+    nseg, L): the history maps the GPU walked (order_np and cnt_np unused)."""
     q, k, v = host
     scale = 1.0 / math.sqrt(cfg.d)
     G = cfg.hq // cfg.hkv
@@ -46,13 +47,17 @@ def es_check(cfg, host, order_np, cnt_np, bufs, tau, perm=None, pairs=None):
     taken = 0
     for b, g, i in pairs:
         n_hist = ((i * cfg.block) // cfg.segment) * cfg.segment // cfg.block
-        assert cnt_np[b, g, i] == n_hist
-        hist = order_np[b, g, i, :n_hist].astype(np.int64)
-        assert np.all(order_np[b, g, i, n_hist:] == -1)
+        if hmap is None:
+            assert cnt_np[b, g, i] == n_hist
+            hist = order_np[b, g, i, :n_hist].astype(np.int64)
+            assert np.all(order_np[b, g, i, n_hist:] == -1)
+        else:
+            hist = None
+        hm = None if hmap is None else hmap[b].astype(np.int64)
         pb = None if perm is None else perm[b]
         rows = oracle.block_rows(i, cfg.block, cfg.L)
         for h in range(g * G, (g + 1) * G):
-            ratio = oracle.es_gain_ratios(q[b], k[b], i, g, h, hist, cfg.block, cfg.segment, scale, pb)
+            ratio = oracle.es_gain_ratios(q[b], k[b], i, g, h, hist, cfg.block, cfg.segment, scale, pb, hm)
             for ri, r in enumerate(rows):
                 n = int(gn[b, h, r])
                 rows_total += 1
@@ -71,8 +76,9 @@ def es_check(cfg, host, order_np, cnt_np, bufs, tau, perm=None, pairs=None):
         ords = [dict() for _ in range(cfg.hkv)]
         ords[g][i] = hist
         o_ref, lse_ref, used_ref = oracle.attend_prefill_es(
-            q[b, g * G:(g + 1) * G], k[b, g:g + 1], v[b, g:g + 1], [ords[g]], cfg.block, cfg.segment, scale, tau,
-            perm=None if pb is None else pb[g:g + 1], qblocks=[i], nused=gn[b, g * G:(g + 1) * G])
+            q[b, g * G:(g + 1) * G], k[b, g:g + 1], v[b, g:g + 1], None if hm is not None else [ords[g]],
+            cfg.block, cfg.segment, scale, tau, perm=None if pb is None else pb[g:g + 1], qblocks=[i],
+            nused=gn[b, g * G:(g + 1) * G], hmap=None if hm is None else hm[g:g + 1])
         rs = slice(rows[0], rows[-1] + 1)
         worst = max(worst, P.max_abs(go[b, g * G:(g + 1) * G, rs], o_ref[:, rs]))
         worst_lse = max(worst_lse, P.max_abs(glse[b, g * G:(g + 1) * G, rs], lse_ref[:, rs]))
