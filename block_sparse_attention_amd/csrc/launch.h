@@ -93,6 +93,7 @@ struct HistMapArgs {
   const uint16_t* k;   // [batch, hkv, L, d] bf16
   int32_t* hmap;       // [batch, hkv, nseg, L]
   float* qrep;         // workspace: [batch, hkv, nseg, d] representative queries
+  float* qpart;        // workspace: partial sums of the segment means
   uint64_t* keys;      // workspace: [batch, hkv, nseg, kcap] sort keys
   int batch, hq, hkv, d, L, segment, nseg, kcap;
   float sm_scale;
@@ -100,6 +101,8 @@ struct HistMapArgs {
 hipError_t launch_history_map(const HistMapArgs& a, hipStream_t s);
 int hist_key_cap(int nseg, int segment);
 size_t hist_workspace_bytes(int batch, int hkv, int nseg, int segment, int d);
+void hist_workspace_split(void* ws, int batch, int hkv, int nseg, int segment, int d, float*& qrep, float*& qpart,
+                          uint64_t*& keys);
 constexpr int kHistMaxPrefix = 32768;   // history positions per segment map
 constexpr int kHistMaxSegments = 64;    // representative queries held in LDS by the key pass
 

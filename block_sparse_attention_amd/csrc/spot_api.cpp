@@ -315,13 +315,12 @@ int spot_history_map(const spot_desc* desc, const void* q, const void* k, int32_
                 spot::kHistMaxPrefix);
   const size_t need = spot::hist_workspace_bytes(desc->batch, desc->hkv, nseg, desc->segment, desc->d);
   if ((st = check_workspace(need, workspace, workspace_bytes))) return st;
-  const size_t qrep_bytes = size_t(desc->batch) * desc->hkv * nseg * desc->d * sizeof(float);
   spot::HistMapArgs a{};
+  spot::hist_workspace_split(workspace, desc->batch, desc->hkv, nseg, desc->segment, desc->d, a.qrep, a.qpart,
+                             a.keys);
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.hmap = hmap;
-  a.qrep = static_cast<float*>(workspace);
-  a.keys = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + ((qrep_bytes + 255) / 256) * 256);
   a.batch = desc->batch;
   a.hq = desc->hq;
   a.hkv = desc->hkv;
