@@ -565,7 +565,9 @@ def main():
                    "ms_per_step_eager_launches": round(pre["ms_step_eager"], 4), "step_launch": "hip_graph_replay",
                    "segment": cfg.segment, "ms_key_permutation": round(pre["ms_perm"], 4),
                    "flop_per_step": pre["flops"]},
-        "roofline": dict(pre["roofline"], measured_ceilings=ceil),
+        "roofline": dict(pre["roofline"], measured_ceilings=ceil,
+                         frac_of_measured_gemm=round(pre["roofline"]["achieved"] / ceil["bf16_gemm_8192_tflops"], 4)
+                         if pre["roofline"]["peak"] else None),
         "cpu_baseline": cpu,
         "decode": dec,
         "decode_mxfp4_indexer": dec_mx,
