@@ -88,8 +88,10 @@ def load_traffic(kernel_file: str, key: str):
 
 
 # ----------------------------------------------------------------- prefill
-def bench_prefill(args, torch, B, I, score_kind=None):
+def bench_prefill(args, torch, B, I, score_kind=None, top_p=None):
     cfg = {c.name: c for c in (I.C1, I.C2, I.C3, I.C5)}[args.workload]
+    if top_p is not None:
+        cfg = cfg.with_(top_p=top_p)
     score_kind = B.SPOT_SCORE_MEANPOOL if score_kind is None else score_kind
     dev = torch.device("cuda:0")
     q, k, v = I.prefill_inputs(cfg)
@@ -502,8 +504,16 @@ def cpu_baseline(res, I, sample_blocks: int):
     pairs = prefill_visible_pairs(idx, None, cfg.L, cfg.block, G)
     flops = 4.0 * cfg.d * float(pairs[sel].sum())
     what = "every query block" if len(blocks) == nb else f"{len(blocks)} seeded query blocks"
+    cpu_model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu_model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 2),
+            "seconds": round(dt, 2), "cpu_model": cpu_model, "blas_threads": int(threads),
             "sample": f"float64 NumPy oracle, whole pipeline ({'permutation, ' if cfg.segment else ''}pool and "
                       f"score every block, select and attend {what} x {cfg.hkv} KV heads of {cfg.name})"}
 
@@ -531,6 +541,15 @@ def main():
         print(f"[bench] decode: {dec}", file=sys.stderr, flush=True)
         dec_mx = bench_decode(args, torch, B, I, mxfp4=True)
         print(f"[bench] decode mxfp4: {dec_mx}", file=sys.stderr, flush=True)
+    # the same kernels keeping every block (p = 1): an in-house dense reference
+    dense = bench_prefill(args, torch, B, I, top_p=1.0)
+    dense_ref = {"workload": dense["cfg"].name, "top_p": 1.0, "ms_per_step": round(dense["ms_step"], 4),
+                 "ms_attention": round(dense["ms_attn"], 4), "value": round(dense["value"], 2), "unit": "TFLOP/s",
+                 "kept_fraction": round(dense["kept_fraction"], 4),
+                 "sparse_speedup_step": round(dense["ms_step"] / pre["ms_step"], 3),
+                 "sparse_speedup_attention": round(dense["ms_attn"] / pre["ms_attn"], 3)}
+    del dense
+    print(f"[bench] dense reference: {dense_ref}", file=sys.stderr, flush=True)
     tay = None
     if not args.no_taylor:
         t = bench_prefill(args, torch, B, I, score_kind=B.SPOT_SCORE_TAYLOR)
@@ -569,6 +588,7 @@ def main():
                          frac_of_measured_gemm=round(pre["roofline"]["achieved"] / ceil["bf16_gemm_8192_tflops"], 4)
                          if pre["roofline"]["peak"] else None),
         "cpu_baseline": cpu,
+        "dense_reference": dense_ref,
         "decode": dec,
         "decode_mxfp4_indexer": dec_mx,
         "taylor_score": tay,
