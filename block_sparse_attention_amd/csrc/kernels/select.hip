@@ -3,9 +3,11 @@
 // residual distribution until the cumulative mass reaches p, floor K_min.
 //
 // One workgroup per row; each thread owns a contiguous run of candidate ids.
-// The residual candidates that can be kept are sorted exactly in LDS (bitonic
-// network on 64-bit keys: inverted order-preserving score bits above the id
-// rank, so ascending keys are score-descending with ties to the lower id),
+// The residual candidates that can be kept are ordered exactly in LDS on
+// 64-bit keys (inverted order-preserving score bits above the id rank, so
+// ascending keys are score-descending with ties to the lower id): small sets
+// by counting each key's rank against all the others, larger ones by a
+// bitonic network;
 // their masses are prefix-summed in fp64 in that order and the first prefix
 // reaching p ends the kept set.  On rows longer than the sort buffer only the
 // candidates above a mass bound enter the sort: if the mass first reaches p
@@ -28,6 +30,9 @@ constexpr int kSelMaxPerThread = 16;   // candidates per thread (16384 / 1024)
 constexpr int kSelTargetPerThread = SPOT_SELECT_PER_THREAD;   // launch as few threads as keep at most this many per thread
 static_assert(kSelTargetPerThread <= kSelMaxPerThread, "per-thread runs are register arrays");
 constexpr int kSortMax = 2048;         // candidates sorted exactly in LDS
+constexpr int kRankReads = 512;        // rank by counting while each thread compares at most this many keys
+constexpr int kRankMax = 512;          // ... which bounds the set to 512 candidates (nthr <= 1024)
+constexpr int kRankRounds = 3;         // and gives each thread at most 3 of them (nthr >= 64)
 constexpr int kRefineMin = 128;        // long rows: above this many candidates, narrow them by a score histogram
 constexpr int kHistBins = 64;          // histogram bins of width 1/kHistScale in score units below the row max
 constexpr float kHistScale = 4.0f;
@@ -40,135 +45,221 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// ---- wave64 reductions and scans on DPP row operations (rows of 16 lanes)
+// plus v_readlane across the four rows; no LDS crossbar round trips.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowRor8 = 0x128, kDppRowRor4 = 0x124, kDppQuad2301 = 0x4E, kDppQuad1032 = 0xB1;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int x) {   // lanes without a source in their row read 0
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, dpp_i32<CTRL>(__builtin_bit_cast(int, x)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = uint32_t(dpp_i32<CTRL>(int(uint32_t(u)))), hi = uint32_t(dpp_i32<CTRL>(int(uint32_t(u >> 32))));
+  return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u)), l));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u >> 32)), l));
+  return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+__device__ __forceinline__ float readlane_f32(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// totals over the wave (same value in every lane); rows first, then the four row totals in order
+__device__ __forceinline__ double wave_total_f64(double x) {
+  x += dpp_f64<kDppRowRor8>(x);
+  x += dpp_f64<kDppRowRor4>(x);
+  x += dpp_f64<kDppQuad2301>(x);
+  x += dpp_f64<kDppQuad1032>(x);
+  return (readlane_f64(x, 0) + readlane_f64(x, 16)) + (readlane_f64(x, 32) + readlane_f64(x, 48));
+}
+__device__ __forceinline__ int wave_total_i32(int x) {
+  x += dpp_i32<kDppRowRor8>(x);
+  x += dpp_i32<kDppRowRor4>(x);
+  x += dpp_i32<kDppQuad2301>(x);
+  x += dpp_i32<kDppQuad1032>(x);
+  return (__builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16)) +
+         (__builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48));
+}
+__device__ __forceinline__ float wave_max_f32(float x) {
+  x = fmaxf(x, dpp_f32<kDppRowRor8>(x));
+  x = fmaxf(x, dpp_f32<kDppRowRor4>(x));
+  x = fmaxf(x, dpp_f32<kDppQuad2301>(x));
+  x = fmaxf(x, dpp_f32<kDppQuad1032>(x));
+  return fmaxf(fmaxf(readlane_f32(x, 0), readlane_f32(x, 16)), fmaxf(readlane_f32(x, 32), readlane_f32(x, 48)));
+}
+// inclusive prefix over the lanes: Hillis-Steele inside each row, then the earlier rows' totals
+__device__ __forceinline__ int wave_incl_scan_i32(int x) {
+  x += dpp_i32<kDppRowShr1>(x);
+  x += dpp_i32<kDppRowShr2>(x);
+  x += dpp_i32<kDppRowShr4>(x);
+  x += dpp_i32<kDppRowShr8>(x);
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+__device__ __forceinline__ double wave_incl_scan_f64(double x) {
+  x += dpp_f64<kDppRowShr1>(x);
+  x += dpp_f64<kDppRowShr2>(x);
+  x += dpp_f64<kDppRowShr4>(x);
+  x += dpp_f64<kDppRowShr8>(x);
+  const double r0 = readlane_f64(x, 15), r1 = readlane_f64(x, 31), r2 = readlane_f64(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  double before = 0.0;
+  if (row >= 1) before = r0;
+  if (row >= 2) before += r1;
+  if (row >= 3) before += r2;
+  return before + x;
+}
+
+// ---- workgroup reductions: one value per wave in LDS, one barrier.  Two
+// scratch slots alternate between successive calls; a slot is rewritten two
+// calls later, after every thread has passed the barrier of the call between.
+constexpr int kSelMaxWaves = 16;
 struct SelScratch {
-  double d[32];
-  int i[32];
-  uint32_t u[32];
-  float f[32];
+  double d[2][kSelMaxWaves];
+  int i[2][kSelMaxWaves];
+  float f[2][kSelMaxWaves];
+};
+struct BlockOps {
+  SelScratch& s;
+  int ph;   // slot of the next call (the same in every thread: calls are workgroup-uniform)
 };
 
-__device__ double block_sum_f64(double x, SelScratch& sc) {
+__device__ double block_sum_f64(double x, BlockOps& b) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  if (lane == 0) sc.d[w] = x;
+  x = wave_total_f64(x);
+  double* slot = b.s.d[b.ph];
+  b.ph ^= 1;
+  if (lane == 0) slot[w] = x;
   __syncthreads();
   double t = 0.0;
-  for (int k = 0; k < nw; ++k) t += sc.d[k];
-  __syncthreads();
+  for (int k = 0; k < nw; ++k) t += slot[k];
   return t;
 }
 
-__device__ int block_sum_i32(int x, SelScratch& sc) {
+__device__ int block_sum_i32(int x, BlockOps& b) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  if (lane == 0) sc.i[w] = x;
+  x = wave_total_i32(x);
+  int* slot = b.s.i[b.ph];
+  b.ph ^= 1;
+  if (lane == 0) slot[w] = x;
   __syncthreads();
   int t = 0;
-  for (int k = 0; k < nw; ++k) t += sc.i[k];
-  __syncthreads();
+  for (int k = 0; k < nw; ++k) t += slot[k];
   return t;
 }
 
-__device__ float block_max_f32(float x, SelScratch& sc) {
+__device__ float block_max_f32(float x, BlockOps& b) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
-  x = wave_max(x);
-  if (lane == 0) sc.f[w] = x;
+  x = wave_max_f32(x);
+  float* slot = b.s.f[b.ph];
+  b.ph ^= 1;
+  if (lane == 0) slot[w] = x;
   __syncthreads();
   float t = -kInf;
-  for (int k = 0; k < nw; ++k) t = fmaxf(t, sc.f[k]);
-  __syncthreads();
+  for (int k = 0; k < nw; ++k) t = fmaxf(t, slot[k]);
   return t;
 }
 
 // exclusive prefix (in thread order) of one int per thread, plus the total
-__device__ int block_excl_scan_i32(int x, SelScratch& sc, int& total) {
+__device__ int block_excl_scan_i32(int x, BlockOps& b, int& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
-  int incl = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) sc.i[w] = incl;
+  const int incl = wave_incl_scan_i32(x);
+  int* slot = b.s.i[b.ph];
+  b.ph ^= 1;
+  if (lane == 63) slot[w] = incl;
   __syncthreads();
   int before = 0, tot = 0;
   for (int k = 0; k < nw; ++k) {
-    if (k < w) before += sc.i[k];
-    tot += sc.i[k];
+    if (k < w) before += slot[k];
+    tot += slot[k];
   }
-  __syncthreads();
   total = tot;
   return before + incl - x;
 }
 
-__device__ double block_excl_scan_f64(double x, SelScratch& sc, double& total) {
+__device__ double block_excl_scan_f64(double x, BlockOps& b, double& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
-  double incl = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) sc.d[w] = incl;
+  const double incl = wave_incl_scan_f64(x);
+  double* slot = b.s.d[b.ph];
+  b.ph ^= 1;
+  if (lane == 63) slot[w] = incl;
   __syncthreads();
   double before = 0.0, tot = 0.0;
   for (int k = 0; k < nw; ++k) {
-    if (k < w) before += sc.d[k];
-    tot += sc.d[k];
+    if (k < w) before += slot[k];
+    tot += slot[k];
   }
-  __syncthreads();
   total = tot;
   return before + (incl - x);
 }
 
 // kept ids ascending (thread runs are contiguous and in order), -1 padding, count
-__device__ void write_row(const SelectArgs& a, int row, uint32_t keepm, int c0, SelScratch& sc) {
+__device__ void write_row(const SelectArgs& a, int row, uint32_t keepm, int c0, BlockOps& sc) {
   int total_kept;
   int pos = block_excl_scan_i32(__popc(keepm), sc, total_kept);
   int32_t* irow = a.idx + size_t(row) * a.nk;
 #pragma unroll
   for (int e = 0; e < kSelMaxPerThread; ++e)
     if (keepm & (1u << e)) irow[pos++] = c0 + e;
-  for (int c = total_kept + threadIdx.x; c < a.nk; c += blockDim.x) irow[c] = -1;
+  // -1 padding: up to three words to a 16-byte boundary, then 16-byte stores
+  const int c1 = min(a.nk, total_kept + int((4u - uint32_t((reinterpret_cast<uintptr_t>(irow + total_kept) >> 2) & 3u)) & 3u));
+  if (int(threadIdx.x) < c1 - total_kept) irow[total_kept + threadIdx.x] = -1;
+  const int n4 = (a.nk - c1) >> 2;
+  int4* irow4 = reinterpret_cast<int4*>(irow + c1);
+  for (int k = threadIdx.x; k < n4; k += blockDim.x) irow4[k] = make_int4(-1, -1, -1, -1);
+  for (int c = c1 + 4 * n4 + threadIdx.x; c < a.nk; c += blockDim.x) irow[c] = -1;
   if (threadIdx.x == 0) a.cnt[row] = total_kept;
 }
 
-// Bitonic sort of the 128 keys s[0..128) ascending by one wave: key i lives in
-// lane i % 64, register i / 64; partners 64 apart meet in one lane, closer
-// ones across lanes through a shuffle.  No workgroup barrier is needed.
-constexpr int kWaveSort = 128;
-__device__ void wave_sort128(uint64_t* s, int lane) {
-  uint64_t x[2] = {s[lane], s[lane + 64]};
+// Rank of each of the n keys k[0..n) = the number of smaller keys (all keys
+// differ in their id word).  Thread t ranks keys t, t + nthr, ... (at most R);
+// every key pair is read from LDS once and compared with all of them.
+// k[n] must hold ~0 when n is odd.
+template <int R>
+__device__ void rank_by_count(const uint64_t* k, int n, uint16_t* rank, uint64_t* ranked) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  uint64_t x[R];
+  int r[R];
 #pragma unroll
-  for (int k = 2; k <= 128; k <<= 1) {
+  for (int t = 0; t < R; ++t) {
+    const int i = tid + t * nthr;
+    x[t] = i < n ? k[i] : 0ull;
+    r[t] = 0;
+  }
+#pragma unroll 4
+  for (int j = 0; j < n; j += 2) {
+    const uint64_t y0 = k[j], y1 = k[j + 1];
 #pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j == 64) {   // only k == 128: ascending across the two registers
-        const uint64_t lo = x[0] < x[1] ? x[0] : x[1], hi = x[0] < x[1] ? x[1] : x[0];
-        x[0] = lo;
-        x[1] = hi;
-      } else {
+    for (int t = 0; t < R; ++t) r[t] += int(y0 < x[t]) + int(y1 < x[t]);
+  }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int i = lane + 64 * h;
-          const uint64_t y = __shfl_xor(x[h], j);
-          const bool asc = (i & k) == 0, lower = (i & j) == 0;
-          const bool take_min = asc == lower;
-          x[h] = take_min ? (x[h] < y ? x[h] : y) : (x[h] < y ? y : x[h]);
-        }
-      }
+  for (int t = 0; t < R; ++t) {
+    const int i = tid + t * nthr;
+    if (i < n) {
+      rank[i] = uint16_t(r[t]);
+      ranked[r[t]] = x[t];
     }
   }
-  s[lane] = x[0];
-  s[lane + 64] = x[1];
 }
 
 __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
-  __shared__ SelScratch sc;
-  __shared__ uint64_t s_sort[kSortMax];
+  __shared__ SelScratch s_red;
+  BlockOps sc{s_red, 0};
+  __shared__ __align__(16) uint64_t s_sort[kSortMax + 2];
   __shared__ uint16_t s_rank[kSortMax];
+  __shared__ uint64_t s_ranked[kRankMax];
   __shared__ int s_kstar;
   __shared__ int s_hcnt[kHistBins];
   __shared__ float s_hmass[kHistBins];
@@ -186,6 +277,12 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
   // this thread's run: candidate c0 + e, e < per
   uint32_t key[kSelMaxPerThread];
   double ex[kSelMaxPerThread];
+  float sv[kSelMaxPerThread];
+#pragma unroll
+  for (int e = 0; e < kSelMaxPerThread; ++e) {   // every load in flight before any is used
+    const int c = c0 + e;
+    sv[e] = srow[(e < per && c < n) ? c : 0];
+  }
   uint32_t resid = 0, forcedm = 0;   // bit masks over the run
   float smax = -kInf;
 #pragma unroll
@@ -198,10 +295,9 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
       if (f) {
         forcedm |= 1u << e;
       } else {
-        const float s = srow[c];
         resid |= 1u << e;
-        key[e] = score_key(s);
-        smax = fmaxf(smax, s);
+        key[e] = score_key(sv[e]);
+        smax = fmaxf(smax, sv[e]);
       }
     }
   }
@@ -243,9 +339,7 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
     }
   }
   bool filtered = candm != resid || n_res > kSortMax;
-  int ncand;
-  int off = block_excl_scan_i32(__popc(candm), sc, ncand);
-  if (by_mass && ncand > kRefineMin) {
+  if (by_mass && n_res > kRefineMin) {
     // Narrow the candidates with a histogram of their masses over score bins
     // below the row max: keep the bins down to one past the bin where the
     // (fp32, any-order) cumulative mass first reaches the target.  The kept
@@ -270,33 +364,40 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
       }
     }
     __syncthreads();
-    if (tid == 0) {
+    static_assert(kHistBins == 64, "one wave scans the bins, lane b holding bin b");
+    if (tid < 64) {
       const float goal = float(target) * 1.001f;
-      float cum = 0.f;
-      int cnt = 0, b = 0;
-      for (; b < kHistBins; ++b) {
-        cum += s_hmass[b];
-        cnt += s_hcnt[b];
-        if (cum >= goal) break;
+      float cum = s_hmass[tid];
+      int cnt = s_hcnt[tid];
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(cum, o);
+        const int z = __shfl_up(cnt, o);
+        if (tid >= o) {
+          cum += y;
+          cnt += z;
+        }
       }
-      int bcut = min(b + 1, kHistBins - 1);
-      if (b + 1 < kHistBins) cnt += s_hcnt[b + 1];
-      s_bcut = (b < kHistBins && cnt < ncand && cnt >= kfloor) ? bcut : kHistBins;   // kHistBins: keep all
+      const int total = __shfl(cnt, 63);
+      const unsigned long long hit = __ballot(cum >= goal);
+      const int b = hit ? __ffsll((long long)hit) - 1 : kHistBins;   // first bin reaching the goal
+      const int bcut = min(b + 1, kHistBins - 1);
+      const int upto = __shfl(cnt, bcut);                               // candidates in bins 0..bcut
+      if (tid == 0)
+        s_bcut = (total > kRefineMin && b < kHistBins && upto < total && upto >= kfloor) ? bcut : kHistBins;
     }
     __syncthreads();
-    const int bcut = s_bcut;
+    const int bcut = s_bcut;   // kHistBins: keep all
     if (bcut < kHistBins) {
 #pragma unroll
       for (int e = 0; e < kSelMaxPerThread; ++e)
         if ((candm & (1u << e)) && int(bin[e]) > bcut) candm &= ~(1u << e);
       filtered = true;
-      off = block_excl_scan_i32(__popc(candm), sc, ncand);
     }
   }
+  int ncand;
+  const int off = block_excl_scan_i32(__popc(candm), sc, ncand);
   if (ncand <= kSortMax && ncand >= kfloor) {
-    int cap = 2;
-    while (cap < ncand) cap <<= 1;
-    if (cap <= kWaveSort) cap = kWaveSort;   // small sets: one wave sorts 128 keys in registers
     int w = off;
 #pragma unroll
     for (int e = 0; e < kSelMaxPerThread; ++e)
@@ -304,40 +405,50 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
         s_sort[w] = (uint64_t(~key[e]) << 32) | uint32_t(w);   // ascending: score desc, then id asc
         ++w;
       }
-    for (int k = ncand + tid; k < cap; k += nthr) s_sort[k] = ~0ull;
-    __syncthreads();
-    if (cap == kWaveSort) {
-      if (tid < 64) wave_sort128(s_sort, tid);
+    const uint64_t* ord;   // the candidates in ascending key order
+    const int rounds = (ncand + nthr - 1) / nthr;
+    if (ncand <= kRankMax && rounds <= kRankRounds && rounds * ncand <= kRankReads) {
+      if (tid == 0) s_sort[ncand] = ~0ull;   // pads an odd count; never below a key
       __syncthreads();
-    } else
-    for (int k = 2; k <= cap; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int e = tid; e < cap; e += nthr) {
-          const int p = e ^ j;
-          if (p > e) {
-            const uint64_t x = s_sort[e], y = s_sort[p];
-            if ((x > y) == ((e & k) == 0)) {
-              s_sort[e] = y;
-              s_sort[p] = x;
+      if (rounds == 1) rank_by_count<1>(s_sort, ncand, s_rank, s_ranked);
+      else rank_by_count<kRankRounds>(s_sort, ncand, s_rank, s_ranked);
+      __syncthreads();
+      ord = s_ranked;
+    } else {
+      int cap = 2;
+      while (cap < ncand) cap <<= 1;
+      for (int k = ncand + tid; k < cap; k += nthr) s_sort[k] = ~0ull;
+      __syncthreads();
+      for (int k = 2; k <= cap; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+          for (int e = tid; e < cap; e += nthr) {
+            const int p = e ^ j;
+            if (p > e) {
+              const uint64_t x = s_sort[e], y = s_sort[p];
+              if ((x > y) == ((e & k) == 0)) {
+                s_sort[e] = y;
+                s_sort[p] = x;
+              }
             }
           }
+          __syncthreads();
         }
-        __syncthreads();
       }
+      for (int k = tid; k < ncand; k += nthr) s_rank[uint32_t(s_sort[k])] = uint16_t(k);
+      ord = s_sort;
     }
-    for (int k = tid; k < ncand; k += nthr) s_rank[uint32_t(s_sort[k])] = uint16_t(k);
     int kstar = 0;
     if (by_mass) {
       if (tid == 0) s_kstar = 0x7fffffff;
       const int rper = (ncand + nthr - 1) / nthr;
       const int k0 = min(tid * rper, ncand), k1 = min(k0 + rper, ncand);
       double part = 0.0;
-      for (int kk = k0; kk < k1; ++kk) part += double(__expf(key_score(~uint32_t(s_sort[kk] >> 32)) - gmax));
+      for (int kk = k0; kk < k1; ++kk) part += double(__expf(key_score(~uint32_t(ord[kk] >> 32)) - gmax));
       double tot;
       double cum = block_excl_scan_f64(part, sc, tot);
       for (int kk = k0; kk < k1; ++kk) {
         const double prev = cum;
-        cum += double(__expf(key_score(~uint32_t(s_sort[kk] >> 32)) - gmax));
+        cum += double(__expf(key_score(~uint32_t(ord[kk] >> 32)) - gmax));
         if (cum >= target && !(prev >= target)) {
           atomicMin(&s_kstar, kk + 1);
           break;

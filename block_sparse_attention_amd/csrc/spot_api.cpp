@@ -92,6 +92,13 @@ size_t meanpool_ws_bytes(const spot_desc* d) {
   return slabs * d->batch * d->hkv * nb * d->d * sizeof(float);
 }
 
+// 16-byte vector loads and stores need 16-byte aligned bases (hipMalloc and torch give 256)
+int check_aligned16(const char* what, const void* p) {
+  if (p && (reinterpret_cast<uintptr_t>(p) & 15u))
+    return fail(SPOT_ERR_INVALID, "%s must be 16-byte aligned", what);
+  return SPOT_OK;
+}
+
 int check_workspace(size_t need, const void* ws, size_t have) {
   if (need == 0) return SPOT_OK;
   if (!ws || have < need) return fail(SPOT_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? have : size_t(0), need);
@@ -416,6 +423,9 @@ int spot_sparse_attn_decode(const spot_desc* desc, const void* q, const void* k_
   const int ns = spot::decode_num_splits(desc->batch, desc->hkv, nk);
   const size_t need = spot::decode_partials_bytes(desc->batch, desc->hq, desc->d, ns);
   if ((st = check_workspace(need, workspace, workspace_bytes))) return st;
+  if ((st = check_aligned16("q", q)) || (st = check_aligned16("k_cache", k_cache)) ||
+      (st = check_aligned16("v_cache", v_cache)) || (st = check_aligned16("workspace", workspace)))
+    return st;
   spot::DecodeArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                      static_cast<const uint16_t*>(v_cache), idx, cnt, static_cast<uint16_t*>(o), lse,
                      static_cast<float*>(workspace), desc->batch, desc->hq, desc->hkv, desc->d, int(desc->kv_len),

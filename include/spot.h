@@ -191,6 +191,8 @@ int spot_sparse_attn_prefill(const spot_desc* desc, const void* q, const void* k
  * o: [batch, hq, d]; lse (nullable): [batch, hq].
  * Work is split over the kept list; partial (max, sum, accumulator) triples go
  * to the workspace and are merged in a fixed order (deterministic).
+ * q, k_cache, v_cache and workspace must be 16-byte aligned (SPOT_ERR_INVALID
+ * otherwise).
  */
 int spot_sparse_attn_decode(const spot_desc* desc, const void* q, const void* k_cache,
                             const void* v_cache, const int32_t* idx, const int32_t* cnt, void* o,

@@ -138,6 +138,8 @@ def test_indexer_and_decode_validation():
     assert call_decode(_decode(), ws=None) == B.SPOT_ERR_WORKSPACE
     assert call_decode(_decode(), ws_bytes=8) == B.SPOT_ERR_WORKSPACE
     assert call_decode(_decode(), o=None) == B.SPOT_ERR_INVALID
+    for kw in (dict(q=FAKE + 8), dict(k=FAKE + 4), dict(v=FAKE + 2), dict(ws=FAKE + 8)):   # 16-byte loads/stores
+        assert call_decode(_decode(), **kw) == B.SPOT_ERR_INVALID, kw
 
 
 def call_perm(d, q=FAKE, k=FAKE, perm=FAKE, ws=FAKE, ws_bytes=1 << 30):

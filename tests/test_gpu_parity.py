@@ -388,7 +388,10 @@ def run_decode(cfg, D, gpu):
 
 @pytest.mark.parametrize("kw", [dict(batch=2, T=16 * 1000 + 5), dict(batch=3, T=4096, hq=16, hkv=2, d=64),
                                 dict(batch=2, T=2000, hq=8, hkv=8), dict(batch=1, T=10),
-                                dict(batch=2, T=5000, top_p=1.0), dict(batch=2, T=5000, top_p=0.0, k_min=7)],
+                                dict(batch=2, T=5000, top_p=1.0), dict(batch=2, T=5000, top_p=0.0, k_min=7),
+                                # 400 kept blocks x 64 (sequence, KV head) pairs: more work units than the
+                                # workgroups launched, several blocks per wave
+                                dict(batch=8, T=16 * 400, top_p=1.0)],
                          ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
 def test_decode_small(gpu, kw):
     cfg = I.C4.with_(name="dec", seed=23, **kw)
