@@ -1,48 +1,31 @@
 // Block-sparse decode attention for gfx950.
 //
 // One query per (sequence, head) at the last position attends the keys of the
-// kept 16-token blocks.  The step re-reads the kept part of the KV cache
-// (SpotAttention "Probleemstelling": every decode step re-reads a cache that
-// grows with the context); with a few dozen kept blocks per sequence it is
-// bound by latency rather than bandwidth, so the work is spread evenly over
-// workgroups that are all resident at once, and each wave issues every load
-// it needs in as few dependent rounds as possible.
+// kept 16-token blocks.  The step is bound by reading the kept part of the KV
+// cache (SpotAttention "Probleemstelling": every decode step re-reads a cache
+// that grows with the context), so the kernel streams rows with 16-byte
+// loads, several blocks in flight per thread, and keeps the arithmetic on the
+// VALU (bf16 pair dot products, fp32 accumulation).
 //
-// decode_split_kernel: the kept list of each (sequence b, KV head g) is cut
-//   into units of kDecUnitBlocks consecutive blocks (more when the list is
-//   long, so that a pair never has more than kDecMaxUnits units), and the
-//   units of all pairs are numbered in (b, g, unit) order.  Every workgroup
-//   derives that numbering from the kept counts and takes units blockIdx.x,
-//   blockIdx.x + gridDim.x, ...  Its four waves take the unit's blocks in
-//   turn (wave w: blocks w, w + 4, ...).  A wave is four rows of 16 lanes:
-//   row r takes key slots r, r + 4, ... and lane c of a row holds dims
-//   c*D/16 .. +D/16 of a key, keeping its own online-softmax state for the G
-//   query heads of the group.  Rows merge through lane swaps, waves through
-//   LDS, and the workgroup writes one partial (acc, m, l) per head and unit.
-// decode_combine_kernel: merges the partials of a pair's units in unit order
-//   (deterministic) and writes O (bf16) and the natural-log LSE.
+// decode_split_kernel: workgroup = (split s, KV head g, sequence b).  Split s
+//   takes kept blocks s, s + nsplit, s + 2*nsplit, ... of sequence b, so the
+//   block ids it needs do not depend on the kept count and their loads
+//   overlap the count's.  A row of 16 lanes owns one key slot of every block
+//   of the split (lane c holds dims c*D/16 .. +D/16), keeps its own
+//   online-softmax state for the G query heads of the group, and the 16 slot
+//   streams are merged through LDS into one partial (acc, m, l) per head.
+// decode_combine_kernel: merges the partials of the splits in split order
+//   (deterministic; all loads issued before the merge) and writes O (bf16)
+//   and the natural-log LSE.
 #include "../launch.h"
 #include "common.h"
 
 namespace spot {
 
-constexpr int kDecRows = 4;            // key streams (rows of 16 lanes) per wave
-constexpr int kDecWaves = 4;           // waves per workgroup
+constexpr int kDecThreads = 256;
+constexpr int kDecUnroll = 4;
 constexpr float kDecRescale = 8.0f;
-constexpr int kDecUnitBlocks = 2 * kDecWaves;   // kept blocks per unit while the list is short: two per wave
-constexpr int kDecMaxUnits = 32;       // units (partials) per (sequence, KV head)
-constexpr int kDecCombineChunk = 16;
-#ifndef SPOT_DECODE_KEYS_PER_ROW
-#define SPOT_DECODE_KEYS_PER_ROW 8     // key slots per row loaded in one round: two 16-key blocks (tuning knob)
-#endif
-constexpr int kDecKpr = SPOT_DECODE_KEYS_PER_ROW;
-#ifndef SPOT_DECODE_MAX_WGS
-#define SPOT_DECODE_MAX_WGS 768        // split workgroups launched: what the GPU holds at once at G = 4 (tuning knob)
-#endif
-
-// Units of a kept list of n blocks, and the blocks per unit.
-__device__ __forceinline__ int dec_units(int n) { return min(kDecMaxUnits, (n + kDecUnitBlocks - 1) / kDecUnitBlocks); }
-__device__ __forceinline__ int dec_unit_blocks(int n, int units) { return units > 0 ? (n + units - 1) / units : 0; }
+constexpr int kDecMaxSplits = 32;
 
 template <int EPL> struct DVec;
 template <> struct DVec<8> {
@@ -60,249 +43,183 @@ template <> struct DVec<4> {
   static __device__ __forceinline__ uint32_t w(const T& v, int k) { return k == 0 ? v.x : v.y; }
 };
 
-// Value of lane ^ 16 / lane ^ 32 through the gfx950 lane swaps (VALU, no LDS).
-__device__ __forceinline__ float lane_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
-                                                  false, false);
-  return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
-}
-__device__ __forceinline__ float lane_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
-                                                  false, false);
-  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
-}
+template <int D, int G>
+__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a, float scale_log2) {
+  constexpr int EPL = D / 16;           // elements per lane
+  constexpr int KS = kDecThreads / 16;  // key-slot streams per workgroup
+  using V = DVec<EPL>;
+  __shared__ float s_m[KS][G], s_l[KS][G];
+  __shared__ float s_acc[KS][G][D];
 
-// Merge the online-softmax state of this lane with that of lane ^ X (X = 16 or 32).
-template <int G, int EPL, int X>
-__device__ __forceinline__ void merge_rows(float (&m)[G], float (&l)[G], float (&acc)[G][EPL]) {
-  auto other = [](float x) { return X == 16 ? lane_xor16(x) : lane_xor32(x); };
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, c = tid & 15, ks = tid >> 4;
+  const int B = a.block, T = a.T;
+  const int32_t* il = a.idx + size_t(b) * a.nk;
+  // this split's first kDecUnroll block ids, loaded beside the count
+  int pre[kDecUnroll];
+#pragma unroll
+  for (int u = 0; u < kDecUnroll; ++u) {
+    const int bi = s + u * a.nsplit;
+    pre[u] = il[bi < a.nk ? bi : 0];
+  }
+  const int n = a.cnt[b];
+  if (s >= n) return;   // the combine reads splits [0, min(n, nsplit)) only
+  const int nmine = (n - s + a.nsplit - 1) / a.nsplit;   // blocks s, s+nsplit, ... below n
+  const int nslots = nmine * B;
+  const size_t kvbase = (size_t(b) * a.hkv + g) * size_t(T) * D;
+  const uint16_t* Kg = a.k + kvbase;
+  const uint16_t* Vg = a.v + kvbase;
+
+  typename V::T qv[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) qv[hh] = V::ld(a.q + (size_t(b) * a.hq + g * G + hh) * D + c * EPL);
+
+  float m[G], l[G], acc[G][EPL];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    const float mo = other(m[hh]), lo = other(l[hh]);
-    const float M = fmaxf(m[hh], mo);
-    const float fs = M == -kInf ? 0.f : __builtin_amdgcn_exp2f(m[hh] - M);
-    const float fo = M == -kInf ? 0.f : __builtin_amdgcn_exp2f(mo - M);
-    l[hh] = l[hh] * fs + lo * fo;
+    m[hh] = -kInf;
+    l[hh] = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[hh][e] = acc[hh][e] * fs + other(acc[hh][e]) * fo;
-    m[hh] = M;
+    for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
   }
-}
 
-// Partials: acc [batch, hkv, kDecMaxUnits, G, D] fp32, then (m, l) [batch, hkv, kDecMaxUnits, G, 2] fp32.
-__device__ __forceinline__ float* part_ml(const DecodeArgs& a, int G) {
-  return a.partials + size_t(a.batch) * a.hkv * kDecMaxUnits * G * a.d;
-}
-
-// Unit x of the (b, g, unit) numbering -> b, g, unit; false past the last unit.
-// Wave-level: lanes hold 64 sequences at a time, an inclusive scan of their
-// unit counts (times hkv) locates x.
-__device__ bool dec_find_unit(const DecodeArgs& a, int x, int& b, int& g, int& u, int& n) {
-  const int lane = threadIdx.x & 63;
-  int before = 0;
-  for (int b0 = 0; b0 < a.batch; b0 += 64) {
-    const int bb = b0 + lane;
-    const int nb = bb < a.batch ? a.cnt[bb] : 0;
-    const int units = bb < a.batch ? dec_units(nb) * a.hkv : 0;
-    int incl = units;
+  // slot = (local block k, key j); stream ks walks keys ks, ks + KS, ...
+  for (int base = ks; base < nslots; base += KS * kDecUnroll) {
+    typename V::T kv[kDecUnroll], vv[kDecUnroll];
+    bool ok[kDecUnroll];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    const unsigned long long hit = __ballot(before + incl > x);
-    if (hit) {
-      const int l0 = __ffsll((long long)hit) - 1;
-      b = b0 + l0;
-      n = __shfl(nb, l0);
-      const int first = before + __shfl(incl - units, l0);
-      const int per_pair = dec_units(n);
-      const int r = x - first;
-      g = r / per_pair;
-      u = r - g * per_pair;
-      return true;
-    }
-    before += __shfl(incl, 63);
-  }
-  return false;
-}
-
-template <int D, int G>
-__global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecodeArgs a, float scale_log2) {
-  constexpr int EPL = D / 16;   // elements per lane
-  using V = DVec<EPL>;
-  __shared__ float s_acc[kDecWaves][G][D];
-  __shared__ float s_ml[kDecWaves][G][2];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, c = lane & 15, row = lane >> 4;
-  const int B = a.block, T = a.T;
-
-  for (int x = blockIdx.x;; x += gridDim.x) {
-    int b, g, u, n;
-    if (!dec_find_unit(a, x, b, g, u, n)) return;   // the same answer in every wave
-    const int pair = b * a.hkv + g;
-    const int upp = dec_units(n), bpu = dec_unit_blocks(n, upp);
-    const int p0 = u * bpu, p1 = min(n, p0 + bpu);           // kept-list positions of this unit
-    const int nmine = p1 - p0 > w ? (p1 - p0 - w + kDecWaves - 1) / kDecWaves : 0;   // positions p0 + w + 4k
-    const int nslots = nmine * B;
-    const int32_t* il = a.idx + size_t(b) * a.nk;
-    const int pre0 = il[min(p0 + w, a.nk - 1)];
-    const int pre1 = il[min(p0 + w + kDecWaves, a.nk - 1)];
-    const size_t kvbase = size_t(pair) * size_t(T) * D;
-    const uint16_t* Kg = a.k + kvbase;
-    const uint16_t* Vg = a.v + kvbase;
-
-    typename V::T qv[G];
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int sl = base + u * KS;
+      ok[u] = false;
+      kv[u] = V::zero();
+      vv[u] = V::zero();
+      if (sl < nslots) {
+        const int kb = sl / B;
+        int blk;
+        if (kb < kDecUnroll) {
+          blk = pre[0];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) qv[hh] = V::ld(a.q + (size_t(b) * a.hq + g * G + hh) * D + c * EPL);
-
-    float m[G], l[G], acc[G][EPL];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      m[hh] = -kInf;
-      l[hh] = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
-    }
-
-    for (int base = 0; base < nslots; base += kDecRows * kDecKpr) {
-      typename V::T kv[kDecKpr], vv[kDecKpr];
-      bool ok[kDecKpr];
-#pragma unroll
-      for (int k = 0; k < kDecKpr; ++k) {
-        const int sl = base + row + kDecRows * k;   // slot = (local block kb, key sl - kb*B)
-        ok[k] = false;
-        kv[k] = V::zero();
-        vv[k] = V::zero();
-        if (sl < nslots) {
-          const int kb = sl / B;
-          const int blk = kb == 0 ? pre0 : kb == 1 ? pre1 : il[p0 + w + kDecWaves * kb];
-          const int pos = blk * B + (sl - kb * B);
-          if (pos < T) {
-            ok[k] = true;
-            kv[k] = V::ld(Kg + size_t(pos) * D + c * EPL);
-            vv[k] = V::ld(Vg + size_t(pos) * D + c * EPL);
-          }
+          for (int u2 = 1; u2 < kDecUnroll; ++u2) blk = (kb == u2) ? pre[u2] : blk;
+        } else {
+          blk = il[s + kb * a.nsplit];
         }
-      }
-#pragma unroll
-      for (int k = 0; k < kDecKpr; ++k) {
-        if (base + kDecRows * k >= nslots) break;   // no row has slot k (wave-uniform)
-        float vf[EPL];
-#pragma unroll
-        for (int k2 = 0; k2 < EPL / 2; ++k2) {
-          const uint32_t wv = V::w(vv[k], k2);
-          vf[2 * k2] = bf16_lo(wv);
-          vf[2 * k2 + 1] = bf16_hi(wv);
-        }
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          float dp = 0.f;
-#pragma unroll
-          for (int k2 = 0; k2 < EPL / 2; ++k2) dp = dot2_bf16(V::w(kv[k], k2), V::w(qv[hh], k2), dp);
-          dp = row16_sum(dp);
-          const float xs = dp * scale_log2;
-          const bool up = ok[k] && xs > m[hh] + kDecRescale;
-          if (__ballot(up)) {   // wave-uniform: rare after a row's first key
-            const float alpha = up ? __builtin_amdgcn_exp2f(m[hh] - xs) : 1.f;
-            l[hh] *= alpha;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[hh][e] *= alpha;
-            m[hh] = up ? xs : m[hh];
-          }
-          const float p = ok[k] ? __builtin_amdgcn_exp2f(xs - m[hh]) : 0.f;
-          l[hh] += p;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(p, vf[e], acc[hh][e]);
+        const int pos = blk * B + sl % B;
+        if (pos < T) {
+          ok[u] = true;
+          kv[u] = V::ld(Kg + size_t(pos) * D + c * EPL);
+          vv[u] = V::ld(Vg + size_t(pos) * D + c * EPL);
         }
       }
     }
-
-    merge_rows<G, EPL, 16>(m, l, acc);
-    merge_rows<G, EPL, 32>(m, l, acc);
-    if (row == 0) {
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      float vf[EPL];
+#pragma unroll
+      for (int k2 = 0; k2 < EPL / 2; ++k2) {
+        const uint32_t w = V::w(vv[u], k2);
+        vf[2 * k2] = bf16_lo(w);
+        vf[2 * k2 + 1] = bf16_hi(w);
+      }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
+        float dp = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; e += 4)
-          *reinterpret_cast<float4*>(&s_acc[w][hh][c * EPL + e]) =
-              make_float4(acc[hh][e], acc[hh][e + 1], acc[hh][e + 2], acc[hh][e + 3]);
-        if (c == 0) {
-          s_ml[w][hh][0] = m[hh];
-          s_ml[w][hh][1] = l[hh];
+        for (int k2 = 0; k2 < EPL / 2; ++k2) dp = dot2_bf16(V::w(kv[u], k2), V::w(qv[hh], k2), dp);
+        dp = row16_sum(dp);
+        if (!ok[u]) continue;
+        const float x = dp * scale_log2;
+        if (x > m[hh] + kDecRescale) {
+          const float alpha = __builtin_amdgcn_exp2f(m[hh] - x);
+          l[hh] *= alpha;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[hh][e] *= alpha;
+          m[hh] = x;
         }
+        const float p = __builtin_amdgcn_exp2f(x - m[hh]);
+        l[hh] += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(p, vf[e], acc[hh][e]);
       }
     }
-    __syncthreads();
-    float* pa = a.partials + (size_t(pair) * kDecMaxUnits + u) * G * D;
-    float* pm = part_ml(a, G) + (size_t(pair) * kDecMaxUnits + u) * G * 2;
-    for (int o = tid; o < G * D; o += 64 * kDecWaves) {
-      const int hh = o / D, dd = o - hh * D;
-      float M = -kInf;
+  }
+
+  // merge the KS slot streams
 #pragma unroll
-      for (int q = 0; q < kDecWaves; ++q) M = fmaxf(M, s_ml[q][hh][0]);
-      float A = 0.f, L = 0.f;
-      if (M != -kInf) {
-#pragma unroll
-        for (int q = 0; q < kDecWaves; ++q) {
-          const float f = __builtin_amdgcn_exp2f(s_ml[q][hh][0] - M);
-          A = fmaf(s_acc[q][hh][dd], f, A);
-          L = fmaf(s_ml[q][hh][1], f, L);
-        }
-      }
-      pa[o] = A;
-      if (dd == 0) *reinterpret_cast<float2*>(pm + hh * 2) = make_float2(M, L);
+  for (int hh = 0; hh < G; ++hh) {
+    if (c == 0) {
+      s_m[ks][hh] = m[hh];
+      s_l[ks][hh] = l[hh];
     }
-    __syncthreads();   // s_acc is rewritten by the next unit
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s_acc[ks][hh][c * EPL + e] = acc[hh][e];
+  }
+  __syncthreads();
+  float* part = a.partials + ((size_t(b) * a.hkv + g) * a.nsplit + s) * G * (D + 2);
+  for (int o = tid; o < G * D; o += kDecThreads) {
+    const int hh = o / D, dd = o % D;
+    float M = -kInf;
+    for (int q = 0; q < KS; ++q) M = fmaxf(M, s_m[q][hh]);
+    float A = 0.f, Lsum = 0.f;
+    if (M != -kInf) {
+      for (int q = 0; q < KS; ++q) {
+        const float f = __builtin_amdgcn_exp2f(s_m[q][hh] - M);
+        A = fmaf(s_acc[q][hh][dd], f, A);
+        Lsum = fmaf(s_l[q][hh], f, Lsum);
+      }
+    }
+    float* ph = part + hh * (D + 2);
+    ph[dd] = A;
+    if (dd == 0) {
+      ph[D] = M;
+      ph[D + 1] = Lsum;
+    }
   }
 }
 
-// Merge the ns unit partials of (pair, head hh) for output dim dd, in unit order; writes O and the LSE.
 template <int D, int G>
-__device__ void dec_combine_one(const DecodeArgs& a, int b, int g, int hh, int dd, int ns) {
-  const int h = g * G + hh;
-  const size_t pair = size_t(b) * a.hkv + g;
-  const float* pa = a.partials + (pair * kDecMaxUnits * G + hh) * D + dd;   // unit s at + s*G*D
-  const float* pm = part_ml(a, G) + (pair * kDecMaxUnits * G + hh) * 2;     // unit s at + s*G*2
-  float M = -kInf, A = 0.f, Lsum = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += kDecCombineChunk) {
-    float ms[kDecCombineChunk], ls[kDecCombineChunk], as[kDecCombineChunk];
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, dd = threadIdx.x;
+  const int g = h / G, hh = h % G;
+  const float* part = a.partials + ((size_t(b) * a.hkv + g) * a.nsplit) * G * (D + 2) + hh * (D + 2);
+  const size_t stride = size_t(G) * (D + 2);
+  const int ns = min(a.cnt[b], a.nsplit);
+  float ms[kDecMaxSplits], ls[kDecMaxSplits], as[kDecMaxSplits];
 #pragma unroll
-    for (int k = 0; k < kDecCombineChunk; ++k) {
-      const int sp = s0 + k;
-      const bool on = sp < ns;
-      const size_t so = on ? size_t(sp) : 0;
-      const float2 ml = *reinterpret_cast<const float2*>(pm + so * G * 2);
-      ms[k] = on ? ml.x : -kInf;
-      ls[k] = on ? ml.y : 0.f;
-      as[k] = on ? pa[so * G * D] : 0.f;
+  for (int s = 0; s < kDecMaxSplits; ++s) {
+    const bool on = s < ns;
+    const float* ps = part + (on ? s : 0) * stride;
+    ms[s] = on ? ps[D] : -kInf;
+    ls[s] = on ? ps[D + 1] : 0.f;
+    as[s] = on ? ps[dd] : 0.f;
+  }
+  float M = -kInf;
+#pragma unroll
+  for (int s = 0; s < kDecMaxSplits; ++s) M = fmaxf(M, ms[s]);
+  float A = 0.f, Lsum = 0.f;
+  if (M != -kInf) {
+#pragma unroll
+    for (int s = 0; s < kDecMaxSplits; ++s) {
+      const float f = __builtin_amdgcn_exp2f(ms[s] - M);   // 0 for empty splits
+      A = fmaf(as[s], f, A);
+      Lsum = fmaf(ls[s], f, Lsum);
     }
-    float Mc = M;
-#pragma unroll
-    for (int k = 0; k < kDecCombineChunk; ++k) Mc = fmaxf(Mc, ms[k]);
-    if (Mc == -kInf) continue;
-    const float f = __builtin_amdgcn_exp2f(M - Mc);   // 0 while nothing has been merged
-    A *= f;
-    Lsum *= f;
-#pragma unroll
-    for (int k = 0; k < kDecCombineChunk; ++k) {
-      const float fk = __builtin_amdgcn_exp2f(ms[k] - Mc);   // 0 for empty units
-      A = fmaf(as[k], fk, A);
-      Lsum = fmaf(ls[k], fk, Lsum);
-    }
-    M = Mc;
   }
   const float val = Lsum > 0.f ? A / Lsum : 0.f;
   a.o[(size_t(b) * a.hq + h) * D + dd] = uint16_t(pack_bf16x2(val, 0.f) & 0xFFFFu);
   if (a.lse && dd == 0) a.lse[size_t(b) * a.hq + h] = (Lsum > 0.f) ? (M + __log2f(Lsum)) * kLn2 : -kInf;
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  dec_combine_one<D, G>(a, b, h / G, h % G, threadIdx.x, dec_units(a.cnt[b]));
-}
+#ifndef SPOT_DECODE_TARGET_WGS
+#define SPOT_DECODE_TARGET_WGS 2048   // split workgroups per step (tuning knob)
+#endif
 
-int decode_num_splits(int, int, int) { return kDecMaxUnits; }
+int decode_num_splits(int batch, int hkv, int nk) {
+  const int pairs = batch * hkv;
+  int ns = (SPOT_DECODE_TARGET_WGS + pairs - 1) / pairs;
+  if (ns > kDecMaxSplits) ns = kDecMaxSplits;
+  if (ns > nk) ns = nk;
+  return ns < 1 ? 1 : ns;
+}
 
 size_t decode_partials_bytes(int batch, int hq, int d, int nsplit) {
   return size_t(batch) * hq * nsplit * (d + 2) * sizeof(float);
@@ -310,9 +227,7 @@ size_t decode_partials_bytes(int batch, int hq, int d, int nsplit) {
 
 template <int D, int G>
 static hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, float scale_log2) {
-  const long long most = (long long)a.batch * a.hkv * kDecMaxUnits;   // units can never exceed this
-  const unsigned grid = unsigned(most < SPOT_DECODE_MAX_WGS ? most : SPOT_DECODE_MAX_WGS);
-  decode_split_kernel<D, G><<<grid, 64 * kDecWaves, 0, s>>>(a, scale_log2);
+  decode_split_kernel<D, G><<<dim3(a.nsplit, a.hkv, a.batch), kDecThreads, 0, s>>>(a, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   decode_combine_kernel<D, G><<<dim3(a.hq, a.batch), D, 0, s>>>(a);
