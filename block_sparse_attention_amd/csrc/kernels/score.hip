@@ -160,11 +160,18 @@ hipError_t launch_pool_blocks(const PoolArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------- mean-pool score
 constexpr int kST = 32;  // score tile (query blocks x key blocks)
 
+// Tiles of pooled rows sit in LDS with rows padded by 4 floats: 16-byte
+// accesses stay aligned and the 16 key rows a wave reads start on distinct
+// 4-bank groups.  Each thread accumulates a 2x2 block of scores over d in
+// ascending order, four dims per LDS read.
+constexpr int kSPad = 4;
+
 template <bool TAYLOR>
 __global__ __launch_bounds__(256) void meanpool_score_kernel(MeanpoolScoreArgs a) {
-  extern __shared__ float sm[];
+  extern __shared__ float4 sm4[];
+  float* sm = reinterpret_cast<float*>(sm4);
   const int d = a.d, nb = a.nb;
-  const int ld = d + 1;
+  const int ld = d + kSPad;
   float* qs = sm;
   float* kn = qs + kST * ld;
   float* kp = kn + kST * ld;
@@ -187,48 +194,52 @@ __global__ __launch_bounds__(256) void meanpool_score_kernel(MeanpoolScoreArgs a
   const float* kpb = a.kbar_perm ? a.kbar_perm + bg * size_t(nb) * d : nullptr;
   const float* vnb = TAYLOR ? a.var_nat + bg * size_t(nb) * d : nullptr;
   const float* vpb = TAYLOR && kpb ? a.var_perm + bg * size_t(nb) * d : nullptr;
+  auto stage = [&](float* dst, const float* src, int row0, int r, int c) {
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(dst + r * ld + c) =
+        (row0 + r < nb) ? *reinterpret_cast<const float4*>(src + size_t(row0 + r) * d + c) : zero;
+  };
   for (int e = threadIdx.x; e < kST * d / 4; e += 256) {
     const int r = e / (d / 4), c = (e % (d / 4)) * 4;
-    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 vq = (i0 + r < nb) ? *reinterpret_cast<const float4*>(qb + size_t(i0 + r) * d + c) : zero;
-    const float4 vn = (j0 + r < nb) ? *reinterpret_cast<const float4*>(knb + size_t(j0 + r) * d + c) : zero;
-    qs[r * ld + c] = vq.x; qs[r * ld + c + 1] = vq.y; qs[r * ld + c + 2] = vq.z; qs[r * ld + c + 3] = vq.w;
-    kn[r * ld + c] = vn.x; kn[r * ld + c + 1] = vn.y; kn[r * ld + c + 2] = vn.z; kn[r * ld + c + 3] = vn.w;
-    if (kpb) {
-      const float4 vp = (j0 + r < nb) ? *reinterpret_cast<const float4*>(kpb + size_t(j0 + r) * d + c) : zero;
-      kp[r * ld + c] = vp.x; kp[r * ld + c + 1] = vp.y; kp[r * ld + c + 2] = vp.z; kp[r * ld + c + 3] = vp.w;
-    }
+    stage(qs, qb, i0, r, c);
+    stage(kn, knb, j0, r, c);
+    if (kpb) stage(kp, kpb, j0, r, c);
     if constexpr (TAYLOR) {
-      const float4 wn = (j0 + r < nb) ? *reinterpret_cast<const float4*>(vnb + size_t(j0 + r) * d + c) : zero;
-      vns[r * ld + c] = wn.x; vns[r * ld + c + 1] = wn.y; vns[r * ld + c + 2] = wn.z; vns[r * ld + c + 3] = wn.w;
-      if (vpb) {
-        const float4 wp = (j0 + r < nb) ? *reinterpret_cast<const float4*>(vpb + size_t(j0 + r) * d + c) : zero;
-        vps[r * ld + c] = wp.x; vps[r * ld + c + 1] = wp.y; vps[r * ld + c + 2] = wp.z; vps[r * ld + c + 3] = wp.w;
-      }
+      stage(vns, vnb, j0, r, c);
+      if (vpb) stage(vps, vpb, j0, r, c);
     }
   }
   __syncthreads();
   float sn[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, sp[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
   float tn[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, tp[2][2] = {{0.f, 0.f}, {0.f, 0.f}};   // TAYLOR: sum qbar_c^2 var_c
-  for (int c = 0; c < d; ++c) {
-    const float q0 = qs[(ty * 2) * ld + c], q1 = qs[(ty * 2 + 1) * ld + c];
-    const float k0 = kn[(tx * 2) * ld + c], k1 = kn[(tx * 2 + 1) * ld + c];
-    sn[0][0] = fmaf(q0, k0, sn[0][0]); sn[0][1] = fmaf(q0, k1, sn[0][1]);
-    sn[1][0] = fmaf(q1, k0, sn[1][0]); sn[1][1] = fmaf(q1, k1, sn[1][1]);
+  auto ld4 = [&](const float* base, int row, int c) { return *reinterpret_cast<const float4*>(base + row * ld + c); };
+  auto acc4 = [](float& s, const float4& x, const float4& y) {
+    s = fmaf(x.x, y.x, s);
+    s = fmaf(x.y, y.y, s);
+    s = fmaf(x.z, y.z, s);
+    s = fmaf(x.w, y.w, s);
+  };
+  auto sq4 = [](const float4& x) { return make_float4(x.x * x.x, x.y * x.y, x.z * x.z, x.w * x.w); };
+#pragma unroll 4
+  for (int c = 0; c < d; c += 4) {
+    const float4 q0 = ld4(qs, ty * 2, c), q1 = ld4(qs, ty * 2 + 1, c);
+    const float4 k0 = ld4(kn, tx * 2, c), k1 = ld4(kn, tx * 2 + 1, c);
+    acc4(sn[0][0], q0, k0); acc4(sn[0][1], q0, k1);
+    acc4(sn[1][0], q1, k0); acc4(sn[1][1], q1, k1);
     if (kpb) {
-      const float p0 = kp[(tx * 2) * ld + c], p1 = kp[(tx * 2 + 1) * ld + c];
-      sp[0][0] = fmaf(q0, p0, sp[0][0]); sp[0][1] = fmaf(q0, p1, sp[0][1]);
-      sp[1][0] = fmaf(q1, p0, sp[1][0]); sp[1][1] = fmaf(q1, p1, sp[1][1]);
+      const float4 p0 = ld4(kp, tx * 2, c), p1 = ld4(kp, tx * 2 + 1, c);
+      acc4(sp[0][0], q0, p0); acc4(sp[0][1], q0, p1);
+      acc4(sp[1][0], q1, p0); acc4(sp[1][1], q1, p1);
     }
     if constexpr (TAYLOR) {
-      const float qq0 = q0 * q0, qq1 = q1 * q1;
-      const float w0 = vns[(tx * 2) * ld + c], w1 = vns[(tx * 2 + 1) * ld + c];
-      tn[0][0] = fmaf(qq0, w0, tn[0][0]); tn[0][1] = fmaf(qq0, w1, tn[0][1]);
-      tn[1][0] = fmaf(qq1, w0, tn[1][0]); tn[1][1] = fmaf(qq1, w1, tn[1][1]);
+      const float4 qq0 = sq4(q0), qq1 = sq4(q1);
+      const float4 w0 = ld4(vns, tx * 2, c), w1 = ld4(vns, tx * 2 + 1, c);
+      acc4(tn[0][0], qq0, w0); acc4(tn[0][1], qq0, w1);
+      acc4(tn[1][0], qq1, w0); acc4(tn[1][1], qq1, w1);
       if (vpb) {
-        const float u0 = vps[(tx * 2) * ld + c], u1 = vps[(tx * 2 + 1) * ld + c];
-        tp[0][0] = fmaf(qq0, u0, tp[0][0]); tp[0][1] = fmaf(qq0, u1, tp[0][1]);
-        tp[1][0] = fmaf(qq1, u0, tp[1][0]); tp[1][1] = fmaf(qq1, u1, tp[1][1]);
+        const float4 u0 = ld4(vps, tx * 2, c), u1 = ld4(vps, tx * 2 + 1, c);
+        acc4(tp[0][0], qq0, u0); acc4(tp[0][1], qq0, u1);
+        acc4(tp[1][0], qq1, u0); acc4(tp[1][1], qq1, u1);
       }
     }
   }
@@ -250,10 +261,10 @@ hipError_t launch_meanpool_score(const MeanpoolScoreArgs& a, hipStream_t s) {
   const int nt = (a.nb + kST - 1) / kST;
   dim3 grid(nt, nt, a.batch * a.hkv);
   if (a.var_nat) {
-    const size_t lds = size_t(5) * kST * (a.d + 1) * sizeof(float);
+    const size_t lds = size_t(5) * kST * (a.d + kSPad) * sizeof(float);
     meanpool_score_kernel<true><<<grid, 256, lds, s>>>(a);
   } else {
-    const size_t lds = size_t(3) * kST * (a.d + 1) * sizeof(float);
+    const size_t lds = size_t(3) * kST * (a.d + kSPad) * sizeof(float);
     meanpool_score_kernel<false><<<grid, 256, lds, s>>>(a);
   }
   return hipGetLastError();
