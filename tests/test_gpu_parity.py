@@ -195,6 +195,51 @@ def test_select_kernel_on_oracle_scores(gpu):
         assert rep.mismatched_rows == 0 or top_p not in (0.0, 1.0)
 
 
+LONG_ROWS = [
+    # (name, candidates, score recipe): flat and narrow rows leave more than 2048 candidates after the
+    # histogram narrowing (cutoff search), N(0, 2.5) leaves about a thousand (bitonic sort), N(0, 4) a
+    # few dozen (ranking by counting); 5001 candidates put every row after the first off 16-byte alignment
+    ("flat", 8192, lambda r, n: np.zeros(n)),
+    ("narrow", 8192, lambda r, n: r.normal(0.0, 0.05, n)),
+    ("wide", 8192, lambda r, n: r.normal(0.0, 2.5, n)),
+    ("ties", 8192, lambda r, n: np.round(r.normal(0.0, 2.5, n), 1)),
+    ("peaked", 5001, lambda r, n: r.normal(0.0, 4.0, n)),
+    ("widest", 16384, lambda r, n: r.normal(0.0, 2.5, n)),
+]
+
+
+@pytest.mark.parametrize("case", LONG_ROWS, ids=lambda c: f"{c[0]}-{c[1]}")
+def test_select_long_decode_rows(gpu, case):
+    """Selection kernel on long decode rows, both sides on the same fp32 scores.  Besides the
+    cutoff rule (parity.compare_selection), the kept residual blocks must be exactly a prefix of
+    the oracle's order (score descending, ties to the lower block id)."""
+    name, nk, recipe = case
+    rng = np.random.default_rng([31, nk, len(name)])
+    rows = 4
+    s = np.stack([recipe(rng, nk) for _ in range(rows)]).astype(np.float32)
+    top_p = float(np.float32(0.9))
+    desc = B.make_desc(dtype=B.SPOT_BF16, batch=rows, hq=32, hkv=8, d=128, q_len=1, kv_len=16 * nk, block=16,
+                       top_p=top_p, n_sink=1, n_recent=1, score_kind=B.SPOT_SCORE_RELU_INDEXER, h_idx=4, d_idx=64)
+    idx = torch.full((rows, 1, 1, nk), -7, dtype=torch.int32, device=gpu)
+    cnt = torch.full((rows, 1, 1), -7, dtype=torch.int32, device=gpu)
+    B.spot_select_topp(desc, torch.from_numpy(s[:, None, None]).to(gpu), idx, cnt)
+    torch.cuda.synchronize()
+    gi, gc = idx.cpu().numpy()[:, 0, 0], cnt.cpu().numpy()[:, 0, 0]
+    rep = P.SelectionReport()
+    forced = oracle.decode_forced(nk, 1, 1)
+    for r in range(rows):
+        kept = gi[r, :gc[r]]
+        assert np.all(gi[r, gc[r]:] == -1) and np.all(np.diff(kept) > 0)
+        det = oracle.topp_detail(s[r].astype(np.float64), forced, top_p, 0)
+        resid = kept[~forced[kept]]
+        assert set(resid.tolist()) == set(det["order"][:resid.size].tolist()), (name, r)
+        if name == "flat":   # equal masses are exact on both sides: the same count
+            assert np.array_equal(kept, det["kept"]), (name, r, kept.size, det["kept"].size)
+        P.compare_selection(rep, kept, s[r].astype(np.float64), forced, top_p, 0, r)
+    log("long rows", name, nk, rep, "kept", gc.tolist())
+    assert not rep.violations, rep.violations[:5]
+
+
 def test_indexer_scores_and_decode_select(gpu):
     cfg = I.C4.with_(batch=3, T=16 * 3000 + 7, name="dec-small")
     D = I.decode_inputs(cfg)
