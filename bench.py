@@ -39,7 +39,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-early-stop", action="store_true", help="skip the early-stopping measurement")
@@ -90,18 +90,35 @@ def load_traffic(kernel_file: str, key: str):
 
 
 # ----------------------------------------------------------------- prefill
-def bench_prefill(args, torch, B, I, score_kind=None, top_p=None):
+def prefill_data(args, torch, I):
+    """Host and device inputs of the prefill workload (made once, shared by its measurements)."""
     cfg = {c.name: c for c in (I.C1, I.C2, I.C3, I.C5)}[args.workload]
+    q, k, v = I.prefill_inputs(cfg)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    dq, dk, dv = (torch.from_numpy(x).to(tdt).to(dev) for x in (q, k, v))
+    return cfg, (q, k), (dq, dk, dv)
+
+
+def settle(torch, fn, ms=30.0):
+    """Run fn untimed until about `ms` of GPU time has passed: after the host has kept the GPU idle (input
+    generation), its clock takes some milliseconds of work to come back up."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    done = 0.0
+    while done < ms:
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        done += e0.elapsed_time(e1)
+
+
+def bench_prefill(args, torch, B, I, data, score_kind=None, top_p=None):
+    cfg, (q, k), (dq, dk, dv) = data
     if top_p is not None:
         cfg = cfg.with_(top_p=top_p)
     score_kind = B.SPOT_SCORE_MEANPOOL if score_kind is None else score_kind
     dev = torch.device("cuda:0")
-    q, k, v = I.prefill_inputs(cfg)
-    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    dq = torch.from_numpy(q).to(tdt).to(dev)
-    dk = torch.from_numpy(k).to(tdt).to(dev)
-    dv = torch.from_numpy(v).to(tdt).to(dev)
-    del v
     desc = B.prefill_desc(dq, dk, cfg.block, cfg.top_p, segment=cfg.segment, score_kind=score_kind)
     bufs = B.alloc_prefill(desc, dev)
     perm = perm_ws = None
@@ -227,6 +244,7 @@ def bench_decode(args, torch, B, I, mxfp4=False):
         B.spot_sparse_attn_decode(desc, q, kc, vc, bufs.idx, bufs.cnt, bufs.o, bufs.lse, bufs.workspace)
         ev[2].record()
 
+    settle(torch, lambda: step([torch.cuda.Event(enable_timing=True) for _ in range(4)]))
     for _ in range(args.warmup):
         step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -312,6 +330,7 @@ def bench_early_stop(args, torch, B, I):
         if ev is not None:
             ev[3].record()
 
+    settle(torch, step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -399,6 +418,7 @@ def bench_history_map(args, torch, B, I):
         if ev is not None:
             ev[2].record()
 
+    settle(torch, step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -537,7 +557,28 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
 
-    pre = bench_prefill(args, torch, B, I)
+    data = prefill_data(args, torch, I)
+    # the ceilings are measured first: their GEMMs and copies also bring the GPU to its working clock after the
+    # host-side input generation, before the warm-up steps of the prefill step
+    ceil = measured_ceilings(torch)
+    print(f"[bench] measured ceilings: {ceil}", file=sys.stderr, flush=True)
+    pre = bench_prefill(args, torch, B, I, data)
+    # the same kernels keeping every block (p = 1): an in-house dense reference
+    dense = bench_prefill(args, torch, B, I, data, top_p=1.0)
+    dense_ref = {"workload": dense["cfg"].name, "top_p": 1.0, "ms_per_step": round(dense["ms_step"], 4),
+                 "ms_attention": round(dense["ms_attn"], 4), "value": round(dense["value"], 2), "unit": "TFLOP/s",
+                 "kept_fraction": round(dense["kept_fraction"], 4),
+                 "sparse_speedup_step": round(dense["ms_step"] / pre["ms_step"], 3),
+                 "sparse_speedup_attention": round(dense["ms_attn"] / pre["ms_attn"], 3)}
+    del dense
+    tay = None
+    if not args.no_taylor:
+        t = bench_prefill(args, torch, B, I, data, score_kind=B.SPOT_SCORE_TAYLOR)
+        tay = {"workload": t["cfg"].name, "score": "second-order Taylor", "value": round(t["value"], 2),
+               "unit": "TFLOP/s", "ms_per_step": round(t["ms_step"], 4), "ms_score_select": round(t["ms_sel"], 4),
+               "ms_attention": round(t["ms_attn"], 4), "kept_fraction": round(t["kept_fraction"], 4),
+               "flop_per_step": t["flops"]}
+        del t
     print(f"[bench] prefill {pre['cfg'].name}: {pre['ms_step_graph']:.4f} ms/step (graph), "
           f"{pre['ms_step_eager']:.4f} ms/step (eager), attention {pre['ms_attn']:.4f} ms, "
           f"score+select {pre['ms_sel']:.4f} ms, kept {pre['kept_fraction']:.4f}", file=sys.stderr, flush=True)
@@ -547,26 +588,9 @@ def main():
         print(f"[bench] decode: {dec}", file=sys.stderr, flush=True)
         dec_mx = bench_decode(args, torch, B, I, mxfp4=True)
         print(f"[bench] decode mxfp4: {dec_mx}", file=sys.stderr, flush=True)
-    # the same kernels keeping every block (p = 1): an in-house dense reference
-    dense = bench_prefill(args, torch, B, I, top_p=1.0)
-    dense_ref = {"workload": dense["cfg"].name, "top_p": 1.0, "ms_per_step": round(dense["ms_step"], 4),
-                 "ms_attention": round(dense["ms_attn"], 4), "value": round(dense["value"], 2), "unit": "TFLOP/s",
-                 "kept_fraction": round(dense["kept_fraction"], 4),
-                 "sparse_speedup_step": round(dense["ms_step"] / pre["ms_step"], 3),
-                 "sparse_speedup_attention": round(dense["ms_attn"] / pre["ms_attn"], 3)}
-    del dense
     print(f"[bench] dense reference: {dense_ref}", file=sys.stderr, flush=True)
-    tay = None
-    if not args.no_taylor:
-        t = bench_prefill(args, torch, B, I, score_kind=B.SPOT_SCORE_TAYLOR)
-        tay = {"workload": t["cfg"].name, "score": "second-order Taylor", "value": round(t["value"], 2),
-               "unit": "TFLOP/s", "ms_per_step": round(t["ms_step"], 4), "ms_score_select": round(t["ms_sel"], 4),
-               "ms_attention": round(t["ms_attn"], 4), "kept_fraction": round(t["kept_fraction"], 4),
-               "flop_per_step": t["flops"]}
-        del t
+    if tay:
         print(f"[bench] taylor: {tay}", file=sys.stderr, flush=True)
-    ceil = measured_ceilings(torch)
-    print(f"[bench] measured ceilings: {ceil}", file=sys.stderr, flush=True)
     es = es_map = None
     if not args.no_early_stop:
         es = bench_early_stop(args, torch, B, I)

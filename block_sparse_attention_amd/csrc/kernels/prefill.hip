@@ -120,9 +120,11 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKT * KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKT * VLD];
   __shared__ int kpos[3][kKT];
-  __shared__ int s_list[kListCap > 0 ? kListCap : 1];
+  // early stopping always stages its (reordered) list; the top-p kernel only up to kListCap entries
+  constexpr int LCAP = ES ? (kListCap > kEsMaxBlocks ? kListCap : kEsMaxBlocks) : kListCap;
+  __shared__ int s_list[LCAP > 0 ? LCAP : 1];
   __shared__ int s_act[2][NW];   // early stop: per-wave "a row is still taking blocks", by tile parity
-  static_assert(!ES || kListCap >= kEsMaxBlocks, "early stopping stages its visiting list in LDS");
+  static_assert(!ES || LCAP >= kEsMaxBlocks, "early stopping stages its visiting list in LDS");
 
   const int pairs = a.batch * a.hkv;
   int pair, i, chunk;
@@ -170,9 +172,9 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
     own_tiles = (n_own * B) / kKT;
   } else {
     nkept = a.cnt[row_id];
-    if constexpr (kListCap > 0)
-      for (int k = tid; k < min(nkept, kListCap); k += NT) s_list[k] = glist[k];
-    lst = (kListCap > 0 && nkept <= kListCap) ? s_list : glist;
+    if constexpr (LCAP > 0)
+      for (int k = tid; k < min(nkept, LCAP); k += NT) s_list[k] = glist[k];
+    lst = (LCAP > 0 && nkept <= LCAP) ? s_list : glist;
   }
   const int32_t* permg =
       PERM ? a.perm + (ES && a.es_hmap ? size_t(pair) * a.nseg + seg_start / max(a.segment, 1) : size_t(pair)) * L
