@@ -374,8 +374,24 @@ def bench_early_stop(args, torch, B, I):
         part = packed[..., c0:c0 + 256]
         walked += float((own_packed[None, :, c0:c0 + 256] + part.max(axis=-1, keepdims=True) * Bk).sum())
     achieved = flops / (ms_attn * 1e-3) / 1e12
+
+    # top-p selection at the workload's p with history means over the permuted keys and without the
+    # permutation: how many blocks the same mass needs in each case (outside the timed steps)
+    kept = {}
+    for name, seg, pm in (("with_permutation", cfg.segment, perm), ("without_permutation", 0, None)):
+        d2 = B.prefill_desc(dq, dk, cfg.block, cfg.top_p, segment=seg)
+        b2 = B.alloc_prefill(d2, dev)
+        B.spot_block_score(d2, dq, dk, pm, None, None, None, b2.scores, b2.workspace)
+        B.spot_select_topp(d2, b2.scores, b2.idx, b2.cnt)
+        torch.cuda.synchronize()
+        kept[name] = int(b2.cnt.cpu().numpy().astype(np.int64).sum())
+        del b2
+    cand = cfg.hkv * cfg.nb * (cfg.nb + 1) // 2
+    top_p_blocks = {"top_p": cfg.top_p, "candidate_blocks": cand, **kept,
+                    "change": round(kept["with_permutation"] / kept["without_permutation"] - 1.0, 4)}
     return dict(
         workload=cfg.name, tau=tau, value=round(flops / (ms_step * 1e-3) / 1e12, 2), unit="TFLOP/s",
+        top_p_kept_blocks=top_p_blocks,
         ms_per_step=round(ms_step, 4), ms_key_permutation=round(ms_perm, 4), ms_score_order=round(ms_front, 4),
         ms_attention=round(ms_attn, 4), taken_fraction=round(float(pairs_row.sum()) / dense_pairs, 4),
         walked_fraction=round(walked / dense_pairs, 4), mean_history_blocks=round(float(nused.mean()), 2),
