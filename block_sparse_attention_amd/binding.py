@@ -25,7 +25,8 @@ ABI_VERSION = 1
 EXPORTS = ("spot_version", "spot_status_string", "spot_last_error", "spot_workspace_size", "spot_block_score",
            "spot_select_topp", "spot_sparse_attn_prefill", "spot_sparse_attn_decode", "spot_key_permutation",
            "spot_order_history", "spot_sparse_attn_prefill_early_stop", "spot_quantize_indexer_keys",
-           "spot_indexer_score_mxfp4", "spot_history_map", "spot_sparse_attn_prefill_history_map")
+           "spot_indexer_score_mxfp4", "spot_history_map", "spot_sparse_attn_prefill_history_map",
+           "spot_validate_perm")
 
 
 class spot_desc(ctypes.Structure):
@@ -75,6 +76,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spot_history_map.argtypes = [D, P, P, P, P, S, P]
     lib.spot_sparse_attn_prefill_history_map.argtypes = [D, ctypes.c_float, P, P, P, P, P, P, P, P, S, P]
     lib.spot_sparse_attn_prefill_early_stop.argtypes = [D, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.spot_validate_perm.argtypes = [D, P, P, P]
     for name in EXPORTS[3:]:
         getattr(lib, name).restype = I
     _lib = lib
@@ -145,6 +147,12 @@ def spot_key_permutation(desc, q, k, perm, importance=None, workspace=None, stre
     st = load_library().spot_key_permutation(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(perm), _ptr(importance),
                                              _ptr(workspace), ws_bytes, _stream() if stream is None else stream)
     _check("spot_key_permutation", st)
+
+
+def spot_validate_perm(desc, perm, bad, stream=None):
+    st = load_library().spot_validate_perm(ctypes.byref(desc), _ptr(perm), _ptr(bad),
+                                           _stream() if stream is None else stream)
+    _check("spot_validate_perm", st)
 
 
 def spot_quantize_indexer_keys(desc, idx_k, k_codes, k_scales, stream=None):

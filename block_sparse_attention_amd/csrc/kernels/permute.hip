@@ -272,6 +272,58 @@ static hipError_t launch_perm_d(PermArgs a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- bijection check
+// Debug check that perm maps each segment onto itself one to one: one
+// workgroup per (segment, batch x KV head) marks the values it sees in an LDS
+// bitmap; a value outside the position's segment, or one already marked,
+// counts as one violation.  As many values as positions are checked, so zero
+// violations means a bijection.
+constexpr int kCheckThreads = 256;
+
+__global__ void perm_check_zero(int32_t* bad) {
+  if (threadIdx.x == 0) *bad = 0;
+}
+
+__global__ __launch_bounds__(kCheckThreads) void perm_check_kernel(PermCheckArgs a) {
+  __shared__ uint32_t bits[kPermMaxSegment / 32];
+  __shared__ int s_bad[kCheckThreads / 64];
+  const int seg = blockIdx.x;
+  const size_t pair = blockIdx.y;
+  const int s0 = seg * a.segment;
+  const int n = min(a.segment, a.L - s0);
+  for (int w = threadIdx.x; w < (n + 31) / 32; w += kCheckThreads) bits[w] = 0u;
+  __syncthreads();
+  const int32_t* p = a.perm + pair * a.L + s0;
+  int bad = 0;
+  for (int i = threadIdx.x; i < n; i += kCheckThreads) {
+    const uint32_t v = uint32_t(p[i]) - uint32_t(s0);   // wraps for values below the segment
+    if (v >= uint32_t(n)) {
+      ++bad;
+      continue;
+    }
+    const uint32_t m = 1u << (v & 31u);
+    if (atomicOr(&bits[v >> 5], m) & m) ++bad;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) bad += __shfl_xor(bad, o);
+  if ((threadIdx.x & 63) == 0) s_bad[threadIdx.x >> 6] = bad;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int t = 0;
+    for (int w = 0; w < kCheckThreads / 64; ++w) t += s_bad[w];
+    if (t) atomicAdd(a.bad, t);
+  }
+}
+
+hipError_t launch_perm_check(const PermCheckArgs& a, hipStream_t s) {
+  perm_check_zero<<<1, 64, 0, s>>>(a.bad);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nseg = (a.L + a.segment - 1) / a.segment;
+  perm_check_kernel<<<dim3(unsigned(nseg), unsigned(a.pairs)), kCheckThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_key_permutation(const PermArgs& a, hipStream_t s) {
   if (a.d == 128) return launch_perm_d<128>(a, s);
   if (a.d == 64) return launch_perm_d<64>(a, s);

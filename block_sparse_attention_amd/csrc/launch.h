@@ -146,6 +146,13 @@ int perm_num_chunks(int L);
 int perm_num_groups(int G, int nr);
 size_t perm_workspace_bytes(int batch, int hkv, int L, int G, int nr);
 constexpr int kPermMaxSegment = 16384;
+
+struct PermCheckArgs {
+  const int32_t* perm;   // [pairs, L]
+  int32_t* bad;          // one int32: violations found
+  int L, segment, pairs;
+};
+hipError_t launch_perm_check(const PermCheckArgs& a, hipStream_t s);
 constexpr int kPermRowsPerGroup = 256;   // query rows per workgroup in the permutation passes
 
 }  // namespace spot

@@ -470,4 +470,16 @@ int spot_key_permutation(const spot_desc* desc, const void* q, const void* k, in
   return launched(spot::launch_key_permutation(a, static_cast<hipStream_t>(stream)), "key_permutation");
 }
 
+int spot_validate_perm(const spot_desc* desc, const int32_t* perm, int32_t* bad, void* stream) {
+  int st = check_common(desc);
+  if (st) return st;
+  if ((st = check_prefill_shape(desc))) return st;
+  if (!perm || !bad) return fail(SPOT_ERR_INVALID, "perm and bad are required");
+  if (desc->segment <= 0) return fail(SPOT_ERR_INVALID, "segment must be > 0");
+  if (desc->segment > spot::kPermMaxSegment)
+    return fail(SPOT_ERR_UNSUPPORTED, "segment %d (max %d)", desc->segment, spot::kPermMaxSegment);
+  spot::PermCheckArgs a{perm, bad, int(desc->q_len), desc->segment, desc->batch * desc->hkv};
+  return launched(spot::launch_perm_check(a, static_cast<hipStream_t>(stream)), "validate_perm");
+}
+
 }  // extern "C"

@@ -10,6 +10,7 @@
  *   spot_sparse_attn_prefill online-softmax attention over the kept blocks (GQA prefill)
  *   spot_sparse_attn_decode  the same for one decode query per sequence
  *   spot_key_permutation     the intra-segment key permutation the prefill gathers through
+ *   spot_validate_perm       debug check that a permutation maps every segment onto itself
  *
  * the selector key cache in FP4 microscaling for the decode scan:
  *
@@ -213,6 +214,19 @@ int spot_sparse_attn_decode(const spot_desc* desc, const void* q, const void* k_
  */
 int spot_key_permutation(const spot_desc* desc, const void* q, const void* k, int32_t* perm, float* importance,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Debug check of a permutation handed to the prefill calls, which trust it:
+ * inside each segment [sS, min((s+1)S, L)) of every (batch, KV head), perm
+ * must be a bijection of the segment's positions ([PBS] §2: the permutation
+ * stays inside segments so that causality between segments holds).
+ * perm: int32 [batch, hkv, q_len]; bad: one int32 of device memory that the
+ * call sets to the number of violations (a value outside its position's
+ * segment, or a value seen before in the segment); 0 means valid.  The result
+ * is ready when the stream reaches it (the call does not synchronise).
+ * Requires segment > 0 and at most 16384.
+ */
+int spot_validate_perm(const spot_desc* desc, const int32_t* perm, int32_t* bad, void* stream);
 
 /*
  * Selector key cache in FP4 microscaling ([Spot] §4 quantisation: the

@@ -157,6 +157,18 @@ def test_key_permutation_validation():
     assert B.spot_workspace_size(_prefill(segment=256), B.SPOT_OP_KEY_PERMUTATION) > 0
 
 
+def call_vperm(d, perm=FAKE, bad=FAKE):
+    return B.load_library().spot_validate_perm(ctypes.byref(d), perm, bad, None)
+
+
+def test_validate_perm_validation():
+    assert call_vperm(_prefill(segment=0)) == B.SPOT_ERR_INVALID
+    assert call_vperm(_prefill(segment=32768, q_len=65536, kv_len=65536)) == B.SPOT_ERR_UNSUPPORTED
+    assert call_vperm(_prefill(segment=256), perm=None) == B.SPOT_ERR_INVALID
+    assert call_vperm(_prefill(segment=256), bad=None) == B.SPOT_ERR_INVALID
+    assert call_vperm(_prefill(segment=256, q_len=512)) == B.SPOT_ERR_INVALID          # q_len != kv_len
+
+
 def call_order(d, scores=FAKE, order=FAKE, cnt=FAKE):
     return B.load_library().spot_order_history(ctypes.byref(d), scores, order, cnt, None, 0, None)
 

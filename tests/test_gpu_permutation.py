@@ -57,6 +57,45 @@ def test_key_permutation_matches_oracle(gpu, kw):
     perm, imp = B.key_permutation(dq, dk, cfg.block, cfg.segment, with_importance=True)
     torch.cuda.synchronize()
     check_permutation(cfg, q, k, perm.cpu().numpy(), imp.cpu().numpy())
+    bad = torch.full((1,), -1, dtype=torch.int32, device=gpu)
+    B.spot_validate_perm(B.prefill_desc(dq, dk, cfg.block, cfg.top_p, segment=cfg.segment), perm, bad)
+    assert int(bad.item()) == 0
+
+
+@pytest.mark.parametrize("L,segment", [(1536, 256), (1000, 256), (777, 64), (16384 + 100, 16384)])
+def test_validate_perm(gpu, L, segment):
+    """The bijection check: random per-segment permutations (ragged last segments) pass; corruptions of
+    known kind count one violation each (a repeated value, a value from another segment, values below 0
+    or beyond L)."""
+    batch, hkv = 2, 3
+    rng = np.random.default_rng([L, segment])
+    perm = np.empty((batch, hkv, L), dtype=np.int32)
+    for b in range(batch):
+        for g in range(hkv):
+            for s0 in range(0, L, segment):
+                perm[b, g, s0:s0 + segment] = rng.permutation(np.arange(s0, min(L, s0 + segment)))
+    desc = B.make_desc(dtype=B.SPOT_BF16, batch=batch, hq=2 * hkv, hkv=hkv, d=128, q_len=L, kv_len=L, block=16,
+                       segment=segment)
+    bad = torch.full((1,), -1, dtype=torch.int32, device=gpu)
+
+    def violations(p):
+        B.spot_validate_perm(desc, torch.from_numpy(p).to(gpu), bad)
+        torch.cuda.synchronize()
+        return int(bad.item())
+
+    assert violations(perm) == 0
+    c = perm.copy()
+    c[0, 0, 5] = c[0, 0, 6]                      # a value repeated inside segment 0
+    assert violations(c) == 1
+    c = perm.copy()
+    c[1, 2, L - 1] = perm[1, 2, 0]               # the last position takes a value of segment 0
+    assert violations(c) == 1
+    c = perm.copy()
+    c[0, 1, 3] = -5                              # below every segment
+    c[1, 0, L - 2] = L + 7                       # beyond L
+    c[1, 1, 2] = c[1, 1, 1]                      # and a repeat
+    assert violations(c) == 3
+    assert violations(perm) == 0                 # the count starts from zero on every call
 
 
 def test_c3_heavy_hitter_prefill_on_device(gpu):
