@@ -33,6 +33,7 @@ constexpr int kSortMax = 2048;         // candidates sorted exactly in LDS
 constexpr int kRankReads = 512;        // rank by counting while each thread compares at most this many keys
 constexpr int kRankMax = 512;          // ... which bounds the set to 512 candidates (nthr <= 1024)
 constexpr int kRankRounds = 3;         // and gives each thread at most 3 of them (nthr >= 64)
+static_assert(kRankMax < kSortMax, "the key after a counted set pads an odd count");
 constexpr int kRefineMin = 128;        // long rows: above this many candidates, narrow them by a score histogram
 constexpr int kHistBins = 64;          // histogram bins of width 1/kHistScale in score units below the row max
 constexpr float kHistScale = 4.0f;
@@ -257,7 +258,7 @@ __device__ void rank_by_count(const uint64_t* k, int n, uint16_t* rank, uint64_t
 __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
   __shared__ SelScratch s_red;
   BlockOps sc{s_red, 0};
-  __shared__ __align__(16) uint64_t s_sort[kSortMax + 2];
+  __shared__ __align__(16) uint64_t s_sort[kSortMax];   // counting reads pairs: s_sort[ncand] pads an odd count (ncand <= kRankMax < kSortMax)
   __shared__ uint16_t s_rank[kSortMax];
   __shared__ uint64_t s_ranked[kRankMax];
   __shared__ int s_kstar;
