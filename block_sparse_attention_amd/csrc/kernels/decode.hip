@@ -210,7 +210,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
 }
 
 #ifndef SPOT_DECODE_TARGET_WGS
-#define SPOT_DECODE_TARGET_WGS 2048   // split workgroups per step (tuning knob)
+#define SPOT_DECODE_TARGET_WGS 1536   // split workgroups per step: 1280-1792 measured 7% faster than 2048 (tuning knob)
 #endif
 
 int decode_num_splits(int batch, int hkv, int nk) {
