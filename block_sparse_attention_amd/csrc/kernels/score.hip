@@ -275,8 +275,16 @@ hipError_t launch_meanpool_score(const MeanpoolScoreArgs& a, hipStream_t s) {
 // elements (16 bytes) per lane; lanes of one indexer head sum their dot
 // products, the head leaders add w_h * ReLU(dot), and the row's lanes sum the
 // heads.  Each lane keeps kIdxUnroll rows in flight; one grid row per sequence.
-constexpr int kIdxUnroll = 4;
-constexpr int kIdxMaxBlocks = 64;   // workgroups per sequence
+#ifndef SPOT_INDEXER_UNROLL
+#define SPOT_INDEXER_UNROLL 4         // rows in flight per lane (tuning knob)
+#endif
+#ifndef SPOT_INDEXER_MAX_BLOCKS
+#define SPOT_INDEXER_MAX_BLOCKS 256   // workgroups per sequence: enough that each takes one round of rows (tuning knob)
+#endif
+constexpr int kIdxUnroll = SPOT_INDEXER_UNROLL;
+constexpr int kIdxMaxBlocks = SPOT_INDEXER_MAX_BLOCKS;
+constexpr int kFp4Unroll = 4;       // the same for the MXFP4 scan
+constexpr int kFp4MaxBlocks = 64;
 
 template <int LPR>
 __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerScoreArgs a) {
@@ -420,19 +428,19 @@ __global__ __launch_bounds__(256) void indexer_score_mxfp4_kernel(IndexerFp4Args
   const float w = a.idx_w[size_t(b) * a.h_idx + head];
   const uint8_t* cb = a.codes + size_t(b) * a.nk * (R / 2);
   const uint8_t* sb = a.scales + size_t(b) * a.nk * (R / 32);
-  const int step = gridDim.x * 4 * RPW * kIdxUnroll;
-  for (int t0 = (blockIdx.x * 4 + wave) * RPW * kIdxUnroll; t0 < a.nk; t0 += step) {
-    uint4 cv[kIdxUnroll];
-    int ex[kIdxUnroll];
+  const int step = gridDim.x * 4 * RPW * kFp4Unroll;
+  for (int t0 = (blockIdx.x * 4 + wave) * RPW * kFp4Unroll; t0 < a.nk; t0 += step) {
+    uint4 cv[kFp4Unroll];
+    int ex[kFp4Unroll];
 #pragma unroll
-    for (int u = 0; u < kIdxUnroll; ++u) {
+    for (int u = 0; u < kFp4Unroll; ++u) {
       const int t = t0 + u * RPW + sub;
       const bool in = t < a.nk;
       cv[u] = in ? *reinterpret_cast<const uint4*>(cb + size_t(t) * (R / 2) + li * 16) : make_uint4(0u, 0u, 0u, 0u);
       ex[u] = in ? int(sb[size_t(t) * (R / 32) + li]) - 127 : 0;
     }
 #pragma unroll
-    for (int u = 0; u < kIdxUnroll; ++u) {
+    for (int u = 0; u < kFp4Unroll; ++u) {
       const uint32_t cw[4] = {cv[u].x, cv[u].y, cv[u].z, cv[u].w};
       float dp = 0.f;
 #pragma unroll
@@ -461,9 +469,9 @@ __global__ __launch_bounds__(256) void indexer_score_mxfp4_kernel(IndexerFp4Args
 
 template <int LPR>
 static void launch_idx_fp4(const IndexerFp4Args& a, hipStream_t s) {
-  const int per_block = 4 * (64 / LPR) * kIdxUnroll;
+  const int per_block = 4 * (64 / LPR) * kFp4Unroll;
   int blocks = (a.nk + per_block - 1) / per_block;
-  if (blocks > kIdxMaxBlocks) blocks = kIdxMaxBlocks;
+  if (blocks > kFp4MaxBlocks) blocks = kFp4MaxBlocks;
   indexer_score_mxfp4_kernel<LPR><<<dim3(blocks, a.batch), 256, 0, s>>>(a);
 }
 
