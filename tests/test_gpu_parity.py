@@ -274,6 +274,8 @@ PIPE_SMALL = [
     dict(L=40, hq=4, hkv=2, d=128, block=64, top_p=0.9),        # one partial block
     dict(L=1, hq=2, hkv=1, d=64, block=16, top_p=0.9),          # a single token
     dict(L=300, hq=2, hkv=2, d=64, block=16, top_p=0.9, dtype="f32"),
+    dict(L=900, hq=16, hkv=4, d=128, block=64, top_p=0.9, batch=2),   # 8 (batch, KV head) pairs: XCD-pinned order
+    dict(L=600, hq=8, hkv=2, d=64, block=32, top_p=0.85, batch=3),
 ]
 
 
