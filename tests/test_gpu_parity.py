@@ -438,7 +438,9 @@ def run_decode(cfg, D, gpu):
                                 dict(batch=2, T=5000, top_p=1.0), dict(batch=2, T=5000, top_p=0.0, k_min=7),
                                 # 400 kept blocks x 64 (sequence, KV head) pairs: more work units than the
                                 # workgroups launched, several blocks per wave
-                                dict(batch=8, T=16 * 400, top_p=1.0)],
+                                dict(batch=8, T=16 * 400, top_p=1.0),
+                                dict(batch=2, T=64 * 300 + 17, block=64),    # larger blocks, ragged last block
+                                dict(batch=3, T=32 * 500, block=32, top_p=0.8)],
                          ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
 def test_decode_small(gpu, kw):
     cfg = I.C4.with_(name="dec", seed=23, **kw)
