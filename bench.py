@@ -566,7 +566,8 @@ def cpu_baseline(res, I, sample_blocks: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (prefill would shard by KV head "
+              "and decode by sequence, with no exchange; one GPU's share is what is timed)", file=sys.stderr)
         sys.exit(2)
     import torch
     from block_sparse_attention_amd import binding as B
