@@ -19,7 +19,8 @@
 //   of the PV product is read with the transposing LDS load.
 //   S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16, so every
 //   lane owns one query column: row max/sum stay in-lane plus one exchange
-//   between the two lane halves.  P is rounded to bf16 for the PV product.
+//   between the two lane halves (the gfx950 lane-half swap, no LDS round
+//   trip).  P is rounded to bf16 for the PV product.
 //   The running max is only moved when a tile raises it by more than 2^8
 //   (the softmax is invariant to the shift, so the result is unchanged).
 //   Work units are ordered longest-first (query block descending) and, when
@@ -74,8 +75,16 @@ __device__ __forceinline__ void unit_of(int w, int pairs, int nb, int chunks, in
   }
 }
 
-__device__ __forceinline__ float xhalf_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float xhalf_sum(float x) { return x + __shfl_xor(x, 32); }
+// lane l and lane l^32 exchange through the gfx950 lane-half swap (a VALU op, no LDS round trip);
+// the two results of the swap hold the own and the partner value in either order
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
@@ -258,6 +267,14 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
       }
   };
 
+  // this lane's max over a score tile (the lane-half exchange comes later)
+  auto lane_max = [&](const f32x16_t (&st)[2]) {
+    float mx = __builtin_fmaxf(st[0][0], st[1][0]);
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = __builtin_fmaxf(__builtin_fmaxf(mx, st[0][e]), st[1][e]);
+    return mx;
+  };
+
   f32x16_t oacc[QG][D / 32];
   float m_run[QG], l_run[QG];   // ES: l_run is the whole row's sum (both lane halves); else this half's
   float dsum[QG];               // ES: mass of the history block in progress
@@ -295,28 +312,36 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
   put_kpos(kpos[1], mV);
   __syncthreads();
   f32x16_t sa[QG][2], sb[QG][2];
+  float ma[QG], mb[QG];   // lane maxima of the unmasked score tiles
   qk(Ks[0], sa);
+#pragma unroll
+  for (int gq = 0; gq < QG; ++gq) ma[gq] = lane_max(sa[gq]);
   __syncthreads();   // iteration 0 overwrites Ks[0]
 
   // One tile t: softmax of s_cur (scores of tile t) and PV(t); QK(t+1) -> s_nxt.
   // K runs one tile ahead of V: reads K(t+1) and V(t) from LDS, fetches
-  // K(t+2) and V(t+1) from HBM, and maps tile t+3.
-  auto step = [&](int t, f32x16_t (&s_cur)[QG][2], f32x16_t (&s_nxt)[QG][2]) -> bool {
+  // K(t+2) and V(t+1) from HBM (issued first, so they have the whole step to
+  // arrive), and maps tile t+3.  m_cur holds this lane's max over tile t,
+  // taken in the previous step beside its MFMAs; only the lane-half exchange
+  // and the rescale test are left between the barrier and the MFMA block.
+  auto step = [&](int t, f32x16_t (&s_cur)[QG][2], f32x16_t (&s_nxt)[QG][2], float (&m_cur)[QG],
+                  float (&m_nxt)[QG]) -> bool {
+    gather(rk, mK, kreg);
+    gather(rv, mV, vreg);
     // (A) mask, max, rare rescale of the running state
     float msub[QG];
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
-      if (ES ? (t < own_tiles && t >= own_tiles - tpb) : (t >= nfull)) {
+      float mx = m_cur[gq];   // taken beside the MFMAs of the previous step
+      if (ES ? (t < own_tiles && t >= own_tiles - tpb) : (t >= nfull)) {   // masked tile: max again
         const int* kp = kpos[t % 3];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
           for (int e = 0; e < 16; ++e)
             if (kp[rt * 32 + 8 * (e >> 2) + 4 * hf + (e & 3)] > r_[gq]) s_cur[gq][rt][e] = -kInf;
+        mx = lane_max(s_cur[gq]);
       }
-      float mx = __builtin_fmaxf(s_cur[gq][0][0], s_cur[gq][1][0]);
-#pragma unroll
-      for (int e = 1; e < 16; ++e) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s_cur[gq][0][e]), s_cur[gq][1][e]);
       mx = xhalf_max(mx);
       const float mcand = mx * scale_log2;
       const bool need = active[gq] && mcand > m_run[gq] + kRescaleThreshold;
@@ -335,10 +360,8 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
       if constexpr (ES) msub[gq] = active[gq] ? msub[gq] : kInf;   // a stopped row's exponentials are 0
     }
 
-    // (B) straight-line: HBM fetches, next map, QK(t+1) on MFMA beside exp(t), PV(t)
-    gather(rk, mK, kreg);
-    gather(rv, mV, vreg);
-    __builtin_amdgcn_sched_barrier(0);   // keep the HBM fetches at the top of the block
+    // (B) straight-line: next map, QK(t+1) on MFMA beside exp(t), PV(t), max of tile t+1
+    __builtin_amdgcn_sched_barrier(0);
 #if SPOT_PREFILL_SCHED == 1
     __builtin_amdgcn_iglp_opt(0);
 #elif SPOT_PREFILL_SCHED == 2
@@ -380,6 +403,11 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
         for (int gq = 0; gq < QG; ++gq)
           oacc[gq][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[gq], oacc[gq][dt], 0, 0, 0);
       }
+    }
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq) {
+      m_nxt[gq] = lane_max(s_nxt[gq]);
+      asm volatile("" : "+v"(m_nxt[gq]));   // keeps the reduction in this block, beside the MFMAs
     }
 #if SPOT_PREFILL_SCHED == 3
     __builtin_amdgcn_s_setprio(0);
@@ -433,10 +461,10 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
   int t = 0;
   bool go = true;
   for (; go && t + 1 < ntiles; t += 2) {
-    go = step(t, sa, sb);
-    if (go) go = step(t + 1, sb, sa);
+    go = step(t, sa, sb, ma, mb);
+    if (go) go = step(t + 1, sb, sa, mb, ma);
   }
-  if (go && t < ntiles) step(t, sa, sb);
+  if (go && t < ntiles) step(t, sa, sb, ma, mb);
 
 #pragma unroll
   for (int gq = 0; gq < QG; ++gq) {
