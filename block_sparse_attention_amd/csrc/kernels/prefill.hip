@@ -13,10 +13,12 @@
 //   One workgroup = NW waves = NW*32 packed query rows of one (batch, KV
 //   head g, query block i); packed row p is head g*G + p/B, row i*B + p%B,
 //   so the G query heads of a group share every K/V tile (GQA packing).
-//   Key tiles of 64 slots walk the concatenated kept blocks; each slot is
-//   gathered (natural or permuted row) from HBM into registers ahead of use
-//   (K two tiles, V one tile) and written to LDS row-major; the V^T operand
-//   of the PV product is read with the transposing LDS load.
+//   Key tiles of 64 slots walk the concatenated kept blocks; each slot's row
+//   (natural or permuted) is loaded from HBM straight into LDS with 16-byte
+//   buffer-to-LDS loads, one step ahead of use (K for tile t+2 and V for
+//   tile t+1 while tile t is processed), rows unpadded with their 16-byte
+//   chunks XOR-swizzled so the fragment reads stay bank-conflict-free; the
+//   V^T operand of the PV product is read with the transposing LDS load.
 //   S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16, so every
 //   lane owns one query column: row max/sum stay in-lane plus one exchange
 //   between the two lane halves (the gfx950 lane-half swap, no LDS round
@@ -28,6 +30,8 @@
 //   pinned to one XCD so its K/V stay in that XCD's L2.
 //
 // prefill_rows_kernel (fp32 or bf16, latency path): one wave per query row.
+#include <type_traits>
+
 #include "../launch.h"
 #include "common.h"
 
@@ -114,26 +118,43 @@ constexpr int kListCap = SPOT_PREFILL_LIST_CAP;
 // softmax mass with the mass accumulated so far (that block included) and
 // stops taking further blocks once it is below tau.  A stopped row adds
 // nothing more; the workgroup leaves the loop when all its rows have stopped.
-template <int D, int NW, int QG, bool PERM, bool ES>
+// LLDS: every kept list of the launch fits the LDS copy (the number of blocks
+// per sequence is at most its capacity), so list entries are LDS reads; else
+// they are read from HBM.
+template <int D, int NW, int QG, bool PERM, bool ES, bool LLDS>
 __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(PrefillArgs a, int chunks,
                                                                                float scale_log2) {
   constexpr int NT = NW * 64;
   constexpr int ROWS = NW * 32 * QG;                // packed query rows per workgroup
-  // Row strides (elements): K rows start 4 banks apart (conflict-free 16-byte
-  // fragment reads); V rows start 16 banks apart, so the four rows of a
-  // transposing read cover all 64 banks.
-  constexpr int KLD = D + 8;
-  constexpr int VLD = D + 32;
+  // K and V tiles: unpadded rows filled by buffer-to-LDS loads (lane l of a
+  // load stores its 16 bytes at the load's base + 16 l), so the 16-byte chunk
+  // c of tile row r sits in slot c ^ swz(r) of that row: the 16 rows of a
+  // K fragment read and the 4 rows x 4 chunks of a transposing V read each
+  // land on distinct bank groups.
+  constexpr int RB = D * 2;                         // bytes per row
   constexpr int CPR = D / 8;                        // 16-byte chunks per row
-  constexpr int CH = (kKT * CPR + NT - 1) / NT;     // chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKT * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKT * VLD];
+  constexpr int CH = kKT * CPR / NT;                // chunks per thread per tile
+  static_assert(CH * NT == kKT * CPR, "every thread loads whole chunks of every tile");
+  // the two buffers of each are separate arrays, so the compiler can tell
+  // the buffer being read from the one the loads are filling
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[kKT * D], Ks1[kKT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs0[kKT * D], Vs1[kKT * D];
+  auto Ks = [&](auto b) -> uint16_t* {
+    if constexpr (decltype(b)::value == 0) return Ks0;
+    else return Ks1;
+  };
+  auto Vs = [&](auto b) -> uint16_t* {
+    if constexpr (decltype(b)::value == 0) return Vs0;
+    else return Vs1;
+  };
   __shared__ int kpos[3][kKT];
-  // early stopping always stages its (reordered) list; the top-p kernel only up to kListCap entries
+  // early stopping always stages its (reordered) list; the top-p kernel when every list of the launch fits
   constexpr int LCAP = ES ? (kListCap > kEsMaxBlocks ? kListCap : kEsMaxBlocks) : kListCap;
   __shared__ int s_list[LCAP > 0 ? LCAP : 1];
   __shared__ int s_act[2][NW];   // early stop: per-wave "a row is still taking blocks", by tile parity
   static_assert(!ES || LCAP >= kEsMaxBlocks, "early stopping stages its visiting list in LDS");
+  static_assert(!ES || LLDS, "early stopping reads its list from LDS");
+  static_assert(!LLDS || LCAP > 0, "no LDS copy of the list");
 
   const int pairs = a.batch * a.hkv;
   int pair, i, chunk;
@@ -168,7 +189,6 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
   const int lgB = 31 - __builtin_clz(B);
   const int seg_start = ((PERM || ES) && a.segment > 0) ? ((i * B) / a.segment) * a.segment : 0;
   int nkept, own_tiles = 0;
-  const int* lst;
   if constexpr (ES) {
     // own segment's blocks ascending, then the history blocks in visiting
     // order (with history maps: the runs of the map in order, all of them)
@@ -177,14 +197,18 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
     nkept = n_own + (a.es_hmap ? sblk : min(max(a.cnt[row_id], 0), sblk));   // at most the blocks before the segment
     for (int k = tid; k < nkept; k += NT)
       s_list[k] = k < n_own ? sblk + k : (a.es_hmap ? k - n_own : glist[k - n_own]);
-    lst = s_list;
     own_tiles = (n_own * B) / kKT;
   } else {
     nkept = a.cnt[row_id];
-    if constexpr (LCAP > 0)
-      for (int k = tid; k < min(nkept, LCAP); k += NT) s_list[k] = glist[k];
-    lst = (LCAP > 0 && nkept <= LCAP) ? s_list : glist;
+    if constexpr (LLDS)
+      for (int k = tid; k < nkept; k += NT) s_list[k] = glist[k];
   }
+  // typed reads (LDS or global), never a generic pointer: a flat read could
+  // alias the LDS the tile loads are filling and would wait for them
+  auto list_at = [&](int k) -> int {
+    if constexpr (LLDS) return s_list[k];
+    else return glist[k];
+  };
   const int32_t* permg =
       PERM ? a.perm + (ES && a.es_hmap ? size_t(pair) * a.nseg + seg_start / max(a.segment, 1) : size_t(pair)) * L
            : nullptr;
@@ -206,6 +230,9 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
     uint32_t off[CH];
     int lim[CH];
   };
+  auto swz = [](int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  };
   auto map_tile = [&](int t, RowMap& m) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -213,7 +240,7 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
       const int s = t * kKT + cid / CPR;
       const int bi = s >> lgB;
       const bool inl = bi < nkept && cid < kKT * CPR;
-      const int base = lst[inl ? bi : 0] << lgB;
+      const int base = list_at(inl ? bi : 0) << lgB;
       const int pos = base + (s & (B - 1));
       const bool valid = inl && unsigned(pos) < unsigned(L);
       const bool hist = base < seg_start;
@@ -222,36 +249,51 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
         const int pp = permg[valid ? pos : 0];
         phys = hist ? pp : pos;
       }
-      m.off[c] = valid ? uint32_t(phys) * (D * 2) + uint32_t(cid % CPR) * 16 : 0x80000000u;
+      // the lane fills slot cid % CPR of tile row cid / CPR: it loads the chunk that slot holds
+      m.off[c] = valid ? uint32_t(phys) * RB + uint32_t(((cid % CPR) ^ swz(cid / CPR)) << 4) : 0x80000000u;
       m.lim[c] = valid ? (hist ? -1 : pos) : 0x7fffffff;
     }
   };
-  auto gather = [&](const __amdgpu_buffer_rsrc_t& rs, const RowMap& m, uint4 (&reg)[CH]) {
+  // HBM -> LDS without registers: the wave's 64 lanes of chunk round c fill
+  // the 1 KiB that starts at chunk wv * 64 + c * NT of the tile
+  auto gather = [&](const __amdgpu_buffer_rsrc_t& rs, const RowMap& m, uint16_t* tile) {
 #pragma unroll
     for (int c = 0; c < CH; ++c)
-      reg[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, m.off[c], 0, 0));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(tile + (wv * 64 + c * NT) * 8), 16, uint32_t(m.off[c]), 0, 0, 0);
   };
-  auto put = [&](uint16_t* dst, int ld, const uint4 (&reg)[CH]) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int cid = tid + c * NT;
-      if (cid < kKT * CPR) *reinterpret_cast<uint4*>(&dst[(cid / CPR) * ld + (cid % CPR) * 8]) = reg[c];
-    }
-  };
+  auto loads_landed = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0): this wave's tile loads are in LDS
   auto put_kpos = [&](int* kp, const RowMap& m) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int cid = tid + c * NT;
-      if (cid < kKT * CPR && cid % CPR == 0) kp[cid / CPR] = m.lim[c];
+      if (cid % CPR == 0) kp[cid / CPR] = m.lim[c];
     }
   };
 
   // S^T tiles = K_tile Q^T (64 keys x 32 queries per group); each K fragment
   // read from LDS feeds the QG groups
+  // byte offsets of this lane's K fragment (row ql, chunk 2 ks + hf) and V
+  // transposing reads (row vrow (+8), columns dt * 32 + vcol ..+3) in a tile
+  uint32_t koff[D / 16], voff[D / 32][2];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = ql * RB + (((2 * ks + hf) ^ swz(ql)) << 4);
+  const int jl = lane & 15, g16 = lane >> 4;
+  const int vrow = 4 * (g16 >> 1) + (jl >> 2);          // key row within a 16-key step
+  const int vcol = 16 * (g16 & 1) + 4 * (jl & 3);       // column within a 32-wide d tile
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      voff[dt][h] = (vrow + 8 * h) * RB + (((dt * 4 + (vcol >> 3)) ^ swz(vrow + 8 * h)) << 4) + (vcol & 7) * 2;
+  auto kfrag = [&](const uint16_t* kt, int rt, int ks) {
+    return *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const char*>(kt) + rt * 32 * RB + koff[ks]);
+  };
+
   auto qk = [&](const uint16_t* kt, f32x16_t (&s)[QG][2]) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(&kt[(rt * 32 + ql) * KLD + hf * 8]);
+      const bf16x8_t k0 = kfrag(kt, rt, 0);
 #pragma unroll
       for (int gq = 0; gq < QG; ++gq)
         s[gq][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[gq][0], f32x16_t{}, 0, 0, 0);
@@ -260,7 +302,7 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
     for (int ks = 1; ks < D / 16; ++ks)
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&kt[(rt * 32 + ql) * KLD + ks * 16 + hf * 8]);
+        const bf16x8_t kf = kfrag(kt, rt, ks);
 #pragma unroll
         for (int gq = 0; gq < QG; ++gq)
           s[gq][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[gq][ks], s[gq][rt], 0, 0, 0);
@@ -291,32 +333,26 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
     active[gq] = true;
   }
   const int tpb = B / kKT;   // ES: tiles per block (block >= 64)
-  const int jl = lane & 15, g16 = lane >> 4;
-  const int vrow = 4 * (g16 >> 1) + (jl >> 2);          // key row within a 16-key step
-  const int vcol = 16 * (g16 & 1) + 4 * (jl & 3);       // column within a 32-wide d tile
 
   __syncthreads();   // kept list staged
 
   RowMap mV, mK, mN;
-  uint4 kreg[CH], vreg[CH];
   map_tile(0, mN);
-  gather(rk, mN, kreg);
-  gather(rv, mN, vreg);
+  gather(rk, mN, Ks0);
+  gather(rv, mN, Vs0);
   map_tile(1, mV);
-  put(Ks[0], KLD, kreg);
-  put(Vs[0], VLD, vreg);
   put_kpos(kpos[0], mN);
-  gather(rk, mV, kreg);
+  gather(rk, mV, Ks1);
   map_tile(2, mK);
-  put(Ks[1], KLD, kreg);
   put_kpos(kpos[1], mV);
+  loads_landed();
   __syncthreads();
   f32x16_t sa[QG][2], sb[QG][2];
   float ma[QG], mb[QG];   // lane maxima of the unmasked score tiles
-  qk(Ks[0], sa);
+  qk(Ks0, sa);
 #pragma unroll
   for (int gq = 0; gq < QG; ++gq) ma[gq] = lane_max(sa[gq]);
-  __syncthreads();   // iteration 0 overwrites Ks[0]
+  __syncthreads();   // iteration 0 loads into Ks0
 
   // One tile t: softmax of s_cur (scores of tile t) and PV(t); QK(t+1) -> s_nxt.
   // K runs one tile ahead of V: reads K(t+1) and V(t) from LDS, fetches
@@ -324,10 +360,13 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
   // arrive), and maps tile t+3.  m_cur holds this lane's max over tile t,
   // taken in the previous step beside its MFMAs; only the lane-half exchange
   // and the rescale test are left between the barrier and the MFMA block.
-  auto step = [&](int t, f32x16_t (&s_cur)[QG][2], f32x16_t (&s_nxt)[QG][2], float (&m_cur)[QG],
+  auto step = [&](auto parity, int t, f32x16_t (&s_cur)[QG][2], f32x16_t (&s_nxt)[QG][2], float (&m_cur)[QG],
                   float (&m_nxt)[QG]) -> bool {
-    gather(rk, mK, kreg);
-    gather(rv, mV, vreg);
+    constexpr int P = decltype(parity)::value;   // t & 1
+    using BP = std::integral_constant<int, P>;
+    using BQ = std::integral_constant<int, P ^ 1>;
+    gather(rk, mK, Ks(BP{}));   // K(t+2) into the buffer QK(t) read in the previous step
+    gather(rv, mV, Vs(BQ{}));   // V(t+1) into the buffer PV(t-1) read
     // (A) mask, max, rare rescale of the running state
     float msub[QG];
 #pragma unroll
@@ -370,8 +409,8 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
     __builtin_amdgcn_s_setprio(1);
 #endif
     map_tile(t + 3, mN);
-    qk(Ks[(t + 1) & 1], s_nxt);   // stale but in bounds on the last tile
-    const uint16_t* vt = Vs[t & 1];
+    qk(Ks(BQ{}), s_nxt);   // stale but in bounds on the last tile
+    const char* vt = reinterpret_cast<const char*>(Vs(BP{}));
     float rs[QG];   // row sums of the bf16-rounded P that enters the PV product
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) rs[gq] = 0.f;
@@ -395,9 +434,8 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
       }
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const uint16_t* base = &vt[(kk * 16 + vrow) * VLD + dt * 32 + vcol];
-        const uint2 lo = lds_read_tr16(base);              // keys kk*16 + 4*hf + 0..3
-        const uint2 hi = lds_read_tr16(base + 8 * VLD);    // keys kk*16 + 8 + 4*hf + 0..3
+        const uint2 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(vt + kk * 16 * RB + voff[dt][0]));  // keys kk*16 + 4*hf + 0..3
+        const uint2 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(vt + kk * 16 * RB + voff[dt][1]));  // keys kk*16 + 8 + 4*hf + 0..3
         const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
         for (int gq = 0; gq < QG; ++gq)
@@ -439,10 +477,9 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
       for (int gq = 0; gq < QG; ++gq) l_run[gq] += rs[gq];
     }
 
-    // (C) stage K(t+2) and V(t+1)
-    put(Ks[t & 1], KLD, kreg);
-    put(Vs[(t + 1) & 1], VLD, vreg);
+    // (C) tile t+2's mask limits; K(t+2) and V(t+1) in LDS before the barrier
     put_kpos(kpos[(t + 2) % 3], mK);
+    loads_landed();
     __syncthreads();
     mV = mK;
     mK = mN;
@@ -461,10 +498,10 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
   int t = 0;
   bool go = true;
   for (; go && t + 1 < ntiles; t += 2) {
-    go = step(t, sa, sb, ma, mb);
-    if (go) go = step(t + 1, sb, sa, mb, ma);
+    go = step(std::integral_constant<int, 0>{}, t, sa, sb, ma, mb);
+    if (go) go = step(std::integral_constant<int, 1>{}, t + 1, sb, sa, mb, ma);
   }
-  if (go && t < ntiles) step(t, sa, sb, ma, mb);
+  if (go && t < ntiles) step(std::integral_constant<int, 0>{}, t, sa, sb, ma, mb);
 
 #pragma unroll
   for (int gq = 0; gq < QG; ++gq) {
@@ -582,15 +619,21 @@ static hipError_t launch_mfma(const PrefillArgs& a, hipStream_t s, float scale_l
   const int chunks = (G * a.block + NW * 32 * QG - 1) / (NW * 32 * QG);
   const long long units = (long long)a.batch * a.hkv * a.nb * chunks;
   const dim3 grid{unsigned(units)};
+  const bool list_lds = kListCap > 0 && a.nb <= kListCap;   // a kept list holds at most nb blocks
   if (a.es) {
     if (a.perm)
-      prefill_mfma_kernel<D, NW, QG, true, true><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
+      prefill_mfma_kernel<D, NW, QG, true, true, true><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
     else
-      prefill_mfma_kernel<D, NW, QG, false, true><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
+      prefill_mfma_kernel<D, NW, QG, false, true, true><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
   } else if (a.perm) {
-    prefill_mfma_kernel<D, NW, QG, true, false><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
+    if (list_lds)
+      prefill_mfma_kernel<D, NW, QG, true, false, true><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
+    else
+      prefill_mfma_kernel<D, NW, QG, true, false, false><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
+  } else if (list_lds) {
+    prefill_mfma_kernel<D, NW, QG, false, false, true><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
   } else {
-    prefill_mfma_kernel<D, NW, QG, false, false><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
+    prefill_mfma_kernel<D, NW, QG, false, false, false><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
   }
   return hipGetLastError();
 }

@@ -166,6 +166,58 @@ def test_prefill_attention_with_permutation_on_oracle_lists(gpu):
     assert err <= P.BF16_ATOL
 
 
+LONG_LIST_CASES = [
+    dict(d=64, hq=2, perm=False),
+    dict(d=128, hq=4, perm=True),
+]
+
+
+@pytest.mark.parametrize("case", LONG_LIST_CASES, ids=lambda c: f"d{c['d']}-perm{int(c['perm'])}")
+def test_prefill_attention_lists_longer_than_lds_copy(gpu, case):
+    """2055 blocks per sequence (block 16, ragged last block): more than the
+    kept-list entries the kernel copies to LDS (2048), so its lists are read
+    from HBM.  Kept lists are drawn on the host (sink, about 2% of the earlier
+    blocks, diagonal); the oracle evaluates sampled query blocks on both
+    sides of the 2048 boundary."""
+    block, nb = 16, 2055
+    L = nb * block - 7
+    segment = 4096 if case["perm"] else 0
+    cfg = I.small_prefill(name="long-lists", L=L, hq=case["hq"], hkv=1, d=case["d"], block=block, top_p=0.9,
+                          seed=53, segment=segment)
+    host, dev = upload_prefill(cfg, gpu)
+    q, k, v = host
+    perm = None
+    dperm = None
+    if case["perm"]:
+        perm, _ = oracle.key_permutation(q[0], k[0], block, segment, 1 / math.sqrt(cfg.d))
+        dperm = torch.from_numpy(perm[None].astype(np.int32)).to(gpu)
+    rng = np.random.default_rng(53)
+    idx = np.full((1, 1, nb, nb), -1, np.int32)
+    cnt = np.zeros((1, 1, nb), np.int32)
+    kept = [[None] * nb]
+    for i in range(nb):
+        mid = np.flatnonzero(rng.random(max(i - 1, 0)) < 0.02) + 1 if i > 1 else np.zeros(0, np.int64)
+        kl = np.unique(np.concatenate([[0], mid, [i]])).astype(np.int64)
+        kept[0][i] = kl
+        idx[0, 0, i, :len(kl)] = kl
+        cnt[0, 0, i] = len(kl)
+    desc = B.prefill_desc(dev[0], dev[1], block, cfg.top_p, segment=segment)
+    o = torch.full_like(dev[0], float("nan"))
+    lse = torch.full((1, cfg.hq, L), float("nan"), device=gpu)
+    B.spot_sparse_attn_prefill(desc, dev[0], dev[1], dev[2], dperm, torch.from_numpy(idx).to(gpu),
+                               torch.from_numpy(cnt).to(gpu), o, lse)
+    torch.cuda.synchronize()
+    qb = [0, 1, 700, 2046, 2047, 2048, 2053, 2054]
+    o_ref, lse_ref = oracle.attend_prefill(q[0], k[0], v[0], kept, block, 1 / math.sqrt(cfg.d), segment=segment,
+                                           perm=perm, qblocks=qb)
+    rows = np.concatenate([np.arange(i * block, min((i + 1) * block, L)) for i in qb])
+    err = P.max_abs(o.float().cpu().numpy()[0][:, rows], o_ref[:, rows])
+    err_lse = P.max_abs(lse.cpu().numpy()[0][:, rows], lse_ref[:, rows])
+    log("long lists", case, "max|dO|", err, "max|dLSE|", err_lse)
+    assert err <= P.BF16_ATOL
+    assert err_lse <= 1e-2
+
+
 # ----------------------------------------------------------------- scores and selection kernels
 def test_select_kernel_on_oracle_scores(gpu):
     """Selection kernel alone: both sides see the same fp32 scores."""
