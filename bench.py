@@ -196,7 +196,8 @@ def bench_prefill(args, torch, B, I, data, score_kind=None, top_p=None):
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
                 "traffic": load_traffic(attn_file, f"prefill_mfma_kernel@{cfg.name}"),
-                "kernel": f"prefill_mfma_kernel<{cfg.d},8,1,{'true' if cfg.segment else 'false'},false>",
+                "kernel": f"prefill_mfma_kernel<{cfg.d},8,1,{'true' if cfg.segment else 'false'},false,"
+                          f"{'true' if cfg.nb <= 2048 else 'false'}>",
                 "flop_per_launch": flops, "avg_launch_ms": round(ms_attn, 4)}
     else:   # the fp32 row kernel on a 256-token input is launch-latency bound
         roof = {"bound": "latency", "achieved": round(achieved, 4), "peak": None, "unit": "TFLOP/s", "frac": None,
@@ -401,7 +402,7 @@ def bench_early_stop(args, torch, B, I):
         flop_per_step=flops,
         roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                   "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                  "kernel": "prefill_mfma_kernel<128,8,1,true,true> (early stop)", "avg_launch_ms": round(ms_attn, 4),
+                  "kernel": "prefill_mfma_kernel<128,8,1,true,true,true> (early stop)", "avg_launch_ms": round(ms_attn, 4),
                   "traffic": load_traffic(os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "kernels",
                                                        "prefill.hip"),
                                           f"prefill_mfma_kernel_early_stop@{cfg.name}"),
@@ -473,7 +474,7 @@ def bench_history_map(args, torch, B, I):
         flop_per_step=flops,
         roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                   "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                  "kernel": "prefill_mfma_kernel<128,8,1,true,true> (early stop, history maps)",
+                  "kernel": "prefill_mfma_kernel<128,8,1,true,true,true> (early stop, history maps)",
                   "avg_launch_ms": round(ms_attn, 4)},
     )
 

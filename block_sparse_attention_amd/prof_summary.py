@@ -32,9 +32,9 @@ COPY_BYTES = 1 << 30
 # heavy-hitter prefill), so "first" takes the first `--steps` launches of a
 # kernel that several parts use, "all" every launch.
 TRACKED = {
-    "prefill_mfma_kernel<128, 8, 1, false, false>": ("prefill.hip", "prefill_mfma_kernel@gqa-bf16-L8192", "all"),
-    "prefill_mfma_kernel<128, 8, 1, true, true>": ("prefill.hip",
-                                                   "prefill_mfma_kernel_early_stop@heavy-perm-bf16-L32768", "all"),
+    "prefill_mfma_kernel<128, 8, 1, false, false, true>": ("prefill.hip", "prefill_mfma_kernel@gqa-bf16-L8192", "all"),
+    "prefill_mfma_kernel<128, 8, 1, true, true, true>": ("prefill.hip",
+                                                         "prefill_mfma_kernel_early_stop@heavy-perm-bf16-L32768", "all"),
     "decode_split_kernel<128, 4>": ("decode.hip", "decode_split_kernel@decode-b16-T131072", "first"),
     "indexer_score_kernel<": ("score.hip", "indexer_score_kernel@decode-b16-T131072", "all"),
     "indexer_score_mxfp4_kernel": ("score.hip", "indexer_score_mxfp4_kernel@decode-b16-T131072", "all"),
