@@ -262,7 +262,9 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (__attribute__((address_space(3))) void*)(tile + (wv * 64 + c * NT) * 8), 16, uint32_t(m.off[c]), 0, 0, 0);
   };
-  auto loads_landed = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0): this wave's tile loads are in LDS
+  // s_waitcnt vmcnt(0) (immediate fields: vmcnt 3:0, expcnt 6:4, lgkmcnt 11:8;
+  // the last two at their maxima): this wave's tile loads are in LDS
+  auto loads_landed = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
   auto put_kpos = [&](int* kp, const RowMap& m) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -271,8 +273,6 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
     }
   };
 
-  // S^T tiles = K_tile Q^T (64 keys x 32 queries per group); each K fragment
-  // read from LDS feeds the QG groups
   // byte offsets of this lane's K fragment (row ql, chunk 2 ks + hf) and V
   // transposing reads (row vrow (+8), columns dt * 32 + vcol ..+3) in a tile
   uint32_t koff[D / 16], voff[D / 32][2];
@@ -290,6 +290,8 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
     return *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const char*>(kt) + rt * 32 * RB + koff[ks]);
   };
 
+  // S^T tiles = K_tile Q^T (64 keys x 32 queries per group); each K fragment
+  // read from LDS feeds the QG groups
   auto qk = [&](const uint16_t* kt, f32x16_t (&s)[QG][2]) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
