@@ -105,7 +105,10 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 #define SPOT_PREFILL_QG 1           // groups of 32 query rows per wave (2: each LDS fragment feeds 2 MFMAs)
 #endif
 #ifndef SPOT_PREFILL_SCHED
-#define SPOT_PREFILL_SCHED 3        // 0: compiler default; 1, 2: iglp strategy 0 / 1; 3: raised wave priority over the MFMA block
+#define SPOT_PREFILL_SCHED 3        // 0: compiler default; 1: iglp strategy 0; 3: raised wave priority over the MFMA block
+#endif
+#if SPOT_PREFILL_SCHED != 0 && SPOT_PREFILL_SCHED != 1 && SPOT_PREFILL_SCHED != 3
+#error "SPOT_PREFILL_SCHED: 0, 1 or 3 (iglp strategy 1 runs the compiler out of memory on this kernel)"
 #endif
 #ifndef SPOT_PREFILL_LIST_CAP
 #define SPOT_PREFILL_LIST_CAP 2048  // kept-list entries staged in LDS (0: read from HBM)
@@ -405,8 +408,6 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
     __builtin_amdgcn_sched_barrier(0);
 #if SPOT_PREFILL_SCHED == 1
     __builtin_amdgcn_iglp_opt(0);
-#elif SPOT_PREFILL_SCHED == 2
-    __builtin_amdgcn_iglp_opt(1);
 #elif SPOT_PREFILL_SCHED == 3
     __builtin_amdgcn_s_setprio(1);
 #endif
