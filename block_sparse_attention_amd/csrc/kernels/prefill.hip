@@ -622,22 +622,26 @@ static hipError_t launch_mfma(const PrefillArgs& a, hipStream_t s, float scale_l
   const int chunks = (G * a.block + NW * 32 * QG - 1) / (NW * 32 * QG);
   const long long units = (long long)a.batch * a.hkv * a.nb * chunks;
   const dim3 grid{unsigned(units)};
-  const bool list_lds = kListCap > 0 && a.nb <= kListCap;   // a kept list holds at most nb blocks
   if (a.es) {
     if (a.perm)
       prefill_mfma_kernel<D, NW, QG, true, true, true><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
     else
       prefill_mfma_kernel<D, NW, QG, false, true, true><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
-  } else if (a.perm) {
-    if (list_lds)
-      prefill_mfma_kernel<D, NW, QG, true, false, true><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
-    else
-      prefill_mfma_kernel<D, NW, QG, true, false, false><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
-  } else if (list_lds) {
-    prefill_mfma_kernel<D, NW, QG, false, false, true><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
-  } else {
-    prefill_mfma_kernel<D, NW, QG, false, false, false><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
+    return hipGetLastError();
   }
+  if constexpr (kListCap > 0) {
+    if (a.nb <= kListCap) {   // a kept list holds at most nb blocks: every list fits the LDS copy
+      if (a.perm)
+        prefill_mfma_kernel<D, NW, QG, true, false, true><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
+      else
+        prefill_mfma_kernel<D, NW, QG, false, false, true><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
+      return hipGetLastError();
+    }
+  }
+  if (a.perm)
+    prefill_mfma_kernel<D, NW, QG, true, false, false><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
+  else
+    prefill_mfma_kernel<D, NW, QG, false, false, false><<<grid, NW * 64, 0, s>>>(a, chunks, scale_log2);
   return hipGetLastError();
 }
 
