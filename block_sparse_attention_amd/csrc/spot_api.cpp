@@ -99,6 +99,15 @@ int check_aligned16(const char* what, const void* p) {
   return SPOT_OK;
 }
 
+// The bf16 attention kernels read q in 16-byte pieces and k, v with 16-byte
+// buffer-to-LDS loads, and write o in 8-byte pieces.
+int check_mfma_operands(const void* q, const void* k, const void* v, const void* o) {
+  int st;
+  if ((st = check_aligned16("q", q)) || (st = check_aligned16("k", k)) || (st = check_aligned16("v", v))) return st;
+  if (reinterpret_cast<uintptr_t>(o) & 7u) return fail(SPOT_ERR_INVALID, "o must be 8-byte aligned");
+  return SPOT_OK;
+}
+
 int check_workspace(size_t need, const void* ws, size_t have) {
   if (need == 0) return SPOT_OK;
   if (!ws || have < need) return fail(SPOT_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? have : size_t(0), need);
@@ -264,6 +273,7 @@ int spot_sparse_attn_prefill(const spot_desc* desc, const void* q, const void* k
   if (perm && desc->segment <= 0) return fail(SPOT_ERR_INVALID, "perm given but segment is 0");
   const int nb = int(ceil_div64(desc->q_len, desc->block));
   if (desc->dtype == SPOT_BF16) {
+    if ((st = check_mfma_operands(q, k, v, o))) return st;
     const int G = desc->hq / desc->hkv;
     const long long units = (long long)desc->batch * desc->hkv * nb * ((G * desc->block + 255) / 256);
     if (units > 0x7fffffffLL) return fail(SPOT_ERR_UNSUPPORTED, "too many work units");
@@ -349,6 +359,7 @@ int spot_sparse_attn_prefill_history_map(const spot_desc* desc, float tau, const
   if (st) return st;
   if ((st = check_prefill_shape(desc))) return st;
   if (!q || !k || !v || !hmap || !o) return fail(SPOT_ERR_INVALID, "q, k, v, hmap and o are required");
+  if ((st = check_mfma_operands(q, k, v, o))) return st;
   if (!std::isfinite(tau) || tau < 0.f) return fail(SPOT_ERR_INVALID, "tau must be finite and >= 0");
   if (desc->segment <= 0) return fail(SPOT_ERR_INVALID, "segment must be > 0");
   if (desc->dtype != SPOT_BF16) return fail(SPOT_ERR_UNSUPPORTED, "early stopping supports bf16 only");
@@ -393,6 +404,7 @@ int spot_sparse_attn_prefill_early_stop(const spot_desc* desc, float tau, const 
   if (st) return st;
   if ((st = check_prefill_shape(desc))) return st;
   if (!q || !k || !v || !order || !cnt || !o) return fail(SPOT_ERR_INVALID, "q, k, v, order, cnt and o are required");
+  if ((st = check_mfma_operands(q, k, v, o))) return st;
   if (!std::isfinite(tau) || tau < 0.f) return fail(SPOT_ERR_INVALID, "tau must be finite and >= 0");
   if (desc->segment <= 0) return fail(SPOT_ERR_INVALID, "segment must be > 0");
   if (desc->dtype != SPOT_BF16) return fail(SPOT_ERR_UNSUPPORTED, "early stopping supports bf16 only");

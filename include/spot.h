@@ -178,7 +178,9 @@ int spot_select_topp(const spot_desc* desc, const float* scores, int32_t* idx, i
  * of the query's own segment (or every block when perm == NULL) contributes
  * its natural rows t <= r.  lse (nullable) receives ln(sum exp(logits)).
  * Kept lists must be ascending, with block ids < nk; every row must see at
- * least one key (guaranteed when the diagonal or block 0 is kept).
+ * least one key (guaranteed when the diagonal or block 0 is kept).  bf16:
+ * q, k and v 16-byte aligned, o 8-byte aligned (the kernel's vector loads
+ * and stores; SPOT_ERR_INVALID otherwise).
  */
 int spot_sparse_attn_prefill(const spot_desc* desc, const void* q, const void* k, const void* v,
                              const int32_t* perm, const int32_t* idx, const int32_t* cnt, void* o,
@@ -285,7 +287,8 @@ int spot_order_history(const spot_desc* desc, const float* scores, int32_t* orde
  * comparison runs on the kernel's fp32 sums, so a row whose ratio lies
  * within rounding of tau may stop one block earlier or later than an exact
  * evaluation.  Requires dtype bf16, d in {64, 128}, block in {64, 128},
- * segment > 0 (a multiple of block), nb <= 2048, tau finite and >= 0.
+ * segment > 0 (a multiple of block), nb <= 2048, tau finite and >= 0, and
+ * the alignment of q, k, v and o that spot_sparse_attn_prefill needs in bf16.
  * No workspace.
  */
 int spot_sparse_attn_prefill_early_stop(const spot_desc* desc, float tau, const void* q, const void* k,

@@ -116,6 +116,8 @@ def test_null_and_missing_arguments():
     assert call_prefill(_prefill(), v=None) == B.SPOT_ERR_INVALID
     assert call_prefill(_prefill(), perm=FAKE) == B.SPOT_ERR_INVALID
     assert call_prefill(_prefill(), o=None) == B.SPOT_ERR_INVALID
+    for kw in (dict(q=FAKE + 8), dict(k=FAKE + 4), dict(v=FAKE + 2), dict(o=FAKE + 4)):   # bf16: 16-byte q/k/v, 8-byte o
+        assert call_prefill(_prefill(), **kw) == B.SPOT_ERR_INVALID, kw
     assert call_select(_prefill(), cnt=None) == B.SPOT_ERR_INVALID
 
 
@@ -189,6 +191,8 @@ def test_early_stop_validation():
     assert call_es(_prefill(segment=256), tau=float("inf")) == B.SPOT_ERR_INVALID
     assert call_es(_prefill(segment=256), order=None) == B.SPOT_ERR_INVALID
     assert call_es(_prefill(segment=256), o=None) == B.SPOT_ERR_INVALID
+    for kw in (dict(q=FAKE + 8), dict(k=FAKE + 4), dict(v=FAKE + 2), dict(o=FAKE + 4)):
+        assert call_es(_prefill(segment=256), **kw) == B.SPOT_ERR_INVALID, kw
     assert call_es(_prefill(segment=256, dtype=B.SPOT_F32)) == B.SPOT_ERR_UNSUPPORTED
     assert call_es(_prefill(segment=256, block=32)) == B.SPOT_ERR_UNSUPPORTED
     assert call_es(_prefill(segment=256, q_len=64 * 3000, kv_len=64 * 3000)) == B.SPOT_ERR_UNSUPPORTED
@@ -250,8 +254,8 @@ def test_history_map_validation():
     def hm(d, q=FAKE, k=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
         return lib.spot_history_map(ctypes.byref(d), q, k, out, ws, ws_bytes, None)
 
-    def att(d, tau=0.01, hmap=FAKE, o=FAKE):
-        return lib.spot_sparse_attn_prefill_history_map(ctypes.byref(d), tau, FAKE, FAKE, FAKE, hmap, o, None, None,
+    def att(d, tau=0.01, hmap=FAKE, o=FAKE, q=FAKE, k=FAKE, v=FAKE):
+        return lib.spot_sparse_attn_prefill_history_map(ctypes.byref(d), tau, q, k, v, hmap, o, None, None,
                                                          None, 0, None)
 
     assert hm(_prefill(segment=0)) == B.SPOT_ERR_INVALID
@@ -265,4 +269,6 @@ def test_history_map_validation():
     assert att(_prefill(segment=0)) == B.SPOT_ERR_INVALID
     assert att(_prefill(segment=256), hmap=None) == B.SPOT_ERR_INVALID
     assert att(_prefill(segment=256), tau=-1.0) == B.SPOT_ERR_INVALID
+    for kw in (dict(q=FAKE + 8), dict(k=FAKE + 4), dict(v=FAKE + 2), dict(o=FAKE + 4)):
+        assert att(_prefill(segment=256), **kw) == B.SPOT_ERR_INVALID, kw
     assert att(_prefill(segment=256, block=16)) == B.SPOT_ERR_UNSUPPORTED
