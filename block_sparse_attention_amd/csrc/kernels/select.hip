@@ -29,6 +29,7 @@ constexpr int kSelMaxPerThread = 16;   // candidates per thread (16384 / 1024)
 #endif
 constexpr int kSelTargetPerThread = SPOT_SELECT_PER_THREAD;   // launch as few threads as keep at most this many per thread
 static_assert(kSelTargetPerThread <= kSelMaxPerThread, "per-thread runs are register arrays");
+static_assert(kSelMaxPerThread % 4 == 0, "runs are loaded in 16-byte groups");
 constexpr int kSortMax = 2048;         // candidates sorted exactly in LDS
 constexpr int kRankReads = 512;        // rank by counting while each thread compares at most this many keys
 constexpr int kRankMax = 512;          // ... which bounds the set to 512 candidates (nthr <= 1024)
@@ -279,10 +280,30 @@ __global__ __launch_bounds__(1024) void select_topp_kernel(SelectArgs a) {
   uint32_t key[kSelMaxPerThread];
   double ex[kSelMaxPerThread];
   float sv[kSelMaxPerThread];
+  // Every load in flight before any is used.  When the runs are whole
+  // 16-byte groups of a 16-byte aligned row, 16-byte buffer loads: a wave's
+  // 4-byte loads of contiguous runs touch one 64-byte segment per lane and
+  // instruction, which the vector cache serves a segment per cycle (with 16
+  // candidates per thread that alone took 3 of the 15 us of a decode row).
+  // Reads past the row return 0 (they belong to no candidate).
+  if ((per & 3) == 0 && (nk & 3) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15u) == 0) {
+    const __amdgpu_buffer_rsrc_t rrow =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(srow), 0, nk * 4, 0x00020000);
 #pragma unroll
-  for (int e = 0; e < kSelMaxPerThread; ++e) {   // every load in flight before any is used
-    const int c = c0 + e;
-    sv[e] = srow[(e < per && c < n) ? c : 0];
+    for (int j = 0; j < kSelMaxPerThread / 4; ++j) {
+      const uint32_t off = (4 * j < per) ? uint32_t(c0 + 4 * j) * 4u : 0x80000000u;
+      const float4 v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rrow, off, 0, 0));
+      sv[4 * j] = v.x;
+      sv[4 * j + 1] = v.y;
+      sv[4 * j + 2] = v.z;
+      sv[4 * j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kSelMaxPerThread; ++e) {
+      const int c = c0 + e;
+      sv[e] = srow[(e < per && c < n) ? c : 0];
+    }
   }
   uint32_t resid = 0, forcedm = 0;   // bit masks over the run
   float smax = -kInf;
