@@ -47,6 +47,7 @@ template <int D, int G>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a, float scale_log2) {
   constexpr int EPL = D / 16;           // elements per lane
   constexpr int KS = kDecThreads / 16;  // key-slot streams per workgroup
+  static_assert(KS == 16, "a round's slot u exists for all streams or none when KS divides the block");
   using V = DVec<EPL>;
   __shared__ float s_m[KS][G], s_l[KS][G];
   __shared__ float s_acc[KS][G][D];
@@ -113,6 +114,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a,
     }
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
+      // slot base + u KS exists for every stream or for none (nslots is a
+      // multiple of 16 = KS for blocks of 16 or more): skip empty slots whole
+      if (base - ks + u * KS >= nslots) break;
       float vf[EPL];
 #pragma unroll
       for (int k2 = 0; k2 < EPL / 2; ++k2) {
