@@ -193,7 +193,8 @@ int spot_sparse_attn_prefill(const spot_desc* desc, const void* q, const void* k
  * q: [batch, hq, d]; k_cache, v_cache: [batch, hkv, kv_len, d];
  * o: [batch, hq, d]; lse (nullable): [batch, hq].
  * Work is split over the kept list; partial (max, sum, accumulator) triples go
- * to the workspace and are merged in a fixed order (deterministic).
+ * to the workspace and are merged in a fixed order (deterministic).  A
+ * sequence with cnt = 0 attends no key: its O is 0 and its lse -inf.
  * q, k_cache, v_cache and workspace must be 16-byte aligned (SPOT_ERR_INVALID
  * otherwise).
  */

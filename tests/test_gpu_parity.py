@@ -501,6 +501,37 @@ def test_decode_small(gpu, kw):
     decode_check(cfg, D, bufs)
 
 
+def test_decode_attention_on_host_lists(gpu):
+    """Decode attention on kept lists drawn on the host (not by the select
+    kernel): an empty list (O = 0, LSE = -inf by the library's convention), the
+    ragged last block alone, a sparse random list and every block."""
+    cfg = I.C4.with_(name="declists", seed=29, batch=4, T=16 * 300 + 9)
+    D = I.decode_inputs(cfg)
+    nt = cfg.nt
+    rng = np.random.default_rng(31)
+    lists = [np.zeros(0, np.int64), np.array([nt - 1]), np.sort(rng.choice(nt, 37, replace=False)), np.arange(nt)]
+    dev = {k: P.to_dev(D[k], "bf16", gpu) for k in ("q", "k_cache", "v_cache")}
+    desc = B.decode_desc(dev["q"], dev["k_cache"], cfg.block, cfg.top_p, cfg.h_idx, cfg.d_idx)
+    bufs = B.alloc_decode(desc, gpu)
+    idx = np.full((cfg.batch, 1, 1, nt), -1, np.int32)
+    for b, kl in enumerate(lists):
+        idx[b, 0, 0, :len(kl)] = kl
+    bufs.idx.copy_(torch.from_numpy(idx))
+    bufs.cnt.copy_(torch.tensor([len(kl) for kl in lists], dtype=torch.int32).view(cfg.batch, 1, 1))
+    B.spot_sparse_attn_decode(desc, dev["q"], dev["k_cache"], dev["v_cache"], bufs.idx, bufs.cnt, bufs.o, bufs.lse,
+                              bufs.workspace)
+    torch.cuda.synchronize()
+    go, glse = bufs.o.float().cpu().numpy(), bufs.lse.cpu().numpy()
+    assert (go[0] == 0).all() and np.isneginf(glse[0]).all()
+    scale = 1 / math.sqrt(cfg.d)
+    for b in range(1, cfg.batch):
+        o_ref, lse_ref = oracle.attend_decode(D["q"][b], D["k_cache"][b], D["v_cache"][b], lists[b], cfg.block,
+                                              cfg.T, scale)
+        err_o, err_l = P.max_abs(go[b], o_ref), P.max_abs(glse[b], lse_ref)
+        log("declists", b, len(lists[b]), f"max|dO|={err_o:.3g} max|dLSE|={err_l:.3g}")
+        assert err_o <= P.BF16_ATOL and err_l <= 1e-2
+
+
 def test_c4_decode_full(gpu):
     cfg = I.C4
     t0 = time.time()
