@@ -21,6 +21,7 @@ PINS = "tests/test_oracle_pins.py"
 ES = "tests/test_oracle_early_stop.py"
 TAYLOR = "tests/test_oracle_taylor.py"
 MXFP4 = "tests/test_oracle_mxfp4.py"
+S2O = "tests/test_oracle_s2o_map.py"
 
 # (name, pin file, line fragment as written in the oracle, planted mistake)
 MUTANTS = [
@@ -54,6 +55,13 @@ MUTANTS = [
      "np.log(1.0 + 0.5 * (vb @ (x * x)))", "np.log(1.0 + (vb @ (x * x)))"),
     ("Taylor term linear in the query", TAYLOR,
      "np.log(1.0 + 0.5 * (vb @ (x * x)))", "np.log(1.0 + 0.5 * (vb @ x))"),
+    ("segment query mean over one head of the group", S2O,
+     "rep_q[g, sg] = q[g * G:(g + 1) * G, sg * segment:min((sg + 1) * segment, L)].mean(axis=(0, 1))",
+     "rep_q[g, sg] = q[g * G, sg * segment:min((sg + 1) * segment, L)].mean(axis=0)"),
+    ("history map in ascending score order", S2O,
+     "hmap[g, sg, :n] = ts[np.lexsort((ts, -c))]", "hmap[g, sg, :n] = ts[np.lexsort((ts, c))]"),
+    ("history map ties by descending position", S2O,
+     "hmap[g, sg, :n] = ts[np.lexsort((ts, -c))]", "hmap[g, sg, :n] = ts[np.lexsort((-ts, -c))]"),
     ("MXFP4 scale one power of two too large", MXFP4,
      "np.clip(ex.astype(np.int64) - 1 - 2, -127, 127)", "np.clip(ex.astype(np.int64) - 1 - 1, -127, 127)"),
 ]
