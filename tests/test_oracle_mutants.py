@@ -30,6 +30,12 @@ MUTANTS = [
     ("exclusive top-p crossing", PINS, "c >= top_p", "c > top_p"),
     ("recency window one block too wide", PINS,
      "return (js < n_sink) | (js > i - n_recent)", "return (js < n_sink) | (js >= i - n_recent)"),
+    ("decode recency window one block too wide", PINS,
+     "return (ts < n_sink) | (ts > nt - 1 - n_recent)", "return (ts < n_sink) | (ts >= nt - 1 - n_recent)"),
+    ("decode sink window one block too wide", PINS,
+     "return (ts < n_sink) | (ts > nt - 1 - n_recent)", "return (ts <= n_sink) | (ts > nt - 1 - n_recent)"),
+    ("decode recency window one block too narrow", PINS,
+     "return (ts < n_sink) | (ts > nt - 1 - n_recent)", "return (ts < n_sink) | (ts > nt - n_recent)"),
     ("history key means without the permutation", PINS,
      "kp[g, i] = k[g, perm[g, rows]].mean(axis=0)", "kp[g, i] = k[g, rows].mean(axis=0)"),
     ("query means over one head of the group", PINS,

@@ -329,6 +329,78 @@ def test_decode_keep_all_is_last_row_of_dense(T):
     np.testing.assert_allclose(lse, lp[:, T - 1], rtol=1e-12, atol=1e-12)
 
 
+def _decode_reserved(nt, n_sink, n_recent):
+    """Reserved blocks of a decode row written from the dual top-p rule's
+    definition (SpotAttention §3, reserved blocks): the first n_sink blocks
+    of the context and its last n_recent blocks."""
+    return set(range(min(n_sink, nt))) | set(range(max(nt - n_recent, 0), nt))
+
+
+@pytest.mark.parametrize("n_sink,n_recent", [(1, 1), (2, 1), (1, 2), (0, 1), (1, 0), (3, 2)])
+@pytest.mark.parametrize("nt", [12, 23])
+def test_decode_reserved_blocks_closed_form(n_sink, n_recent, nt):
+    """Indexer dots all <= 0 make every decode score exactly 0 (ReLU), so the
+    residual distribution is uniform (1/n each): the kept set is the reserved
+    blocks plus the ceil(p*n) lowest residual ids.  Several p off the 1/n grid
+    make a sink or recency window one block too wide or too narrow change the
+    kept set; the output must be library attention over exactly those keys."""
+    r = _rng(40 + 7 * n_sink + n_recent + nt)
+    B, h_idx, d_idx, hq, hkv, d = 16, 2, 8, 4, 2, 8
+    T = nt * B - 5                                   # ragged last block
+    qI = np.abs(r.standard_normal((h_idx, d_idx))) + 0.1
+    kI = -np.abs(r.standard_normal((nt, h_idx, d_idx)))
+    w = np.array([0.4, 0.6])
+    kc, vc = r.standard_normal((hkv, T, d)), r.standard_normal((hkv, T, d))
+    q = r.standard_normal((hq, d))
+    reserved = _decode_reserved(nt, n_sink, n_recent)
+    resid = [t for t in range(nt) if t not in reserved]
+    n = len(resid)
+    for p in (0.13, 0.37, 0.62, 0.87):
+        assert abs(p * n - round(p * n)) > 1e-6         # off the 1/n grid
+        out = oracle.decode(q, kc, vc, qI, w, kI, B, T, top_p=p, n_sink=n_sink, n_recent=n_recent)
+        assert np.all(out["scores"] == 0.0)
+        want = sorted(reserved | set(resid[:math.ceil(p * n)]))
+        assert list(out["kept"]) == want, (p, n_sink, n_recent)
+        mask = np.zeros((1, T), dtype=bool)
+        for t in want:
+            mask[0, t * B: min(T, (t + 1) * B)] = True
+        ref = sdpa(q[:, None], np.repeat(kc, 2, 0), np.repeat(vc, 2, 0), mask=np.repeat(mask[None], hq, 0))
+        np.testing.assert_allclose(out["o"], ref[:, 0], rtol=1e-12, atol=1e-12)
+    # p <= 0 keeps the reserved blocks only; p >= 1 keeps every block
+    assert list(oracle.select_decode(np.zeros(nt), n_sink, n_recent, 0.0, 0)) == sorted(reserved)
+    assert list(oracle.select_decode(np.zeros(nt), n_sink, n_recent, 1.0, 0)) == list(range(nt))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_decode_select_matches_brute_force(seed):
+    """Decode rows of at most 14 blocks with random sink / recency sizes:
+    the oracle's selection equals the smallest subset of the residual blocks
+    reaching mass p (largest mass, then lowest ids), plus the reserved blocks
+    written from their definition."""
+    r = _rng(3000 + seed)
+    nt = int(r.integers(2, 15))
+    n_sink, n_recent = int(r.integers(0, 4)), int(r.integers(0, 4))
+    if n_sink + n_recent == 0:
+        n_recent = 1
+    scores = r.standard_normal(nt) * r.choice([0.3, 1.0, 3.0])
+    if seed % 3 == 0:
+        scores = np.maximum(np.round(scores, 0), 0.0)   # ReLU-like ties at zero
+    p = float(r.choice([0.2, 0.45, 0.7, 0.9]))
+    reserved = _decode_reserved(nt, n_sink, n_recent)
+    forced = np.array([t in reserved for t in range(nt)])
+    resid = [t for t in range(nt) if not forced[t]]
+    if resid:
+        sr = scores[resid]
+        e = np.exp(sr - sr.max())
+        pis = e / e.sum()
+        for m in range(len(resid) + 1):
+            for sub in itertools.combinations(range(len(resid)), m):
+                if abs(pis[list(sub)].sum() - p) < 1e-9:
+                    pytest.skip("draw on the float boundary")
+    got = oracle.select_decode(scores, n_sink, n_recent, p, 0)
+    assert list(got) == _brute_force_keep(scores, forced, p)
+
+
 def test_decode_sparse_is_masked_library_attention():
     r = _rng(9)
     hq, hkv, d, B, T = 4, 1, 8, 16, 200
