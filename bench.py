@@ -1,19 +1,23 @@
 """Benchmark of the block-sparse attention hot path on one MI355X.
 
-One step = the whole prefill path on the GQA workload (L=8192, 32 query / 8 KV
-heads, d=128, bf16, block 64, top-p 0.9): mean-pool block scores, top-p
-selection, sparse attention.  Inputs are resident in HBM before timing.  The
-step is timed two ways over K steps: its four launches issued call by call on
-the stream, and captured once as a HIP graph and replayed; `ms_per_step` is
-the faster of the two (`config.step_launch` names it, both times are in
-`config`).
+Headline step = the whole prefill path on the long-context workload
+(L=131072, 32 query / 8 KV heads, d=128, bf16, block 128, top-p 0.9, 2% planted
+heavy hitters): mean-pool block scores, top-p selection, sparse attention.
+Inputs are resident in HBM before timing.  The step is timed two ways over K
+steps: its launches issued call by call on the stream, and captured once as a
+HIP graph and replayed; `ms_per_step` is the faster of the two
+(`config.step_launch` names it, both times are in `config`).
 
 Prints one JSON line.  `value` is effective TFLOP/s over kept blocks
 (4*d*visible query-key pairs per step / step time).  The line also carries the
-roofline of the dominant kernel (the attention kernel, bf16 MFMA bound), a
-decode measurement on the sparse-decode workload (batch 16, context 131072,
-KV GB/s against HBM) and the float64 oracle timed on a bounded sample on the
-host cores.
+roofline of the dominant kernel (the attention kernel, bf16 MFMA bound), the
+float64 oracle timed on the host cores over 64 seeded query blocks of the same
+workload, and under `configs` one object per synthetic workload: the tiny fp32
+prefill (time only), the GQA prefill (with the keep-all reference and the
+Taylor score), the heavy-hitter prefill with the GPU key permutation inside
+the step (plus the early-stopping variants), the sparse decode step (bf16 and
+MXFP4 indexer caches, and a keep-all run that streams the whole KV cache) and
+the long prefill's keep-all reference.
 """
 from __future__ import annotations
 
@@ -33,6 +37,8 @@ sys.path.insert(0, ROOT)
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 METRIC = "effective TFLOP/s sparse prefill (kept blocks); decode KV GB/s; % roofline"
+HEADLINE = "long-bf16-L131072"
+KDIR = os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "kernels")
 
 
 def parse():
@@ -40,15 +46,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--workload", default=HEADLINE,
+                    help="prefill workload of the headline step: long-bf16-L131072 (default), gqa-bf16-L8192, "
+                         "heavy-perm-bf16-L32768 (permutation generated on the GPU inside the step), tiny-fp32-L256")
+    ap.add_argument("--headline-only", action="store_true", help="time the headline workload only")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--no-early-stop", action="store_true", help="skip the early-stopping measurement")
+    ap.add_argument("--no-early-stop", action="store_true", help="skip the early-stopping measurements")
     ap.add_argument("--es-tau", type=float, default=0.01, help="early-stopping threshold tau")
     ap.add_argument("--no-taylor", action="store_true", help="skip the Taylor-score measurement")
-    ap.add_argument("--cpu-sample-blocks", type=int, default=0, help="0: every query block")
-    ap.add_argument("--workload", default="gqa-bf16-L8192",
-                    help="prefill workload of the step: gqa-bf16-L8192 (default), heavy-perm-bf16-L32768 "
-                         "(permutation generated on the GPU inside the step), long-bf16-L131072, tiny-fp32-L256")
+    ap.add_argument("--cpu-blocks", type=int, default=0,
+                    help="query blocks the oracle covers (0: the workload's seeded sample, or every block)")
     return ap.parse_args()
 
 
@@ -90,14 +98,16 @@ def load_traffic(kernel_file: str, key: str):
 
 
 # ----------------------------------------------------------------- prefill
-def prefill_data(args, torch, I):
-    """Host and device inputs of the prefill workload (made once, shared by its measurements)."""
-    cfg = {c.name: c for c in (I.C1, I.C2, I.C3, I.C5)}[args.workload]
-    q, k, v = I.prefill_inputs(cfg)
+def prefill_host(I, name):
+    cfg = {c.name: c for c in (I.C1, I.C2, I.C3, I.C5)}[name]
+    return cfg, I.prefill_inputs(cfg)
+
+
+def prefill_device(torch, cfg, host):
+    """Device copies of the workload's inputs (made once, shared by its measurements)."""
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
-    dq, dk, dv = (torch.from_numpy(x).to(tdt).to(dev) for x in (q, k, v))
-    return cfg, (q, k), (dq, dk, dv)
+    return tuple(torch.from_numpy(x).to(tdt).to(dev) for x in host)
 
 
 def settle(torch, fn, ms=30.0):
@@ -113,8 +123,10 @@ def settle(torch, fn, ms=30.0):
         done += e0.elapsed_time(e1)
 
 
-def bench_prefill(args, torch, B, I, data, score_kind=None, top_p=None):
-    cfg, (q, k), (dq, dk, dv) = data
+def bench_prefill(args, torch, B, cfg, dev_in, score_kind=None, top_p=None):
+    """Times the prefill step (key permutation when the workload has segments, block scores, top-p
+    selection, sparse attention) on resident inputs."""
+    dq, dk, dv = dev_in
     if top_p is not None:
         cfg = cfg.with_(top_p=top_p)
     score_kind = B.SPOT_SCORE_MEANPOOL if score_kind is None else score_kind
@@ -169,6 +181,7 @@ def bench_prefill(args, torch, B, I, data, score_kind=None, top_p=None):
     t1.record()
     torch.cuda.synchronize()
     ms_step_graph = t0.elapsed_time(t1) / args.steps
+    del graph
     # the same work either way: report the faster launch mode
     ms_step = min(ms_step_graph, ms_step_eager)
     step_launch = "hip_graph_replay" if ms_step_graph <= ms_step_eager else "stream_launches"
@@ -190,7 +203,7 @@ def bench_prefill(args, torch, B, I, data, score_kind=None, top_p=None):
     dense_pairs = G * cfg.hkv * cfg.L * (cfg.L + 1) / 2
     kept_fraction = float(pairs.sum()) / dense_pairs
 
-    attn_file = os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "kernels", "prefill.hip")
+    attn_file = os.path.join(KDIR, "prefill.hip")
     achieved = flops / (ms_attn * 1e-3) / 1e12
     if cfg.dtype == "bf16":
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -201,40 +214,89 @@ def bench_prefill(args, torch, B, I, data, score_kind=None, top_p=None):
                 "flop_per_launch": flops, "avg_launch_ms": round(ms_attn, 4)}
     else:   # the fp32 row kernel on a 256-token input is launch-latency bound
         roof = {"bound": "latency", "achieved": round(achieved, 4), "peak": None, "unit": "TFLOP/s", "frac": None,
-                "traffic": None, "kernel": "prefill_rows_kernel<float,64>", "flop_per_launch": flops,
+                "traffic": None, "kernel": f"prefill_rows_kernel<float,{cfg.d}>", "flop_per_launch": flops,
                 "avg_launch_ms": round(ms_attn, 4)}
-    res = dict(
+    perm_blocks = None
+    if perm is not None and score_kind == B.SPOT_SCORE_MEANPOOL:
+        # top-p at the workload's p with history means over the permuted keys and without the permutation:
+        # how many blocks the same mass needs in each case (outside the timed steps)
+        kept = {}
+        for name, seg, pm in (("with_permutation", cfg.segment, perm), ("without_permutation", 0, None)):
+            d2 = B.prefill_desc(dq, dk, cfg.block, cfg.top_p, segment=seg)
+            b2 = B.alloc_prefill(d2, dev)
+            B.spot_block_score(d2, dq, dk, pm, None, None, None, b2.scores, b2.workspace)
+            B.spot_select_topp(d2, b2.scores, b2.idx, b2.cnt)
+            torch.cuda.synchronize()
+            kept[name] = int(b2.cnt.cpu().numpy().astype(np.int64).sum())
+            del b2
+        cand = cfg.batch * cfg.hkv * cfg.nb * (cfg.nb + 1) // 2
+        perm_blocks = {"top_p": cfg.top_p, "candidate_blocks": cand, **kept,
+                       "change": round(kept["with_permutation"] / kept["without_permutation"] - 1.0, 4)}
+    return dict(
         cfg=cfg, ms_step=ms_step, ms_step_eager=ms_step_eager, ms_step_graph=ms_step_graph, step_launch=step_launch,
         ms_perm=ms_perm, ms_sel=ms_sel, ms_attn=ms_attn,
         flops=flops, kept_fraction=kept_fraction, value=flops / (ms_step * 1e-3) / 1e12, roofline=roof,
-        host=(q, k, None), idx=idx, cnt=cnt,
+        perm_blocks=perm_blocks,
     )
-    return res
+
+
+def prefill_object(res, headline=False):
+    """JSON object of one prefill measurement."""
+    cfg = res["cfg"]
+    out = {"workload": cfg.name, "dtype": cfg.dtype, "seq_len": cfg.L, "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d,
+           "block": cfg.block, "top_p": cfg.top_p, "segment": cfg.segment,
+           "value": round(res["value"], 4 if cfg.dtype != "bf16" else 2), "unit": "TFLOP/s",
+           "ms_per_step": round(res["ms_step"], 4), "step_launch": res["step_launch"],
+           "ms_per_step_stream_launches": round(res["ms_step_eager"], 4),
+           "ms_per_step_graph_replay": round(res["ms_step_graph"], 4),
+           "ms_key_permutation": round(res["ms_perm"], 4), "ms_score_select": round(res["ms_sel"], 4),
+           "ms_attention": round(res["ms_attn"], 4), "kept_fraction": round(res["kept_fraction"], 4),
+           "flop_per_step": res["flops"]}
+    if not headline:
+        out["roofline"] = res["roofline"]
+    if res.get("perm_blocks"):
+        out["top_p_kept_blocks"] = res["perm_blocks"]
+    return out
+
+
+def dense_object(sparse, dense):
+    return {"workload": dense["cfg"].name, "top_p": 1.0, "ms_per_step": round(dense["ms_step"], 4),
+            "ms_attention": round(dense["ms_attn"], 4), "value": round(dense["value"], 2), "unit": "TFLOP/s",
+            "kept_fraction": round(dense["kept_fraction"], 4),
+            "attention_frac_of_peak": dense["roofline"]["frac"],
+            "sparse_speedup_step": round(dense["ms_step"] / sparse["ms_step"], 3),
+            "sparse_speedup_attention": round(dense["ms_attn"] / sparse["ms_attn"], 3)}
 
 
 # ----------------------------------------------------------------- decode
-def bench_decode(args, torch, B, I, mxfp4=False):
+def decode_device(torch, B, I):
+    """Device inputs of the sparse-decode workload (made once, shared by its measurements), with the
+    MXFP4 encoding of the indexer keys (made once, when keys are appended; outside every step)."""
     cfg = I.C4
     dev = torch.device("cuda:0")
     D = I.decode_inputs(cfg)
     up = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)
-    q, kc, vc = up(D["q"]), up(D["k_cache"]), up(D["v_cache"])
-    iq, ik = up(D["idx_q"]), up(D["idx_k"])
-    iw = torch.from_numpy(D["idx_w"]).to(dev)
+    t = dict(q=up(D["q"]), kc=up(D["k_cache"]), vc=up(D["v_cache"]), iq=up(D["idx_q"]), ik=up(D["idx_k"]),
+             iw=torch.from_numpy(D["idx_w"]).to(dev))
     del D
-    desc = B.decode_desc(q, kc, cfg.block, cfg.top_p, cfg.h_idx, cfg.d_idx)
+    t["codes"], t["scales"] = B.quantize_indexer_keys(t["ik"], cfg.block, cfg.T)
+    torch.cuda.synchronize()
+    return cfg, t
+
+
+def bench_decode(args, torch, B, cfg, t, mxfp4=False, top_p=None):
+    dev = torch.device("cuda:0")
+    top_p = cfg.top_p if top_p is None else top_p
+    q, kc, vc, iq, iw = t["q"], t["kc"], t["vc"], t["iq"], t["iw"]
+    desc = B.decode_desc(q, kc, cfg.block, top_p, cfg.h_idx, cfg.d_idx)
     bufs = B.alloc_decode(desc, dev)
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
-    if mxfp4:   # the cache is encoded once, when keys are appended (outside the step)
-        kcodes, kscales = B.quantize_indexer_keys(ik, cfg.block, cfg.T)
-        torch.cuda.synchronize()
-        del ik
 
     def score():
         if mxfp4:
-            B.spot_indexer_score_mxfp4(desc, iq, iw, kcodes, kscales, bufs.scores)
+            B.spot_indexer_score_mxfp4(desc, iq, iw, t["codes"], t["scales"], bufs.scores)
         else:
-            B.spot_block_score(desc, None, None, None, iq, iw, ik, bufs.scores)
+            B.spot_block_score(desc, None, None, None, iq, iw, t["ik"], bufs.scores)
 
     def step(ev):
         ev[0].record()
@@ -258,7 +320,7 @@ def bench_decode(args, torch, B, I, mxfp4=False):
     ms_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     ms_step_eager = ms_front + ms_attn
 
-    # the step's four launches as one HIP graph, replayed with a cold cache each time
+    # the step's launches as one HIP graph, replayed with a cold cache each time
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         score()
@@ -273,6 +335,7 @@ def bench_decode(args, torch, B, I, mxfp4=False):
         e[1].record()
     torch.cuda.synchronize()
     ms_step_graph = float(np.mean([e[0].elapsed_time(e[1]) for e in gev]))
+    del graph
     # the same work either way: report the faster launch mode
     ms_step = min(ms_step_graph, ms_step_eager)
     step_launch = "hip_graph_replay" if ms_step_graph <= ms_step_eager else "stream_launches"
@@ -286,33 +349,29 @@ def bench_decode(args, torch, B, I, mxfp4=False):
     step_bytes = kv_bytes + scan_bytes + qo_bytes
     attn_gbs = (kv_bytes + qo_bytes) / (ms_attn * 1e-3) / 1e9
     return dict(
-        workload=cfg.name, indexer_cache="mxfp4" if mxfp4 else "bf16",
+        workload=cfg.name, indexer_cache="mxfp4" if mxfp4 else "bf16", top_p=top_p,
         value=round(step_bytes / (ms_step * 1e-3) / 1e9, 1), unit="GB/s",
+        frac_of_hbm_peak=round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         ms_per_step=round(ms_step, 4), step_launch=step_launch, ms_per_step_stream_launches=round(ms_step_eager, 4),
         ms_per_step_graph_replay=round(ms_step_graph, 4), ms_score_select=round(ms_front, 4), ms_indexer_scan=round(ms_scan, 4),
         indexer_scan_gbs=round(scan_bytes / (ms_scan * 1e-3) / 1e9, 1), indexer_scan_bytes=scan_bytes,
-        ms_attention=round(ms_attn, 4),
+        ms_select=round(ms_front - ms_scan, 4), ms_attention=round(ms_attn, 4),
         kept_fraction=round(float(kept_keys.sum()) / (cfg.batch * cfg.T), 4), bytes_per_step=step_bytes,
         roofline={"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "kernel": "decode_split_kernel<128,4>+combine",
-                  "traffic": load_traffic(os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "kernels",
-                                                       "decode.hip"), f"decode_split_kernel@{cfg.name}"),
+                  "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "kernel": "decode attention (split + combine)",
+                  "traffic": load_traffic(os.path.join(KDIR, "decode.hip"), f"decode_split_kernel@{cfg.name}"
+                                          + ("" if top_p < 1.0 else "-keep-all")),
                   "bytes_per_launch": kv_bytes + qo_bytes},
     )
 
 
 # ----------------------------------------------------------------- early stopping
-def bench_early_stop(args, torch, B, I):
+def bench_early_stop(args, torch, B, cfg, dev_in):
     """Early-stopped prefill on the heavy-hitter workload (L=32768, segment
     2048): key permutation, block scores, history visiting order and the
     early-stopped attention, captured as one HIP graph."""
-    cfg = I.C3
     dev = torch.device("cuda:0")
-    q, k, v = I.prefill_inputs(cfg)
-    dq = torch.from_numpy(q).to(torch.bfloat16).to(dev)
-    dk = torch.from_numpy(k).to(torch.bfloat16).to(dev)
-    dv = torch.from_numpy(v).to(torch.bfloat16).to(dev)
-    del q, k, v
+    dq, dk, dv = dev_in
     tau = args.es_tau
     desc = B.prefill_desc(dq, dk, cfg.block, 1.0, segment=cfg.segment)
     bufs = B.alloc_prefill_early_stop(desc, dev)
@@ -379,23 +438,8 @@ def bench_early_stop(args, torch, B, I):
         walked += float((own_packed[None, :, c0:c0 + 256] + part.max(axis=-1, keepdims=True) * Bk).sum())
     achieved = flops / (ms_attn * 1e-3) / 1e12
 
-    # top-p selection at the workload's p with history means over the permuted keys and without the
-    # permutation: how many blocks the same mass needs in each case (outside the timed steps)
-    kept = {}
-    for name, seg, pm in (("with_permutation", cfg.segment, perm), ("without_permutation", 0, None)):
-        d2 = B.prefill_desc(dq, dk, cfg.block, cfg.top_p, segment=seg)
-        b2 = B.alloc_prefill(d2, dev)
-        B.spot_block_score(d2, dq, dk, pm, None, None, None, b2.scores, b2.workspace)
-        B.spot_select_topp(d2, b2.scores, b2.idx, b2.cnt)
-        torch.cuda.synchronize()
-        kept[name] = int(b2.cnt.cpu().numpy().astype(np.int64).sum())
-        del b2
-    cand = cfg.hkv * cfg.nb * (cfg.nb + 1) // 2
-    top_p_blocks = {"top_p": cfg.top_p, "candidate_blocks": cand, **kept,
-                    "change": round(kept["with_permutation"] / kept["without_permutation"] - 1.0, 4)}
     return dict(
         workload=cfg.name, tau=tau, value=round(flops / (ms_step * 1e-3) / 1e12, 2), unit="TFLOP/s",
-        top_p_kept_blocks=top_p_blocks,
         ms_per_step=round(ms_step, 4), ms_key_permutation=round(ms_perm, 4), ms_score_order=round(ms_front, 4),
         ms_attention=round(ms_attn, 4), taken_fraction=round(float(pairs_row.sum()) / dense_pairs, 4),
         walked_fraction=round(walked / dense_pairs, 4), mean_history_blocks=round(float(nused.mean()), 2),
@@ -403,24 +447,18 @@ def bench_early_stop(args, torch, B, I):
         roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                   "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
                   "kernel": "prefill_mfma_kernel<128,8,1,true,true,true> (early stop)", "avg_launch_ms": round(ms_attn, 4),
-                  "traffic": load_traffic(os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "kernels",
-                                                       "prefill.hip"),
+                  "traffic": load_traffic(os.path.join(KDIR, "prefill.hip"),
                                           f"prefill_mfma_kernel_early_stop@{cfg.name}"),
                   "walked_tflops": round(4.0 * cfg.d * walked / (ms_attn * 1e-3) / 1e12, 2)},
     )
 
 
-def bench_history_map(args, torch, B, I):
+def bench_history_map(args, torch, B, cfg, dev_in):
     """Early-stopped prefill on representative-query history maps on the
     heavy-hitter workload: maps of every segment, then the attention walking
     them, captured as one HIP graph."""
-    cfg = I.C3
     dev = torch.device("cuda:0")
-    q, k, v = I.prefill_inputs(cfg)
-    dq = torch.from_numpy(q).to(torch.bfloat16).to(dev)
-    dk = torch.from_numpy(k).to(torch.bfloat16).to(dev)
-    dv = torch.from_numpy(v).to(torch.bfloat16).to(dev)
-    del q, k, v
+    dq, dk, dv = dev_in
     tau = args.es_tau
     desc = B.prefill_desc(dq, dk, cfg.block, 1.0, segment=cfg.segment)
     bufs = B.alloc_prefill_early_stop(desc, dev)
@@ -511,45 +549,78 @@ def measured_ceilings(torch):
 
 
 # ----------------------------------------------------------------- oracle on the host
-def cpu_baseline(res, I, sample_blocks: int):
-    """The float64 oracle on the host over the workload (or a seeded sample of
-    query blocks on the long ones): pool and score every block, select and
-    attend the sampled query blocks, permutation included when the workload
-    uses one."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+_ORC = {}   # inputs of the oracle's per-unit work, inherited by the forked workers
+
+
+def _oracle_worker_init():
+    try:   # one BLAS thread per worker process: the pool supplies the parallelism
+        from threadpoolctl import threadpool_limits
+        _ORC["limit"] = threadpool_limits(1)
     except Exception:
-        threads = 1
-    cfg = res["cfg"]
-    q, k, v = I.prefill_inputs(cfg)
-    if sample_blocks <= 0 and cfg.L > 16384:
-        sample_blocks = 8
-    if sample_blocks <= 0 or sample_blocks >= cfg.nb:
-        blocks = list(range(cfg.nb))
+        pass
+
+
+def _oracle_unit(unit):
+    """Select and attend one (KV head, query block) with the float64 oracle; returns its visible
+    (query, key) pairs summed over the group's heads and the seconds it took."""
+    import oracle
+    g, i = unit
+    c = _ORC
+    t0 = time.perf_counter()
+    kept = oracle.topp_keep(c["scores"][g, i, :i + 1], oracle.prefill_forced(i, c["n_sink"], c["n_recent"]),
+                            c["top_p"], c["k_min"])
+    G = c["G"]
+    oracle.attend_prefill(c["q"][g * G:(g + 1) * G], c["k"][g:g + 1], c["v"][g:g + 1], [{i: kept}], c["block"],
+                          c["scale"], c["segment"], None if c["perm"] is None else c["perm"][g:g + 1], qblocks=[i])
+    dt = time.perf_counter() - t0
+    L, B = c["L"], c["block"]
+    bs = [min(B, L - j * B) for j in range(i + 1)]
+    nrow = bs[i]
+    full = sum(bs[int(j)] for j in kept if int(j) != i)
+    diag = i in set(int(j) for j in kept)
+    return G * (nrow * full + (nrow * (nrow + 1) // 2 if diag else 0)), dt
+
+
+def cpu_baseline(cfg, host, I, n_blocks: int = 0):
+    """The float64 oracle on the host over the workload's seeded sample of query blocks (every block
+    on the short workloads): widen the inputs, permutation when the workload uses one, pool and score
+    every block (one process), then select and attend each (KV head, sampled query block) in a pool
+    of forked worker processes with one BLAS thread each.  Runs before the process touches the GPU."""
+    import multiprocessing as mp
+
+    import oracle
+    if n_blocks > 0:
+        blocks = I.oracle_query_blocks(cfg.with_(oracle_qblocks=n_blocks))
     else:
-        rng = np.random.default_rng([cfg.seed, 1234])
-        blocks = sorted({cfg.nb - 1} | set(rng.choice(cfg.nb, sample_blocks - 1, replace=False).tolist()))
-    scale = 1 / math.sqrt(cfg.d)
-    t0 = time.time()
+        blocks = I.oracle_query_blocks(cfg)
+    blocks = [int(b) for b in blocks]
+    ncpu = os.cpu_count() or 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = ncpu
+    workers = max(1, min(ncpu, avail, 16))
+    q, k, v = host
+    t0 = time.perf_counter()
+    q64, k64, v64 = (np.asarray(x[0], dtype=np.float64) for x in (q, k, v))
+    scale = 1.0 / math.sqrt(cfg.d)
     perm = None
     if cfg.segment:
-        perm, _ = oracle.key_permutation(q[0], k[0], cfg.block, cfg.segment, scale)
-    out = oracle.prefill(q[0], k[0], v[0], cfg.block, cfg.top_p, qblocks=blocks, segment=cfg.segment, perm=perm)
-    dt = time.time() - t0
-    G = cfg.hq // cfg.hkv
-    nb = cfg.nb
-    idx = np.full((1, cfg.hkv, nb, nb), -1, np.int64)
-    sel = np.zeros((1, cfg.hkv, nb), bool)
-    for g in range(cfg.hkv):
-        for i in blocks:
-            kl = out["kept"][g][i]
-            idx[0, g, i, :len(kl)] = kl
-            sel[0, g, i] = True
-    pairs = prefill_visible_pairs(idx, None, cfg.L, cfg.block, G)
-    flops = 4.0 * cfg.d * float(pairs[sel].sum())
-    what = "every query block" if len(blocks) == nb else f"{len(blocks)} seeded query blocks"
+        perm, _ = oracle.key_permutation(q64, k64, cfg.block, cfg.segment, scale)
+    qbar, kn, kp = oracle.pool_blocks(q64, k64, cfg.block, perm)
+    scores = oracle.meanpool_scores(qbar, kn, kp, cfg.block, cfg.segment, scale)
+    t_front = time.perf_counter() - t0
+    _ORC.update(q=q64, k=k64, v=v64, perm=perm, scores=scores, block=cfg.block, segment=cfg.segment, L=cfg.L,
+                G=cfg.hq // cfg.hkv, scale=scale, top_p=cfg.top_p, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
+                k_min=cfg.k_min)
+    units = [(g, i) for i in sorted(blocks, reverse=True) for g in range(cfg.hkv)]   # longest first
+    with mp.get_context("fork").Pool(workers, initializer=_oracle_worker_init) as pool:
+        res = pool.map(_oracle_unit, units, chunksize=1)
+    dt = time.perf_counter() - t0
+    _ORC.clear()
+    pairs = float(sum(r[0] for r in res))
+    unit_s = float(sum(r[1] for r in res))
+    flops = 4.0 * cfg.d * pairs
     cpu_model = ""
     try:
         for ln in open("/proc/cpuinfo"):
@@ -558,10 +629,17 @@ def cpu_baseline(res, I, sample_blocks: int):
                 break
     except OSError:
         pass
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 2), "cpu_model": cpu_model, "blas_threads": int(threads),
-            "sample": f"float64 NumPy oracle, whole pipeline ({'permutation, ' if cfg.segment else ''}pool and "
-                      f"score every block, select and attend {what} x {cfg.hkv} KV heads of {cfg.name})"}
+    what = "every query block" if len(blocks) == cfg.nb else \
+        f"{len(blocks)} seeded query blocks ({', '.join(str(b) for b in blocks[:3])}, ..., {blocks[-1]})"
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"float64 NumPy oracle on {cfg.name}: widen inputs, "
+                      f"{'key permutation, ' if cfg.segment else ''}pool and score every block (one process), "
+                      f"then select and attend {what} x {cfg.hkv} KV heads in {workers} worker processes",
+            "workers": workers, "blas_threads_per_worker": 1, "os_cpu_count": ncpu, "cpus_available": avail,
+            "cpu_model": cpu_model, "seconds": round(dt, 2), "seconds_pool_and_score": round(t_front, 2),
+            "query_blocks": len(blocks), "units": len(units),
+            "seconds_per_query_block": round(dt / len(blocks), 4),
+            "cpu_seconds_per_unit": round(unit_s / len(units), 4), "flop": flops}
 
 
 def main():
@@ -573,55 +651,78 @@ def main():
     import torch
     from block_sparse_attention_amd import binding as B
     from block_sparse_attention_amd import inputs as I
+
+    def say(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    head_cfg, head_host = prefill_host(I, args.workload)
+    say(f"inputs of {head_cfg.name} generated")
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's worker processes are forked before this process touches the GPU
+        cpu = cpu_baseline(head_cfg, head_host, I, args.cpu_blocks)
+        say(f"cpu baseline: {cpu}")
+
     B.load_library()
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
-
-    data = prefill_data(args, torch, I)
+    head_dev = prefill_device(torch, head_cfg, head_host)
+    del head_host
     # the ceilings are measured first: their GEMMs and copies also bring the GPU to its working clock after the
     # host-side input generation, before the warm-up steps of the prefill step
     ceil = measured_ceilings(torch)
-    print(f"[bench] measured ceilings: {ceil}", file=sys.stderr, flush=True)
-    pre = bench_prefill(args, torch, B, I, data)
+    say(f"measured ceilings: {ceil}")
+    pre = bench_prefill(args, torch, B, head_cfg, head_dev)
+    say(f"headline {head_cfg.name}: {prefill_object(pre)}")
     # the same kernels keeping every block (p = 1): an in-house dense reference
-    dense = bench_prefill(args, torch, B, I, data, top_p=1.0)
-    dense_ref = {"workload": dense["cfg"].name, "top_p": 1.0, "ms_per_step": round(dense["ms_step"], 4),
-                 "ms_attention": round(dense["ms_attn"], 4), "value": round(dense["value"], 2), "unit": "TFLOP/s",
-                 "kept_fraction": round(dense["kept_fraction"], 4),
-                 "sparse_speedup_step": round(dense["ms_step"] / pre["ms_step"], 3),
-                 "sparse_speedup_attention": round(dense["ms_attn"] / pre["ms_attn"], 3)}
+    dense = bench_prefill(args, torch, B, head_cfg, head_dev, top_p=1.0)
+    configs = {head_cfg.name: dict(prefill_object(pre, headline=True), headline=True,
+                                   dense_reference=dense_object(pre, dense))}
+    say(f"dense reference: {configs[head_cfg.name]['dense_reference']}")
     del dense
-    tay = None
-    if not args.no_taylor:
-        t = bench_prefill(args, torch, B, I, data, score_kind=B.SPOT_SCORE_TAYLOR)
-        tay = {"workload": t["cfg"].name, "score": "second-order Taylor", "value": round(t["value"], 2),
-               "unit": "TFLOP/s", "ms_per_step": round(t["ms_step"], 4), "ms_score_select": round(t["ms_sel"], 4),
-               "ms_attention": round(t["ms_attn"], 4), "kept_fraction": round(t["kept_fraction"], 4),
-               "flop_per_step": t["flops"]}
-        del t
-    print(f"[bench] prefill {pre['cfg'].name}: {pre['ms_step_graph']:.4f} ms/step (graph), "
-          f"{pre['ms_step_eager']:.4f} ms/step (eager), attention {pre['ms_attn']:.4f} ms, "
-          f"score+select {pre['ms_sel']:.4f} ms, kept {pre['kept_fraction']:.4f}", file=sys.stderr, flush=True)
-    dec = dec_mx = None
-    if not args.no_decode:
-        dec = bench_decode(args, torch, B, I)
-        print(f"[bench] decode: {dec}", file=sys.stderr, flush=True)
-        dec_mx = bench_decode(args, torch, B, I, mxfp4=True)
-        print(f"[bench] decode mxfp4: {dec_mx}", file=sys.stderr, flush=True)
-    print(f"[bench] dense reference: {dense_ref}", file=sys.stderr, flush=True)
-    if tay:
-        print(f"[bench] taylor: {tay}", file=sys.stderr, flush=True)
-    es = es_map = None
-    if not args.no_early_stop:
-        es = bench_early_stop(args, torch, B, I)
-        print(f"[bench] early stop: {es}", file=sys.stderr, flush=True)
-        es_map = bench_history_map(args, torch, B, I)
-        print(f"[bench] early stop on history maps: {es_map}", file=sys.stderr, flush=True)
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(pre, I, args.cpu_sample_blocks)
-        print(f"[bench] cpu baseline: {cpu}", file=sys.stderr, flush=True)
+    if args.headline_only:
+        del head_dev
+    else:
+        del head_dev
+        torch.cuda.empty_cache()
+        for c in (I.C1, I.C2, I.C3, I.C5):
+            if c.name == head_cfg.name:
+                continue
+            cfg, host = prefill_host(I, c.name)
+            dev_in = prefill_device(torch, cfg, host)
+            del host
+            r = bench_prefill(args, torch, B, cfg, dev_in)
+            obj = prefill_object(r)
+            if cfg.dtype == "bf16":
+                obj["dense_reference"] = dense_object(r, bench_prefill(args, torch, B, cfg, dev_in, top_p=1.0))
+            if cfg.name == I.C2.name and not args.no_taylor:
+                t = bench_prefill(args, torch, B, cfg, dev_in, score_kind=B.SPOT_SCORE_TAYLOR)
+                obj["taylor_score"] = {"score": "second-order Taylor", "value": round(t["value"], 2),
+                                       "unit": "TFLOP/s", "ms_per_step": round(t["ms_step"], 4),
+                                       "ms_score_select": round(t["ms_sel"], 4),
+                                       "ms_attention": round(t["ms_attn"], 4),
+                                       "kept_fraction": round(t["kept_fraction"], 4), "flop_per_step": t["flops"]}
+            if cfg.name == I.C3.name and not args.no_early_stop:
+                obj["early_stop"] = bench_early_stop(args, torch, B, cfg, dev_in)
+                obj["early_stop_history_map"] = bench_history_map(args, torch, B, cfg, dev_in)
+            configs[cfg.name] = obj
+            say(f"{cfg.name}: {obj}")
+            del dev_in
+            torch.cuda.empty_cache()
+        if not args.no_decode:
+            dcfg, t = decode_device(torch, B, I)
+            dec = {"bf16_indexer": bench_decode(args, torch, B, dcfg, t)}
+            say(f"decode: {dec['bf16_indexer']}")
+            dec["mxfp4_indexer"] = bench_decode(args, torch, B, dcfg, t, mxfp4=True)
+            say(f"decode mxfp4: {dec['mxfp4_indexer']}")
+            # every block kept (p = 1): the attention streams the whole 8 GiB KV cache
+            dec["keep_all"] = bench_decode(args, torch, B, dcfg, t, top_p=1.0)
+            say(f"decode keep-all: {dec['keep_all']}")
+            configs[dcfg.name] = dict(dec, workload=dcfg.name, batch=dcfg.batch, context=dcfg.T, hq=dcfg.hq,
+                                      hkv=dcfg.hkv, d=dcfg.d, block=dcfg.block, h_idx=dcfg.h_idx, d_idx=dcfg.d_idx,
+                                      top_p=dcfg.top_p)
+            del t
 
     cfg = pre["cfg"]
     line = {
@@ -630,24 +731,20 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.L, "hq": cfg.hq, "hkv": cfg.hkv,
                    "d": cfg.d, "block": cfg.block, "top_p": cfg.top_p, "n_sink": cfg.n_sink,
-                   "n_recent": cfg.n_recent, "kept_fraction": round(pre["kept_fraction"], 4),
+                   "n_recent": cfg.n_recent, "heavy_hitters": cfg.heavy_hitters, "segment": cfg.segment,
+                   "kept_fraction": round(pre["kept_fraction"], 4),
                    "ms_attention": round(pre["ms_attn"], 4), "ms_score_select": round(pre["ms_sel"], 4),
+                   "ms_key_permutation": round(pre["ms_perm"], 4),
                    "ms_per_step_stream_launches": round(pre["ms_step_eager"], 4),
                    "ms_per_step_graph_replay": round(pre["ms_step_graph"], 4), "step_launch": pre["step_launch"],
-                   "segment": cfg.segment, "ms_key_permutation": round(pre["ms_perm"], 4),
                    "flop_per_step": pre["flops"]},
         "roofline": dict(pre["roofline"], measured_ceilings=ceil,
                          frac_of_measured_gemm=round(pre["roofline"]["achieved"] / ceil["bf16_gemm_8192_tflops"], 4)
                          if pre["roofline"]["peak"] else None),
         "cpu_baseline": cpu,
-        "dense_reference": dense_ref,
-        "decode": dec,
-        "decode_mxfp4_indexer": dec_mx,
-        "taylor_score": tay,
-        "early_stop": es,
-        "early_stop_history_map": es_map,
+        "configs": configs,
     }
-    print(json.dumps(line))
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
