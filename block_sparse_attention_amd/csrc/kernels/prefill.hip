@@ -29,7 +29,7 @@
 //   the number of (batch, KV head) pairs is a multiple of 8, each KV head is
 //   pinned to one XCD so its K/V stay in that XCD's L2.
 //
-// prefill_rows_kernel (fp32 or bf16, latency path): one wave per query row.
+// prefill_rows_kernel (fp32, latency path): one wave per query row.
 #include <type_traits>
 
 #include "../launch.h"

@@ -196,6 +196,7 @@ int spot_block_score(const spot_desc* desc, const void* q, const void* k, const 
   if (is_pooled(desc)) {
     if ((st = check_prefill_shape(desc))) return st;
     if (!q || !k) return fail(SPOT_ERR_INVALID, "q and k are required for MEANPOOL and TAYLOR");
+    if ((st = check_aligned16("q", q)) || (st = check_aligned16("k", k))) return st;   // 16-byte row loads
     if (perm && desc->segment <= 0) return fail(SPOT_ERR_INVALID, "perm given but segment is 0");
     const size_t need = meanpool_ws_bytes(desc);
     if ((st = check_workspace(need, workspace, workspace_bytes))) return st;
@@ -222,6 +223,7 @@ int spot_block_score(const spot_desc* desc, const void* q, const void* k, const 
   if (desc->score_kind == SPOT_SCORE_RELU_INDEXER) {
     if ((st = check_indexer(desc))) return st;
     if (!idx_q || !idx_w || !idx_k) return fail(SPOT_ERR_INVALID, "idx_q, idx_w and idx_k are required for RELU_INDEXER");
+    if ((st = check_aligned16("idx_q", idx_q)) || (st = check_aligned16("idx_k", idx_k))) return st;
     const int nk = int(ceil_div64(desc->kv_len, desc->block));
     spot::IndexerScoreArgs ia{static_cast<const uint16_t*>(idx_q), idx_w, static_cast<const uint16_t*>(idx_k), scores,
                               desc->batch, nk, desc->h_idx, desc->d_idx};
@@ -297,6 +299,7 @@ int spot_quantize_indexer_keys(const spot_desc* desc, const void* idx_k, uint8_t
   int st = check_mxfp4_indexer(desc);
   if (st) return st;
   if (!idx_k || !k_codes || !k_scales) return fail(SPOT_ERR_INVALID, "idx_k, k_codes and k_scales are required");
+  if ((st = check_aligned16("idx_k", idx_k)) || (st = check_aligned16("k_codes", k_codes))) return st;
   const long long nk = ceil_div64(desc->kv_len, desc->block);
   const long long groups = (long long)desc->batch * nk * (desc->h_idx * desc->d_idx / 32);
   return launched(spot::launch_quantize_mxfp4(static_cast<const uint16_t*>(idx_k), k_codes, k_scales, groups,
@@ -310,6 +313,7 @@ int spot_indexer_score_mxfp4(const spot_desc* desc, const void* idx_q, const flo
   if (st) return st;
   if (!idx_q || !idx_w || !k_codes || !k_scales || !scores)
     return fail(SPOT_ERR_INVALID, "idx_q, idx_w, k_codes, k_scales and scores are required");
+  if ((st = check_aligned16("idx_q", idx_q)) || (st = check_aligned16("k_codes", k_codes))) return st;
   spot::IndexerFp4Args a{static_cast<const uint16_t*>(idx_q), idx_w, k_codes, k_scales, scores, desc->batch,
                          int(ceil_div64(desc->kv_len, desc->block)), desc->h_idx, desc->d_idx};
   return launched(spot::launch_indexer_score_mxfp4(a, static_cast<hipStream_t>(stream)), "indexer_score_mxfp4");
@@ -321,6 +325,7 @@ int spot_history_map(const spot_desc* desc, const void* q, const void* k, int32_
   if (st) return st;
   if ((st = check_prefill_shape(desc))) return st;
   if (!q || !k || !hmap) return fail(SPOT_ERR_INVALID, "q, k and hmap are required");
+  if ((st = check_aligned16("q", q)) || (st = check_aligned16("k", k))) return st;
   if (desc->dtype != SPOT_BF16) return fail(SPOT_ERR_UNSUPPORTED, "history maps support bf16 only");
   if (desc->segment <= 0) return fail(SPOT_ERR_INVALID, "segment must be > 0");
   const int L = int(desc->q_len);
@@ -451,6 +456,7 @@ int spot_key_permutation(const spot_desc* desc, const void* q, const void* k, in
   if (st) return st;
   if ((st = check_prefill_shape(desc))) return st;
   if (!q || !k || !perm) return fail(SPOT_ERR_INVALID, "q, k and perm are required");
+  if ((st = check_aligned16("q", q)) || (st = check_aligned16("k", k))) return st;
   if (desc->dtype != SPOT_BF16) return fail(SPOT_ERR_UNSUPPORTED, "key permutation supports bf16 only");
   if (desc->segment <= 0) return fail(SPOT_ERR_INVALID, "segment must be > 0");
   if (desc->segment > spot::kPermMaxSegment)

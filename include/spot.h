@@ -151,6 +151,10 @@ int spot_workspace_size(const spot_desc* desc, int op, size_t* bytes);
  * block t < nk
  *     scores[b,0,0,t] = sum_h idx_w[b,h] * max(0, < idx_q[b,h], idx_k[b,t,h] >)
  *   Uses idx_q, idx_w, idx_k; q, k, perm are ignored.
+ *
+ * Alignment: q and k (pooled scores) or idx_q and idx_k (indexer) must be
+ * 16-byte aligned (the kernels read rows in 16-byte pieces; SPOT_ERR_INVALID
+ * otherwise).
  */
 int spot_block_score(const spot_desc* desc, const void* q, const void* k, const int32_t* perm,
                      const void* idx_q, const float* idx_w, const void* idx_k, float* scores,
@@ -213,7 +217,8 @@ int spot_sparse_attn_decode(const spot_desc* desc, const void* q, const void* k_
  * q: [batch, hq, L, d] bf16; k: [batch, hkv, L, d] bf16; perm: int32
  * [batch, hkv, L] (output); importance: float [batch, hkv, L] (nullable
  * output).  Requires dtype bf16, segment > 0, a multiple of block and at most
- * 16384.  Workspace: spot_workspace_size(SPOT_OP_KEY_PERMUTATION).
+ * 16384, and q, k 16-byte aligned.  Workspace:
+ * spot_workspace_size(SPOT_OP_KEY_PERMUTATION).
  */
 int spot_key_permutation(const spot_desc* desc, const void* q, const void* k, int32_t* perm, float* importance,
                          void* workspace, size_t workspace_bytes, void* stream);
@@ -251,7 +256,8 @@ int spot_validate_perm(const spot_desc* desc, const int32_t* perm, int32_t* bad,
  *   keys read from the encoding (decoded value = E2M1 value * 2^(e-127)):
  *     scores[b,0,0,t] = sum_h idx_w[b,h] * max(0, < idx_q[b,h], key[b,t,h] >)
  * Both need score_kind RELU_INDEXER and the indexer limits of
- * spot_block_score; no workspace.
+ * spot_block_score, and idx_k, idx_q and k_codes 16-byte aligned; no
+ * workspace.
  */
 int spot_quantize_indexer_keys(const spot_desc* desc, const void* idx_k, uint8_t* k_codes, uint8_t* k_scales,
                                void* stream);
@@ -309,7 +315,7 @@ int spot_sparse_attn_prefill_early_stop(const spot_desc* desc, float tau, const 
  *   hmap[b,g,s,j] = -1 for j >= s*S, and all of segment 0.
  * q: [batch, hq, L, d] bf16; k: [batch, hkv, L, d] bf16; hmap: int32
  * [batch, hkv, nseg, L] (output), nseg = ceil(L / S).  Requires segment > 0,
- * nseg <= 64 and (nseg - 1) * S <= 32768.  Workspace:
+ * nseg <= 64, (nseg - 1) * S <= 32768 and q, k 16-byte aligned.  Workspace:
  * spot_workspace_size(SPOT_OP_HISTORY_MAP).  Scores are fp32, so keys whose
  * scores agree to fp32 rounding may be ordered differently from an exact
  * evaluation.

@@ -119,6 +119,9 @@ def test_null_and_missing_arguments():
     for kw in (dict(q=FAKE + 8), dict(k=FAKE + 4), dict(v=FAKE + 2), dict(o=FAKE + 4)):   # bf16: 16-byte q/k/v, 8-byte o
         assert call_prefill(_prefill(), **kw) == B.SPOT_ERR_INVALID, kw
     assert call_select(_prefill(), cnt=None) == B.SPOT_ERR_INVALID
+    for kw in (dict(q=FAKE + 8), dict(k=FAKE + 4)):      # pooled scores read q and k rows in 16-byte pieces
+        assert call_score(_prefill(), **kw) == B.SPOT_ERR_INVALID, kw
+        assert call_score(_prefill(dtype=B.SPOT_F32), **kw) == B.SPOT_ERR_INVALID, kw
 
 
 def test_selection_parameters():
@@ -142,6 +145,10 @@ def test_indexer_and_decode_validation():
     assert call_decode(_decode(), o=None) == B.SPOT_ERR_INVALID
     for kw in (dict(q=FAKE + 8), dict(k=FAKE + 4), dict(v=FAKE + 2), dict(ws=FAKE + 8)):   # 16-byte loads/stores
         assert call_decode(_decode(), **kw) == B.SPOT_ERR_INVALID, kw
+    for kw in (dict(iq=FAKE + 8), dict(ik=FAKE + 2)):    # indexer rows in 16-byte pieces
+        args = dict(iq=FAKE, iw=FAKE, ik=FAKE)
+        args.update(kw)
+        assert call_score(_decode(), q=None, k=None, **args) == B.SPOT_ERR_INVALID, kw
 
 
 def call_perm(d, q=FAKE, k=FAKE, perm=FAKE, ws=FAKE, ws_bytes=1 << 30):
@@ -157,6 +164,8 @@ def test_key_permutation_validation():
     assert call_perm(_prefill(segment=256), ws=None) == B.SPOT_ERR_WORKSPACE
     assert call_perm(_prefill(segment=256), ws_bytes=64) == B.SPOT_ERR_WORKSPACE
     assert B.spot_workspace_size(_prefill(segment=256), B.SPOT_OP_KEY_PERMUTATION) > 0
+    assert call_perm(_prefill(segment=256), q=FAKE + 8) == B.SPOT_ERR_INVALID
+    assert call_perm(_prefill(segment=256), k=FAKE + 2) == B.SPOT_ERR_INVALID
 
 
 def call_vperm(d, perm=FAKE, bad=FAKE):
@@ -246,6 +255,10 @@ def test_mxfp4_indexer_validation():
     assert q(_decode(), x=None) == B.SPOT_ERR_INVALID
     assert sc(_decode(), s=None) == B.SPOT_ERR_INVALID
     assert sc(_decode(), out=None) == B.SPOT_ERR_INVALID
+    assert q(_decode(), x=FAKE + 2) == B.SPOT_ERR_INVALID                  # 16-byte loads and stores
+    assert q(_decode(), c=FAKE + 8) == B.SPOT_ERR_INVALID
+    assert sc(_decode(), iq=FAKE + 4) == B.SPOT_ERR_INVALID
+    assert sc(_decode(), c=FAKE + 1) == B.SPOT_ERR_INVALID
 
 
 def test_history_map_validation():
@@ -263,6 +276,8 @@ def test_history_map_validation():
     assert hm(_prefill(segment=256), out=None) == B.SPOT_ERR_INVALID
     assert hm(_prefill(segment=256), ws=None) == B.SPOT_ERR_WORKSPACE
     assert hm(_prefill(segment=256), ws_bytes=16) == B.SPOT_ERR_WORKSPACE
+    assert hm(_prefill(segment=256), q=FAKE + 8) == B.SPOT_ERR_INVALID
+    assert hm(_prefill(segment=256), k=FAKE + 2) == B.SPOT_ERR_INVALID
     assert hm(_prefill(segment=64, q_len=64 * 65, kv_len=64 * 65)) == B.SPOT_ERR_UNSUPPORTED        # 65 segments
     assert hm(_prefill(segment=8192, q_len=8192 * 6, kv_len=8192 * 6)) == B.SPOT_ERR_UNSUPPORTED    # prefix 40960
     assert B.spot_workspace_size(_prefill(segment=256), B.SPOT_OP_HISTORY_MAP) > 0

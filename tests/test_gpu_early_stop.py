@@ -16,9 +16,14 @@ from tests.test_gpu_parity import log, upload_prefill
 pytestmark = pytest.mark.gpu
 
 # A row's stop point may differ from the exact rule only where the oracle's
-# gain ratio lies within this relative distance of tau: the kernel sums fp32
-# exponentials of bf16 products and rounds P to bf16 before summing.
-RATIO_REL = 1e-2
+# gain ratio lies within this relative distance of tau.  The kernel's ratio
+# is (sum of the block's P) / (sum of all P so far), every P rounded to bf16
+# (relative error at most 2^-8 per term, so at most 2^-8 on each sum; one
+# heavy key can carry a whole block's mass, so the bound is reached) and the
+# sums kept in fp32 (at most a few hundred tiles: below 1e-4 relative).  The
+# ratio is therefore within (1 + 2^-8) / (1 - 2^-8) - 1 + 1e-4 = 7.9e-3 of
+# the exact one.
+RATIO_REL = (1 + 2.0 ** -8) / (1 - 2.0 ** -8) - 1 + 1e-4
 
 
 def order_nested(order_np, cnt_np, b, hkv, blocks):
@@ -44,6 +49,7 @@ def es_check(cfg, host, order_np, cnt_np, bufs, tau, perm=None, pairs=None, hmap
         if pairs is None else pairs
     rows_total = exact = near = 0
     worst = worst_lse = 0.0
+    near_dev = 0.0   # largest |ratio / tau - 1| at a row whose stop point differs
     taken = 0
     for b, g, i in pairs:
         n_hist = ((i * cfg.block) // cfg.segment) * cfg.segment // cfg.block
@@ -68,6 +74,9 @@ def es_check(cfg, host, order_np, cnt_np, bufs, tau, perm=None, pairs=None, hmap
                     exact += 1
                 else:
                     near += 1
+                    # the first block where the two decisions part: one side stops there, the other goes on
+                    k_part = max(min(n, n_exact) - 1, 0)
+                    near_dev = max(near_dev, abs(float(ratio[ri, k_part]) / tau - 1.0))
                     # did not stop earlier than allowed, and stopped where the ratio was (nearly) below tau
                     assert np.all(ratio[ri, :max(n - 1, 0)] >= tau * (1 - RATIO_REL)), (b, h, r, n, n_exact)
                     assert n == n_hist or ratio[ri, n - 1] < tau * (1 + RATIO_REL), (b, h, r, n, n_exact)
@@ -83,9 +92,10 @@ def es_check(cfg, host, order_np, cnt_np, bufs, tau, perm=None, pairs=None, hmap
         worst = max(worst, P.max_abs(go[b, g * G:(g + 1) * G, rs], o_ref[:, rs]))
         worst_lse = max(worst_lse, P.max_abs(glse[b, g * G:(g + 1) * G, rs], lse_ref[:, rs]))
     log(cfg.name, f"tau={tau} rows={rows_total} exact stops={exact} within-rounding={near} "
-        f"history blocks taken={taken} max|dO|={worst:.3g} max|dLSE|={worst_lse:.3g}")
+        f"history blocks taken={taken} max|dO|={worst:.3g} max|dLSE|={worst_lse:.3g} "
+        f"largest |ratio/tau-1| at a differing stop={near_dev:.3g} (window {RATIO_REL:.3g})")
     assert worst <= P.BF16_ATOL, worst
-    assert worst_lse <= 10 * P.BF16_ATOL, worst_lse
+    assert worst_lse <= P.BF16_LSE_ATOL, worst_lse
     assert near <= max(2, rows_total // 100)
     return taken
 

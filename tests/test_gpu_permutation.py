@@ -15,8 +15,15 @@ from tests.test_gpu_parity import log, pipeline_check, upload_prefill
 
 pytestmark = pytest.mark.gpu
 
-IMP_RTOL = 2e-3     # importance: bf16 products, fp32 accumulation and exp2
-ORDER_RTOL = 1e-3   # two keys may swap order when their oracle importances are this close
+# Importance error relative to the row's largest importance.  Every
+# probability is exp(x - lse) of a logit x that is a bf16 x bf16 dot product
+# over d = 128 summed in fp32: at most d * 2^-24 * sum|q_c k_c| * scale, about
+# 3.4e-4 for a heavy-hitter key (norm 4x, |q||k| about 500); exp2, the lse and
+# the fp32 sums over the block's rows and the group's heads add about 1e-6.
+IMP_RTOL = 1e-3
+# Two keys may appear in either order only when their oracle importances are
+# this close (the selection window of the block lists).
+ORDER_RTOL = 1e-4
 
 
 def check_permutation(cfg, q, k, perm_gpu, imp_gpu):
