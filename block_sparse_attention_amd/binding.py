@@ -26,7 +26,7 @@ EXPORTS = ("spot_version", "spot_status_string", "spot_last_error", "spot_worksp
            "spot_select_topp", "spot_sparse_attn_prefill", "spot_sparse_attn_decode", "spot_key_permutation",
            "spot_order_history", "spot_sparse_attn_prefill_early_stop", "spot_quantize_indexer_keys",
            "spot_indexer_score_mxfp4", "spot_history_map", "spot_sparse_attn_prefill_history_map",
-           "spot_validate_perm")
+           "spot_validate_perm", "spot_sparse_attn_decode_noalloc")
 
 
 class spot_desc(ctypes.Structure):
@@ -77,6 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spot_sparse_attn_prefill_history_map.argtypes = [D, ctypes.c_float, P, P, P, P, P, P, P, P, S, P]
     lib.spot_sparse_attn_prefill_early_stop.argtypes = [D, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.spot_validate_perm.argtypes = [D, P, P, P]
+    lib.spot_sparse_attn_decode_noalloc.argtypes = [D, P, P, P, P, P, P, P, P]
     for name in EXPORTS[3:]:
         getattr(lib, name).restype = I
     _lib = lib
@@ -140,6 +141,13 @@ def spot_sparse_attn_decode(desc, q, k_cache, v_cache, idx, cnt, o, lse=None, wo
                                                 _ptr(idx), _ptr(cnt), _ptr(o), _ptr(lse), _ptr(workspace),
                                                 ws_bytes, _stream() if stream is None else stream)
     _check("spot_sparse_attn_decode", st)
+
+
+def spot_sparse_attn_decode_noalloc(desc, q, k_cache, v_cache, idx, cnt, o, lse=None, stream=None):
+    st = load_library().spot_sparse_attn_decode_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                        _ptr(idx), _ptr(cnt), _ptr(o), _ptr(lse),
+                                                        _stream() if stream is None else stream)
+    _check("spot_sparse_attn_decode_noalloc", st)
 
 
 def spot_key_permutation(desc, q, k, perm, importance=None, workspace=None, stream=None):

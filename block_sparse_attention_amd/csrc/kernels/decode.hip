@@ -17,6 +17,8 @@
 // decode_combine_kernel: merges the partials of the splits in split order
 //   (deterministic; all loads issued before the merge) and writes O (bf16)
 //   and the natural-log LSE.
+#include <mutex>
+
 #include "../launch.h"
 #include "common.h"
 
@@ -227,6 +229,33 @@ int decode_num_splits(int batch, int hkv, int nk) {
 
 size_t decode_partials_bytes(int batch, int hq, int d, int nsplit) {
   return size_t(batch) * hq * nsplit * (d + 2) * sizeof(float);
+}
+
+// Device-resident scratch of the allocation-free decode entry point: the
+// split partials of one call.  Each GPU the library runs on holds its own
+// copy until the process ends; every call on a GPU uses that GPU's copy, so
+// calls that overlap on one GPU race.  Nothing in it must start at zero: the
+// combine reads only the partials the same call's split workgroups wrote.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+hipError_t decode_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // the array's name is a host-side stand-in: its device address on this GPU comes from the runtime
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 template <int D, int G>

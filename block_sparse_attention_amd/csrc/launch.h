@@ -130,6 +130,10 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 int decode_num_splits(int batch, int hkv, int nk);
 size_t decode_partials_bytes(int batch, int hq, int d, int nsplit);
+// allocation-free decode: a file-scope device array of this size holds the partials; decode_scratch gives
+// its address on the current device (looked up once per device)
+constexpr size_t kDecodeScratchBytes = size_t(8) << 20;
+hipError_t decode_scratch(float** ptr);
 
 struct PermArgs {
   const uint16_t* q;   // [batch, hq, L, d] bf16

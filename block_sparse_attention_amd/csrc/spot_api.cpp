@@ -450,6 +450,34 @@ int spot_sparse_attn_decode(const spot_desc* desc, const void* q, const void* k_
   return launched(spot::launch_decode(a, static_cast<hipStream_t>(stream)), "sparse_attn_decode");
 }
 
+int spot_sparse_attn_decode_noalloc(const spot_desc* desc, const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* idx, const int32_t* cnt, void* o, float* lse, void* stream) {
+  int st = check_common(desc);
+  if (st) return st;
+  if (desc->q_len != 1) return fail(SPOT_ERR_INVALID, "decode needs q_len == 1");
+  if (desc->dtype != SPOT_BF16) return fail(SPOT_ERR_UNSUPPORTED, "decode supports bf16 only");
+  const int G = desc->hq / desc->hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(SPOT_ERR_UNSUPPORTED, "hq/hkv = %d (supported: 1, 2, 4, 8)", G);
+  if (!q || !k_cache || !v_cache || !idx || !cnt || !o) return fail(SPOT_ERR_INVALID, "q, k_cache, v_cache, idx, cnt and o are required");
+  if ((st = check_aligned16("q", q)) || (st = check_aligned16("k_cache", k_cache)) ||
+      (st = check_aligned16("v_cache", v_cache)))
+    return st;
+  const int nk = int(ceil_div64(desc->kv_len, desc->block));
+  const int ns = spot::decode_num_splits(desc->batch, desc->hkv, nk);
+  const size_t need = spot::decode_partials_bytes(desc->batch, desc->hq, desc->d, ns);
+  if (need > spot::kDecodeScratchBytes)
+    return fail(SPOT_ERR_UNSUPPORTED, "decode partials of %zu bytes exceed the built-in scratch of %zu bytes "
+                "(batch * hq too large for the allocation-free call)", need, spot::kDecodeScratchBytes);
+  float* scratch = nullptr;
+  hipError_t e = spot::decode_scratch(&scratch);
+  if (e != hipSuccess) return fail(SPOT_ERR_LAUNCH, "decode scratch address: %s", hipGetErrorString(e));
+  spot::DecodeArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+                     static_cast<const uint16_t*>(v_cache), idx, cnt, static_cast<uint16_t*>(o), lse, scratch,
+                     desc->batch, desc->hq, desc->hkv, desc->d, int(desc->kv_len), desc->block, nk, ns,
+                     effective_scale(desc)};
+  return launched(spot::launch_decode(a, static_cast<hipStream_t>(stream)), "sparse_attn_decode_noalloc");
+}
+
 int spot_key_permutation(const spot_desc* desc, const void* q, const void* k, int32_t* perm, float* importance,
                          void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_common(desc);

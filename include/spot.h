@@ -207,6 +207,24 @@ int spot_sparse_attn_decode(const spot_desc* desc, const void* q, const void* k_
                             float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Allocation-free variant of spot_sparse_attn_decode, for callers that cannot
+ * allocate device memory (code under stream/graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, layouts, result
+ * and errors as spot_sparse_attn_decode, without the workspace: the partials
+ * live in a device array built into the library (8 MiB on each GPU the
+ * library runs on, held until the process ends).  Inputs whose partials do
+ * not fit (batch * hq * nsplit * (d + 2) * 4 bytes above 8 MiB; nsplit is at
+ * most 32) return SPOT_ERR_UNSUPPORTED before anything is enqueued.  The call
+ * allocates nothing.  Every call on one GPU shares that GPU's array: calls
+ * that may overlap on one GPU (several streams, several threads) race and
+ * must be serialised by the caller.  The first call on each device looks up
+ * the array's address on that device (the device current at the call).
+ */
+int spot_sparse_attn_decode_noalloc(const spot_desc* desc, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* idx, const int32_t* cnt, void* o,
+                                    float* lse, void* stream);
+
+/*
  * Key permutation by global importance ([PBS] §3; index arrays as in [S2O] §1).
  * For KV head g, importance[t] = the causal softmax probability
  * softmax_{t' <= r}(sm_scale * q_{h,r} . k_{t'})[t], averaged over the query

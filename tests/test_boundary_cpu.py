@@ -151,6 +151,23 @@ def test_indexer_and_decode_validation():
         assert call_score(_decode(), q=None, k=None, **args) == B.SPOT_ERR_INVALID, kw
 
 
+def test_decode_noalloc_validation():
+    lib = B.load_library()
+
+    def call(d, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cnt=FAKE, o=FAKE):
+        return lib.spot_sparse_attn_decode_noalloc(ctypes.byref(d), q, k, v, idx, cnt, o, None, None)
+
+    assert call(_decode(q_len=2)) == B.SPOT_ERR_INVALID
+    assert call(_decode(dtype=B.SPOT_F32)) == B.SPOT_ERR_UNSUPPORTED
+    assert call(_decode(hq=12, hkv=4)) == B.SPOT_ERR_UNSUPPORTED
+    assert call(_decode(), o=None) == B.SPOT_ERR_INVALID
+    for kw in (dict(q=FAKE + 8), dict(k=FAKE + 4), dict(v=FAKE + 2)):
+        assert call(_decode(), **kw) == B.SPOT_ERR_INVALID, kw
+    # partials beyond the built-in 8 MiB scratch: 512 sequences x 32 heads x 1 split x 130 floats
+    assert call(_decode(batch=512, hq=32, hkv=4)) == B.SPOT_ERR_UNSUPPORTED
+    assert b"scratch" in lib.spot_last_error()
+
+
 def call_perm(d, q=FAKE, k=FAKE, perm=FAKE, ws=FAKE, ws_bytes=1 << 30):
     return B.load_library().spot_key_permutation(ctypes.byref(d), q, k, perm, None, ws, ws_bytes, None)
 
