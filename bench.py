@@ -50,6 +50,8 @@ def parse():
                     help="prefill workload of the headline step: long-bf16-L131072 (default), gqa-bf16-L8192, "
                          "heavy-perm-bf16-L32768 (permutation generated on the GPU inside the step), tiny-fp32-L256")
     ap.add_argument("--headline-only", action="store_true", help="time the headline workload only")
+    ap.add_argument("--configs", default="",
+                    help="comma-separated workloads to time besides the headline (default: every one)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-early-stop", action="store_true", help="skip the early-stopping measurements")
@@ -686,8 +688,9 @@ def main():
     else:
         del head_dev
         torch.cuda.empty_cache()
+        wanted = set(x for x in args.configs.split(",") if x) or None
         for c in (I.C1, I.C2, I.C3, I.C5):
-            if c.name == head_cfg.name:
+            if c.name == head_cfg.name or (wanted is not None and c.name not in wanted):
                 continue
             cfg, host = prefill_host(I, c.name)
             dev_in = prefill_device(torch, cfg, host)
@@ -710,7 +713,7 @@ def main():
             say(f"{cfg.name}: {obj}")
             del dev_in
             torch.cuda.empty_cache()
-        if not args.no_decode:
+        if not args.no_decode and (wanted is None or I.C4.name in wanted):
             dcfg, t = decode_device(torch, B, I)
             dec = {"bf16_indexer": bench_decode(args, torch, B, dcfg, t)}
             say(f"decode: {dec['bf16_indexer']}")

@@ -4,8 +4,9 @@
 // kept 16-token blocks.  The step is bound by reading the kept part of the KV
 // cache (SpotAttention "Probleemstelling": every decode step re-reads a cache
 // that grows with the context), so the kernel streams rows with 16-byte
-// loads, several blocks in flight per thread, and keeps the arithmetic on the
-// VALU (bf16 pair dot products, fp32 accumulation).
+// loads, the next round's loads issued before the current round is used, and
+// keeps the arithmetic on the VALU (bf16 pair dot products, fp32
+// accumulation).
 //
 // decode_split_kernel: workgroup = (split s, KV head g, sequence b).  Split s
 //   takes kept blocks s, s + nsplit, s + 2*nsplit, ... of sequence b, so the
@@ -45,11 +46,11 @@ template <> struct DVec<4> {
   static __device__ __forceinline__ uint32_t w(const T& v, int k) { return k == 0 ? v.x : v.y; }
 };
 
-template <int D, int G>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a, float scale_log2) {
+template <int D, int G, int NT>
+__global__ __launch_bounds__(NT) void decode_split_kernel(DecodeArgs a, float scale_log2) {
   constexpr int EPL = D / 16;           // elements per lane
-  constexpr int KS = kDecThreads / 16;  // key-slot streams per workgroup
-  static_assert(KS == 16, "a round's slot u exists for all streams or none when KS divides the block");
+  constexpr int KS = NT / 16;           // key-slot streams per workgroup
+  constexpr int U = kDecUnroll;         // slots per stream and round
   using V = DVec<EPL>;
   __shared__ float s_m[KS][G], s_l[KS][G];
   __shared__ float s_acc[KS][G][D];
@@ -57,127 +58,146 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a,
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, c = tid & 15, ks = tid >> 4;
   const int B = a.block, T = a.T;
+  const int lgB = 31 - __builtin_clz(B);
   const int32_t* il = a.idx + size_t(b) * a.nk;
-  // this split's first kDecUnroll block ids, loaded beside the count
-  int pre[kDecUnroll];
+  // block ids of this split's first round, loaded beside the count (stream ks, slot u of round 0 is
+  // key (ks + KS u) mod B of local block (ks + KS u) / B, i.e. kept block s + nsplit (ks + KS u) / B)
+  int ids[U];
 #pragma unroll
-  for (int u = 0; u < kDecUnroll; ++u) {
-    const int bi = s + u * a.nsplit;
-    pre[u] = il[bi < a.nk ? bi : 0];
+  for (int u = 0; u < U; ++u) {
+    const int bi = s + ((ks + KS * u) >> lgB) * a.nsplit;
+    ids[u] = il[bi < a.nk ? bi : 0];
   }
   const int n = a.cnt[b];
   if (s >= n) return;   // the combine reads splits [0, min(n, nsplit)) only
-  const int nmine = (n - s + a.nsplit - 1) / a.nsplit;   // blocks s, s+nsplit, ... below n
-  const int nslots = nmine * B;
-  const size_t kvbase = (size_t(b) * a.hkv + g) * size_t(T) * D;
-  const uint16_t* Kg = a.k + kvbase;
-  const uint16_t* Vg = a.v + kvbase;
+  const size_t pair = size_t(b) * a.hkv + g;
+  const int nmine = (n - s + a.nsplit - 1) / a.nsplit;   // blocks s, s + nsplit, ... below n
 
-  typename V::T qv[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) qv[hh] = V::ld(a.q + (size_t(b) * a.hq + g * G + hh) * D + c * EPL);
+  {
+    const int nslots = nmine * B;
+    const int nj = ks < nslots ? (nslots - ks + KS - 1) / KS : 0;   // this stream's slots
+    const int nrounds = ((nslots + KS - 1) / KS + U - 1) / U;
+    const size_t kvbase = pair * size_t(T) * D;
+    const uint16_t* Kg = a.k + kvbase;
+    const uint16_t* Vg = a.v + kvbase;
 
-  float m[G], l[G], acc[G][EPL];
+    typename V::T qv[G];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    m[hh] = -kInf;
-    l[hh] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
-  }
+    for (int hh = 0; hh < G; ++hh) qv[hh] = V::ld(a.q + (size_t(b) * a.hq + g * G + hh) * D + c * EPL);
 
-  // slot = (local block k, key j); stream ks walks keys ks, ks + KS, ...
-  for (int base = ks; base < nslots; base += KS * kDecUnroll) {
-    typename V::T kv[kDecUnroll], vv[kDecUnroll];
-    bool ok[kDecUnroll];
+    float m[G], l[G], acc[G][EPL];
 #pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
-      const int sl = base + u * KS;
-      ok[u] = false;
-      kv[u] = V::zero();
-      vv[u] = V::zero();
-      if (sl < nslots) {
-        const int kb = sl / B;
-        int blk;
-        if (kb < kDecUnroll) {
-          blk = pre[0];
+    for (int hh = 0; hh < G; ++hh) {
+      m[hh] = -kInf;
+      l[hh] = 0.f;
 #pragma unroll
-          for (int u2 = 1; u2 < kDecUnroll; ++u2) blk = (kb == u2) ? pre[u2] : blk;
-        } else {
-          blk = il[s + kb * a.nsplit];
+      for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
+    }
+
+    // slot j of stream ks is slot ks + KS j of the split: key (ks + KS j) mod B of local block (ks + KS j) / B
+    auto block_ids = [&](int r, int (&out)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int sl = ks + KS * (r * U + u);
+        out[u] = sl < nslots ? il[s + (sl >> lgB) * a.nsplit] : 0;
+      }
+    };
+    auto issue = [&](int r, const int (&bid)[U], typename V::T (&kv)[U], typename V::T (&vv)[U], bool (&ok)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int sl = ks + KS * (r * U + u);
+        const int pos = (bid[u] << lgB) + (sl & (B - 1));
+        ok[u] = sl < nslots && pos < T;
+        kv[u] = ok[u] ? V::ld(Kg + size_t(pos) * D + c * EPL) : V::zero();
+        vv[u] = ok[u] ? V::ld(Vg + size_t(pos) * D + c * EPL) : V::zero();
+      }
+    };
+    auto consume = [&](int r, const typename V::T (&kv)[U], const typename V::T (&vv)[U], const bool (&ok)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // the 16 lanes of a stream agree on whether its slot exists: skip empty slots whole
+        if (r * U + u >= nj) break;
+        float vf[EPL];
+#pragma unroll
+        for (int k2 = 0; k2 < EPL / 2; ++k2) {
+          const uint32_t w = V::w(vv[u], k2);
+          vf[2 * k2] = bf16_lo(w);
+          vf[2 * k2 + 1] = bf16_hi(w);
         }
-        const int pos = blk * B + sl % B;
-        if (pos < T) {
-          ok[u] = true;
-          kv[u] = V::ld(Kg + size_t(pos) * D + c * EPL);
-          vv[u] = V::ld(Vg + size_t(pos) * D + c * EPL);
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          float dp = 0.f;
+#pragma unroll
+          for (int k2 = 0; k2 < EPL / 2; ++k2) dp = dot2_bf16(V::w(kv[u], k2), V::w(qv[hh], k2), dp);
+          dp = row16_sum(dp);
+          if (!ok[u]) continue;
+          const float x = dp * scale_log2;
+          if (x > m[hh] + kDecRescale) {
+            const float alpha = __builtin_amdgcn_exp2f(m[hh] - x);
+            l[hh] *= alpha;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[hh][e] *= alpha;
+            m[hh] = x;
+          }
+          const float p = __builtin_amdgcn_exp2f(x - m[hh]);
+          l[hh] += p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(p, vf[e], acc[hh][e]);
         }
       }
-    }
-#pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
-      // slot base + u KS exists for every stream or for none (nslots is a
-      // multiple of 16 = KS for blocks of 16 or more): skip empty slots whole
-      if (base - ks + u * KS >= nslots) break;
-      float vf[EPL];
-#pragma unroll
-      for (int k2 = 0; k2 < EPL / 2; ++k2) {
-        const uint32_t w = V::w(vv[u], k2);
-        vf[2 * k2] = bf16_lo(w);
-        vf[2 * k2 + 1] = bf16_hi(w);
-      }
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float dp = 0.f;
-#pragma unroll
-        for (int k2 = 0; k2 < EPL / 2; ++k2) dp = dot2_bf16(V::w(kv[u], k2), V::w(qv[hh], k2), dp);
-        dp = row16_sum(dp);
-        if (!ok[u]) continue;
-        const float x = dp * scale_log2;
-        if (x > m[hh] + kDecRescale) {
-          const float alpha = __builtin_amdgcn_exp2f(m[hh] - x);
-          l[hh] *= alpha;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[hh][e] *= alpha;
-          m[hh] = x;
-        }
-        const float p = __builtin_amdgcn_exp2f(x - m[hh]);
-        l[hh] += p;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(p, vf[e], acc[hh][e]);
-      }
-    }
-  }
+    };
 
-  // merge the KS slot streams
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    if (c == 0) {
-      s_m[ks][hh] = m[hh];
-      s_l[ks][hh] = l[hh];
-    }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) s_acc[ks][hh][c * EPL + e] = acc[hh][e];
-  }
-  __syncthreads();
-  float* part = a.partials + ((size_t(b) * a.hkv + g) * a.nsplit + s) * G * (D + 2);
-  for (int o = tid; o < G * D; o += kDecThreads) {
-    const int hh = o / D, dd = o % D;
-    float M = -kInf;
-    for (int q = 0; q < KS; ++q) M = fmaxf(M, s_m[q][hh]);
-    float A = 0.f, Lsum = 0.f;
-    if (M != -kInf) {
-      for (int q = 0; q < KS; ++q) {
-        const float f = __builtin_amdgcn_exp2f(s_m[q][hh] - M);
-        A = fmaf(s_acc[q][hh][dd], f, A);
-        Lsum = fmaf(s_l[q][hh], f, Lsum);
+    // two register sets alternate: round r + 1's loads are in flight while round r is consumed, and round
+    // r + 2's block ids while round r + 1's loads are issued
+    typename V::T ka[U], va[U], kb2[U], vb[U];
+    bool oka[U], okb[U];
+    issue(0, ids, ka, va, oka);
+    block_ids(1, ids);
+    int r = 0;
+    for (; r + 1 < nrounds; r += 2) {
+      issue(r + 1, ids, kb2, vb, okb);
+      block_ids(r + 2, ids);
+      consume(r, ka, va, oka);
+      if (r + 2 < nrounds) {
+        issue(r + 2, ids, ka, va, oka);
+        block_ids(r + 3, ids);
       }
+      consume(r + 1, kb2, vb, okb);
     }
-    float* ph = part + hh * (D + 2);
-    ph[dd] = A;
-    if (dd == 0) {
-      ph[D] = M;
-      ph[D + 1] = Lsum;
+    if (r < nrounds) consume(r, ka, va, oka);
+
+    // merge the KS slot streams through LDS
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      if (c == 0) {
+        s_m[ks][hh] = m[hh];
+        s_l[ks][hh] = l[hh];
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[ks][hh][c * EPL + e] = acc[hh][e];
+    }
+    __syncthreads();
+    float* part = a.partials + (pair * a.nsplit + s) * G * (D + 2);
+    for (int o = tid; o < G * D; o += NT) {
+      const int hh = o / D, dd = o % D;
+      float M = -kInf;
+#pragma unroll
+      for (int q = 0; q < KS; ++q) M = fmaxf(M, s_m[q][hh]);
+      float A = 0.f, Lsum = 0.f;
+      if (M != -kInf) {
+#pragma unroll
+        for (int q = 0; q < KS; ++q) {
+          const float f = __builtin_amdgcn_exp2f(s_m[q][hh] - M);
+          A = fmaf(s_acc[q][hh][dd], f, A);
+          Lsum = fmaf(s_l[q][hh], f, Lsum);
+        }
+      }
+      float* ph = part + hh * (D + 2);
+      ph[dd] = A;
+      if (dd == 0) {
+        ph[D] = M;
+        ph[D + 1] = Lsum;
+      }
     }
   }
 }
@@ -260,7 +280,7 @@ hipError_t decode_scratch(float** ptr) {
 
 template <int D, int G>
 static hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, float scale_log2) {
-  decode_split_kernel<D, G><<<dim3(a.nsplit, a.hkv, a.batch), kDecThreads, 0, s>>>(a, scale_log2);
+  decode_split_kernel<D, G, kDecThreads><<<dim3(a.nsplit, a.hkv, a.batch), kDecThreads, 0, s>>>(a, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   decode_combine_kernel<D, G><<<dim3(a.hq, a.batch), D, 0, s>>>(a);

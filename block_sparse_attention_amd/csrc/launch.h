@@ -123,7 +123,7 @@ struct DecodeArgs {
   const int32_t* cnt;  // [batch]
   uint16_t* o;         // [batch, hq, d]
   float* lse;          // nullable
-  float* partials;     // workspace
+  float* partials;     // workspace: [batch, hkv, nsplit, G, d + 2] fp32 (acc, max, sum)
   int batch, hq, hkv, d, T, block, nk, nsplit;
   float sm_scale;
 };
