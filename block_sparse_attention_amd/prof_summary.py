@@ -26,20 +26,23 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 KDIR = os.path.join(PKG, "csrc", "kernels")
 COPY_BYTES = 1 << 30
 
-# kernel-name fragment -> (source file, workload key, launches used).  The
-# profiling workload runs its parts in a fixed order (GQA prefill, decode with
-# the bf16 indexer cache, decode with the MXFP4 cache, early-stopped
-# heavy-hitter prefill), so "first" takes the first `--steps` launches of a
-# kernel that several parts use, "all" every launch.
-TRACKED = {
-    "prefill_mfma_kernel<128, 8, 1, false, false, true>": ("prefill.hip", "prefill_mfma_kernel@gqa-bf16-L8192", "all"),
-    "prefill_mfma_kernel<128, 8, 1, true, true, true>": ("prefill.hip",
-                                                         "prefill_mfma_kernel_early_stop@heavy-perm-bf16-L32768", "all"),
-    "decode_split_kernel<128, 4>": ("decode.hip", "decode_split_kernel@decode-b16-T131072", "first"),
-    "indexer_score_kernel<": ("score.hip", "indexer_score_kernel@decode-b16-T131072", "all"),
-    "indexer_score_mxfp4_kernel": ("score.hip", "indexer_score_mxfp4_kernel@decode-b16-T131072", "all"),
-    "pool_blocks_kernel<unsigned short>": ("score.hip", "pool_blocks_kernel@gqa-bf16-L8192", "first"),
-}
+# (kernel-name fragment, source file, workload key, first, count): the launches
+# of that kernel from position first * steps to (first + count) * steps - 1,
+# in the profiling workload's fixed order (long-context prefill, GQA prefill,
+# decode with the bf16 indexer cache, with the MXFP4 cache, keeping every
+# block, early-stopped heavy-hitter prefill); count 0 takes every launch.
+TRACKED = [
+    ("prefill_mfma_kernel<128, 8, 1, false, false, true>", "prefill.hip", "prefill_mfma_kernel@long-bf16-L131072", 0, 1),
+    ("prefill_mfma_kernel<128, 8, 1, false, false, true>", "prefill.hip", "prefill_mfma_kernel@gqa-bf16-L8192", 1, 1),
+    ("prefill_mfma_kernel<128, 8, 1, true, true, true>", "prefill.hip",
+     "prefill_mfma_kernel_early_stop@heavy-perm-bf16-L32768", 0, 0),
+    ("decode_split_kernel<128, 4", "decode.hip", "decode_split_kernel@decode-b16-T131072", 0, 1),
+    ("decode_split_kernel<128, 4", "decode.hip", "decode_split_kernel@decode-b16-T131072-keep-all", 2, 1),
+    ("indexer_score_kernel<", "score.hip", "indexer_score_kernel@decode-b16-T131072", 0, 1),
+    ("indexer_score_mxfp4_kernel", "score.hip", "indexer_score_mxfp4_kernel@decode-b16-T131072", 0, 0),
+    ("pool_blocks_kernel<unsigned short>", "score.hip", "pool_blocks_kernel@long-bf16-L131072", 0, 1),
+    ("pool_blocks_kernel<unsigned short>", "score.hip", "pool_blocks_kernel@gqa-bf16-L8192", 1, 1),
+]
 
 
 def digest(path: str) -> str:
@@ -186,14 +189,17 @@ def main():
                   "", f"Calibration on a 1 GiB device copy: FETCH_SIZE reads {ff:.4f} x the bytes moved, "
                   f"WRITE_SIZE {wf:.4f} x; measured values below are divided by these factors.", "",
                   "| kernel | launches | fetch MB | write MB | total MB |", "|---|---:|---:|---:|---:|"]
-        for frag, (src, key, use) in TRACKED.items():
+        for frag, src, key, first, count in TRACKED:
             fk = [k for k in fv if frag in k]
             wk = [k for k in wv if frag in k]
             if not fk or not wk:
                 continue
             fl, wl = fv[fk[0]], wv[wk[0]]
-            if use == "first":
-                fl, wl = fl[:args.steps], wl[:args.steps]
+            if count:
+                fl = fl[first * args.steps:(first + count) * args.steps]
+                wl = wl[first * args.steps:(first + count) * args.steps]
+            if not fl or not wl:
+                continue
             fetch = statistics.median(fl) * 1024 / ff
             write = statistics.median(wl) * 1024 / wf
             lines.append(f"| `{frag}` ({key.split('@')[1]}) | {len(fl)} | {fetch / 1e6:.2f} | {write / 1e6:.2f} | "
