@@ -13,7 +13,8 @@ from dataclasses import dataclass
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libspot.so")
+# SPOT_LIBRARY names another build of the same library (for example the host-sanitizer build)
+LIB_PATH = os.environ.get("SPOT_LIBRARY") or os.path.join(_PKG, "libspot.so")
 
 SPOT_OK, SPOT_ERR_INVALID, SPOT_ERR_UNSUPPORTED, SPOT_ERR_WORKSPACE, SPOT_ERR_LAUNCH = 0, -1, -2, -3, -4
 SPOT_F32, SPOT_BF16 = 0, 1

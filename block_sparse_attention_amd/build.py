@@ -1,6 +1,13 @@
 """Builds libspot.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-Usage: python -m block_sparse_attention_amd.build [-v]
+Usage: python -m block_sparse_attention_amd.build [-v] [--sanitize]
+
+--sanitize builds _build_san/libspot_san.so instead: the same sources with
+the host code (the C ABI's validation, sizing and dispatch) instrumented by
+AddressSanitizer and UndefinedBehaviorSanitizer; device code is compiled as
+usual (the sanitizers are passed to the host pass only).  It runs the CPU
+boundary tests with the clang sanitizer runtime preloaded
+(tests/test_boundary_sanitized.py).
 """
 from __future__ import annotations
 
@@ -47,19 +54,34 @@ def _run(cmd: list[str], verbose: bool) -> None:
             sys.stderr.write("\n".join(lines) + "\n")
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every source and link libspot.so; returns the library path."""
-    os.makedirs(OBJDIR, exist_ok=True)
+SAN_DIR = os.path.join(PKG, "_build_san")
+SAN_LIB = os.path.join(SAN_DIR, "libspot_san.so")
+
+
+def host_sanitizer_flags() -> list[str]:
+    """Host-pass-only sanitizer options (each one behind -Xarch_host)."""
+    out = []
+    for opt in ("-fsanitize=" + kind for kind in ("address", "undefined")):
+        out += ["-Xarch_host", opt]
+    return out + ["-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = False, jobs: int | None = None, sanitize: bool = False) -> str:
+    """Compile every source and link libspot.so (or the host-sanitizer build); returns the library path."""
+    objdir, lib = (SAN_DIR, SAN_LIB) if sanitize else (OBJDIR, LIB)
+    flags = FLAGS + (host_sanitizer_flags() + ["-g"] if sanitize else [])
+    os.makedirs(objdir, exist_ok=True)
     srcs = sources()
-    objs = [os.path.join(OBJDIR, os.path.basename(s) + ".o") for s in srcs]
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
     jobs = jobs or min(8, os.cpu_count() or 1)
     with ThreadPoolExecutor(jobs) as ex:
-        list(ex.map(lambda so: _run([HIPCC, *FLAGS, "-c", so[0], "-o", so[1]], verbose), zip(srcs, objs)))
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+        list(ex.map(lambda so: _run([HIPCC, *flags, "-c", so[0], "-o", so[1]], verbose), zip(srcs, objs)))
+    tmp = lib + ".tmp"
+    link = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}"] + (host_sanitizer_flags() if sanitize else [])
+    _run(link + [*objs, "-o", tmp], verbose)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))
