@@ -26,7 +26,10 @@
 namespace spot {
 
 constexpr int kDecThreads = 256;
-constexpr int kDecUnroll = 4;
+#ifndef SPOT_DECODE_UNROLL
+#define SPOT_DECODE_UNROLL 2      // key slots per stream and load round: 112 VGPRs (4: 150) (tuning knob)
+#endif
+constexpr int kDecUnroll = SPOT_DECODE_UNROLL;
 constexpr float kDecRescale = 8.0f;
 constexpr int kDecMaxSplits = 32;
 
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
 }
 
 #ifndef SPOT_DECODE_TARGET_WGS
-#define SPOT_DECODE_TARGET_WGS 1536   // split workgroups per step: 1280-1792 measured 7% faster than 2048 (tuning knob)
+#define SPOT_DECODE_TARGET_WGS 1024   // split workgroups per step: 512-1536 measured, 1024 best overall (tuning knob)
 #endif
 
 int decode_num_splits(int batch, int hkv, int nk) {
