@@ -27,6 +27,9 @@ What each function follows:
   mxfp4_dequantize   format is the OCP Microscaling (MX) v1.0 MXFP4 element
                      and scale encoding: FP4 E2M1 elements, one E8M0
                      power-of-two scale per 32 elements
+  int4_quantize,     [Spot] §4 (selector K-cache in INT4 microscaling): groups
+  int4_dequantize    of 32 elements with one bf16 scale max|x|/7, elements
+                     rounded to integers in [-7, 7], ties to even
   key_block_variance [SPLA] §2.1 (block statistics: per-dimension variance,
                      the diagonal of the block covariance)
   taylor_scores      [SPLA] §2.1 second-order Taylor block score, as a log mass
@@ -64,6 +67,11 @@ MXFP4: the shared exponent is floor(log2(max |x|)) - 2 (the largest E2M1
 exponent), clamped to the E8M0 range, -127 for an all-zero group; elements
 are rounded to the nearest E2M1 value, ties to the even code, and saturate at
 6; the sign bit is the input's sign bit (so -0 keeps its sign).
+INT4: symmetric integers in [-7, 7] with one scale per 32 elements, the
+scale being max|x| / 7 rounded to bf16 (4.5 bits per element, 16 / 4.5 =
+3.56x smaller than bf16, the page's "about 3.5x"); x / scale rounded to the
+nearest integer with ties to the even one, clamped; an all-zero group has
+scale 0 and codes 0.
 Representative query: the mean of Q over the group's heads and the segment's
 rows; the history map sorts the prefix by sm_scale * <representative, key>
 descending, ties by position; early-stopped attention on the map visits its
@@ -243,6 +251,53 @@ def mxfp4_unpack(packed):
     out[..., 0::2] = packed & 15
     out[..., 1::2] = packed >> 4
     return out
+
+
+# ----------------------------------------------------------------- INT4 indexer keys
+INT4_GROUP = 32
+INT4_MAX = 7
+
+
+def _round_bf16(x):
+    """float64 values rounded to the nearest bf16 value (8 significant bits), ties to even; bf16 has the
+    float32 exponent range, so below 2^-126 the spacing stays 2^-133."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(a)                                  # a = m * 2**ex, 0.5 <= m < 1
+    ulp = np.exp2(np.maximum(ex.astype(np.float64) - 8.0, -133.0))
+    r = np.rint(a / ulp) * ulp                           # a / ulp is exact; rint: ties to even
+    return np.where(a == 0, 0.0, np.sign(x) * r)
+
+
+def int4_quantize(x):
+    """[Spot] §4 INT4 microscaling of the selector keys.
+
+    Groups of 32 consecutive elements share one scale s = max|x| / 7 rounded to
+    bf16; each element is round(x / s) to the nearest integer (ties to the even
+    one), clamped to [-7, 7] (0 for an all-zero group, whose scale is 0).
+    x: (..., n) with n a multiple of 32.  Returns codes int8 (..., n) and scales
+    float64 (..., n // 32) holding bf16 values.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    shape = x.shape
+    g = x.reshape(-1, INT4_GROUP)
+    scales = _round_bf16(np.abs(g).max(axis=1) / INT4_MAX)
+    safe = np.where(scales > 0, scales, 1.0)
+    codes = np.clip(np.rint(g / safe[:, None]), -INT4_MAX, INT4_MAX)
+    codes = np.where(scales[:, None] > 0, codes, 0.0).astype(np.int8)
+    return codes.reshape(shape), scales.reshape(shape[:-1] + (shape[-1] // INT4_GROUP,))
+
+
+def int4_dequantize(codes, scales):
+    """Values of INT4 codes: code * scale of its group."""
+    codes = np.asarray(codes, dtype=np.float64)
+    return codes * np.repeat(np.asarray(scales, dtype=np.float64), INT4_GROUP, axis=-1)
+
+
+def int4_pack(codes):
+    """Two 4-bit two's-complement codes per byte: element 2k in the low nibble, 2k+1 in the high one."""
+    u = (np.asarray(codes, dtype=np.int16) & 15).astype(np.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
 
 
 # ----------------------------------------------------------------- D1 indexer score
@@ -630,13 +685,17 @@ def prefill(q, k, v, block, top_p, n_sink=1, n_recent=1, k_min=0, sm_scale=None,
 def decode(q, k_cache, v_cache, idx_q, idx_w, idx_k, block, T, top_p, n_sink=1, n_recent=1,
            k_min=0, sm_scale=None, idx_format="bf16"):
     """Whole decode step for one sequence: indexer score -> select -> attend.
-    idx_format "mxfp4": the indexer keys are scored from their MXFP4 encoding."""
+    idx_format "mxfp4" or "int4": the indexer keys are scored from that encoding."""
     d = q.shape[-1]
     sm_scale = 1.0 / np.sqrt(d) if not sm_scale else sm_scale
     if idx_format == "mxfp4":
         nt, h_idx, d_idx = idx_k.shape
         codes, scales = mxfp4_quantize(np.asarray(idx_k, dtype=np.float64).reshape(nt, h_idx * d_idx))
         idx_k = mxfp4_dequantize(codes, scales).reshape(nt, h_idx, d_idx)
+    elif idx_format == "int4":
+        nt, h_idx, d_idx = idx_k.shape
+        codes, scales = int4_quantize(np.asarray(idx_k, dtype=np.float64).reshape(nt, h_idx * d_idx))
+        idx_k = int4_dequantize(codes, scales).reshape(nt, h_idx, d_idx)
     s = indexer_scores(idx_q, idx_w, idx_k)
     kept = select_decode(s, n_sink, n_recent, top_p, k_min)
     o, lse = attend_decode(q, k_cache, v_cache, kept, block, T, sm_scale)

@@ -21,6 +21,7 @@ PINS = "tests/test_oracle_pins.py"
 ES = "tests/test_oracle_early_stop.py"
 TAYLOR = "tests/test_oracle_taylor.py"
 MXFP4 = "tests/test_oracle_mxfp4.py"
+INT4 = "tests/test_oracle_int4.py"
 S2O = "tests/test_oracle_s2o_map.py"
 
 # (name, pin file, line fragment as written in the oracle, planted mistake)
@@ -68,6 +69,17 @@ MUTANTS = [
      "hmap[g, sg, :n] = ts[np.lexsort((ts, -c))]", "hmap[g, sg, :n] = ts[np.lexsort((ts, c))]"),
     ("history map ties by descending position", S2O,
      "hmap[g, sg, :n] = ts[np.lexsort((ts, -c))]", "hmap[g, sg, :n] = ts[np.lexsort((-ts, -c))]"),
+    ("INT4 scale from max / 8", INT4,
+     "scales = _round_bf16(np.abs(g).max(axis=1) / INT4_MAX)",
+     "scales = _round_bf16(np.abs(g).max(axis=1) / (INT4_MAX + 1))"),
+    ("INT4 scale not rounded to bf16", INT4,
+     "scales = _round_bf16(np.abs(g).max(axis=1) / INT4_MAX)", "scales = np.abs(g).max(axis=1) / INT4_MAX"),
+    ("INT4 ties away from zero", INT4,
+     "codes = np.clip(np.rint(g / safe[:, None]), -INT4_MAX, INT4_MAX)",
+     "codes = np.clip(np.trunc(g / safe[:, None] + np.copysign(0.5, g)), -INT4_MAX, INT4_MAX)"),
+    ("INT4 ties upward", INT4,
+     "codes = np.clip(np.rint(g / safe[:, None]), -INT4_MAX, INT4_MAX)",
+     "codes = np.clip(np.floor(g / safe[:, None] + 0.5), -INT4_MAX, INT4_MAX)"),
     ("MXFP4 scale one power of two too large", MXFP4,
      "np.clip(ex.astype(np.int64) - 1 - 2, -127, 127)", "np.clip(ex.astype(np.int64) - 1 - 1, -127, 127)"),
 ]
