@@ -15,8 +15,9 @@ float64 oracle timed on the host cores over 64 seeded query blocks of the same
 workload, and under `configs` one object per synthetic workload: the tiny fp32
 prefill (time only), the GQA prefill (with the keep-all reference and the
 Taylor score), the heavy-hitter prefill with the GPU key permutation inside
-the step (plus the early-stopping variants), the sparse decode step (bf16 and
-MXFP4 indexer caches, and a keep-all run that streams the whole KV cache) and
+the step (plus the early-stopping variants), the sparse decode step (bf16,
+MXFP4 and INT4 indexer caches, and a keep-all run that streams the whole KV
+cache) and
 the long prefill's keep-all reference.
 """
 from __future__ import annotations
@@ -282,11 +283,12 @@ def decode_device(torch, B, I):
              iw=torch.from_numpy(D["idx_w"]).to(dev))
     del D
     t["codes"], t["scales"] = B.quantize_indexer_keys(t["ik"], cfg.block, cfg.T)
+    t["codes4"], t["scales4"] = B.quantize_indexer_keys_int4(t["ik"], cfg.block, cfg.T)
     torch.cuda.synchronize()
     return cfg, t
 
 
-def bench_decode(args, torch, B, cfg, t, mxfp4=False, top_p=None):
+def bench_decode(args, torch, B, cfg, t, cache="bf16", top_p=None):
     dev = torch.device("cuda:0")
     top_p = cfg.top_p if top_p is None else top_p
     q, kc, vc, iq, iw = t["q"], t["kc"], t["vc"], t["iq"], t["iw"]
@@ -295,8 +297,10 @@ def bench_decode(args, torch, B, cfg, t, mxfp4=False, top_p=None):
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
 
     def score():
-        if mxfp4:
+        if cache == "mxfp4":
             B.spot_indexer_score_mxfp4(desc, iq, iw, t["codes"], t["scales"], bufs.scores)
+        elif cache == "int4":
+            B.spot_indexer_score_int4(desc, iq, iw, t["codes4"], t["scales4"], bufs.scores)
         else:
             B.spot_block_score(desc, None, None, None, iq, iw, t["ik"], bufs.scores)
 
@@ -346,12 +350,13 @@ def bench_decode(args, torch, B, cfg, t, mxfp4=False, top_p=None):
     bs = np.minimum(cfg.block, cfg.T - np.arange(cfg.nt) * cfg.block)
     kept_keys = np.array([bs[idx[b, :cnt[b]]].sum() for b in range(cfg.batch)], dtype=np.float64)
     kv_bytes = float(kept_keys.sum()) * cfg.hkv * cfg.d * 2 * 2
-    scan_bytes = cfg.batch * cfg.nt * cfg.h_idx * cfg.d_idx * (0.5 + 1.0 / 32 if mxfp4 else 2.0)
+    scan_bytes = cfg.batch * cfg.nt * cfg.h_idx * cfg.d_idx * {"bf16": 2.0, "mxfp4": 0.5 + 1.0 / 32,
+                                                                "int4": 0.5 + 2.0 / 32}[cache]
     qo_bytes = cfg.batch * cfg.hq * cfg.d * 2 * 2.0 + cfg.batch * cfg.h_idx * (cfg.d_idx * 2 + 4)
     step_bytes = kv_bytes + scan_bytes + qo_bytes
     attn_gbs = (kv_bytes + qo_bytes) / (ms_attn * 1e-3) / 1e9
     return dict(
-        workload=cfg.name, indexer_cache="mxfp4" if mxfp4 else "bf16", top_p=top_p,
+        workload=cfg.name, indexer_cache=cache, top_p=top_p,
         value=round(step_bytes / (ms_step * 1e-3) / 1e9, 1), unit="GB/s",
         frac_of_hbm_peak=round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         ms_per_step=round(ms_step, 4), step_launch=step_launch, ms_per_step_stream_launches=round(ms_step_eager, 4),
@@ -717,8 +722,10 @@ def main():
             dcfg, t = decode_device(torch, B, I)
             dec = {"bf16_indexer": bench_decode(args, torch, B, dcfg, t)}
             say(f"decode: {dec['bf16_indexer']}")
-            dec["mxfp4_indexer"] = bench_decode(args, torch, B, dcfg, t, mxfp4=True)
+            dec["mxfp4_indexer"] = bench_decode(args, torch, B, dcfg, t, cache="mxfp4")
             say(f"decode mxfp4: {dec['mxfp4_indexer']}")
+            dec["int4_indexer"] = bench_decode(args, torch, B, dcfg, t, cache="int4")
+            say(f"decode int4: {dec['int4_indexer']}")
             # every block kept (p = 1): the attention streams the whole 8 GiB KV cache
             dec["keep_all"] = bench_decode(args, torch, B, dcfg, t, top_p=1.0)
             say(f"decode keep-all: {dec['keep_all']}")

@@ -27,7 +27,8 @@ EXPORTS = ("spot_version", "spot_status_string", "spot_last_error", "spot_worksp
            "spot_select_topp", "spot_sparse_attn_prefill", "spot_sparse_attn_decode", "spot_key_permutation",
            "spot_order_history", "spot_sparse_attn_prefill_early_stop", "spot_quantize_indexer_keys",
            "spot_indexer_score_mxfp4", "spot_history_map", "spot_sparse_attn_prefill_history_map",
-           "spot_validate_perm", "spot_sparse_attn_decode_noalloc")
+           "spot_validate_perm", "spot_sparse_attn_decode_noalloc", "spot_quantize_indexer_keys_int4",
+           "spot_indexer_score_int4")
 
 
 class spot_desc(ctypes.Structure):
@@ -79,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spot_sparse_attn_prefill_early_stop.argtypes = [D, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.spot_validate_perm.argtypes = [D, P, P, P]
     lib.spot_sparse_attn_decode_noalloc.argtypes = [D, P, P, P, P, P, P, P, P]
+    lib.spot_quantize_indexer_keys_int4.argtypes = [D, P, P, P, P]
+    lib.spot_indexer_score_int4.argtypes = [D, P, P, P, P, P, P]
     for name in EXPORTS[3:]:
         getattr(lib, name).restype = I
     _lib = lib
@@ -174,6 +177,18 @@ def spot_indexer_score_mxfp4(desc, idx_q, idx_w, k_codes, k_scales, scores, stre
     st = load_library().spot_indexer_score_mxfp4(ctypes.byref(desc), _ptr(idx_q), _ptr(idx_w), _ptr(k_codes),
                                                  _ptr(k_scales), _ptr(scores), _stream() if stream is None else stream)
     _check("spot_indexer_score_mxfp4", st)
+
+
+def spot_quantize_indexer_keys_int4(desc, idx_k, k_codes, k_scales, stream=None):
+    st = load_library().spot_quantize_indexer_keys_int4(ctypes.byref(desc), _ptr(idx_k), _ptr(k_codes),
+                                                        _ptr(k_scales), _stream() if stream is None else stream)
+    _check("spot_quantize_indexer_keys_int4", st)
+
+
+def spot_indexer_score_int4(desc, idx_q, idx_w, k_codes, k_scales, scores, stream=None):
+    st = load_library().spot_indexer_score_int4(ctypes.byref(desc), _ptr(idx_q), _ptr(idx_w), _ptr(k_codes),
+                                                _ptr(k_scales), _ptr(scores), _stream() if stream is None else stream)
+    _check("spot_indexer_score_int4", st)
 
 
 def spot_history_map(desc, q, k, hmap, workspace=None, stream=None):
@@ -434,6 +449,19 @@ def quantize_indexer_keys(idx_k, block: int, kv_len: int):
     return codes, scales
 
 
+def quantize_indexer_keys_int4(idx_k, block: int, kv_len: int):
+    """INT4 encoding of the indexer keys idx_k (batch, nT, h_idx, d_idx) bf16.
+    Returns (codes uint8 (batch, nT, h_idx*d_idx/2), scales bf16 (batch, nT, h_idx*d_idx/32))."""
+    _require(idx_k, "idx_k", dtype=torch.bfloat16)
+    b, nt, h_idx, d_idx = idx_k.shape
+    desc = make_desc(dtype=SPOT_BF16, batch=b, hq=1, hkv=1, d=128, q_len=1, kv_len=kv_len, block=block,
+                     score_kind=SPOT_SCORE_RELU_INDEXER, h_idx=h_idx, d_idx=d_idx)
+    codes = torch.empty(b, nt, h_idx * d_idx // 2, dtype=torch.uint8, device=idx_k.device)
+    scales = torch.empty(b, nt, h_idx * d_idx // 32, dtype=torch.bfloat16, device=idx_k.device)
+    spot_quantize_indexer_keys_int4(desc, idx_k, codes, scales)
+    return codes, scales
+
+
 def decode(q, k_cache, v_cache, idx_q, idx_w, idx_k, block: int, top_p: float, *, n_sink: int = 1,
            n_recent: int = 1, k_min: int = 0, sm_scale: float = 0.0,
            bufs: DecodeBuffers | None = None) -> DecodeBuffers:
@@ -441,8 +469,9 @@ def decode(q, k_cache, v_cache, idx_q, idx_w, idx_k, block: int, top_p: float, *
 
     q (batch, hq, d) bf16; k_cache/v_cache (batch, hkv, T, d) bf16;
     idx_q (batch, h_idx, d_idx) bf16; idx_w (batch, h_idx) fp32;
-    idx_k (batch, nT, h_idx, d_idx) bf16, or its MXFP4 encoding as the pair
-    (codes, scales) from quantize_indexer_keys.
+    idx_k (batch, nT, h_idx, d_idx) bf16, or an encoding of it as the pair
+    (codes, scales): uint8 scales are MXFP4 (quantize_indexer_keys), bf16
+    scales INT4 (quantize_indexer_keys_int4).
     """
     h_idx, d_idx = idx_q.shape[1], idx_q.shape[2]
     desc = decode_desc(q, k_cache, block, top_p, h_idx, d_idx, n_sink=n_sink, n_recent=n_recent, k_min=k_min,
@@ -452,13 +481,17 @@ def decode(q, k_cache, v_cache, idx_q, idx_w, idx_k, block: int, top_p: float, *
         _require(t, name, dtype=torch.bfloat16)
     if mx:
         _require(idx_k[0], "k_codes", dtype=torch.uint8)
-        _require(idx_k[1], "k_scales", dtype=torch.uint8)
+        if idx_k[1].dtype != torch.bfloat16:
+            _require(idx_k[1], "k_scales", dtype=torch.uint8)
     else:
         _require(idx_k, "idx_k", dtype=torch.bfloat16)
     _require(idx_w, "idx_w", dtype=torch.float32)
     if bufs is None:
         bufs = alloc_decode(desc, q.device)
-    if mx:
+    if mx and idx_k[1].dtype == torch.bfloat16:
+        _require(idx_k[1], "k_scales", dtype=torch.bfloat16)
+        spot_indexer_score_int4(desc, idx_q, idx_w, idx_k[0], idx_k[1], bufs.scores)
+    elif mx:
         spot_indexer_score_mxfp4(desc, idx_q, idx_w, idx_k[0], idx_k[1], bufs.scores)
     else:
         spot_block_score(desc, None, None, None, idx_q, idx_w, idx_k, bufs.scores)

@@ -444,17 +444,18 @@ __global__ __launch_bounds__(256) void indexer_score_mxfp4_kernel(IndexerFp4Args
   const int R = a.h_idx * a.d_idx;
   const int lph = a.d_idx / 32;   // lanes per indexer head
   const int e0 = li * 32;
-  const int head = e0 / a.d_idx;
+  const bool act = e0 < R;        // LPR rounds R / 32 up to a power of two: the extra lanes hold no group
+  const int head = act ? e0 / a.d_idx : 0;
   uint32_t qw[16];
   {
-    const uint4* qp = reinterpret_cast<const uint4*>(a.idx_q + size_t(b) * R + e0);
+    const uint4* qp = reinterpret_cast<const uint4*>(a.idx_q + size_t(b) * R + (act ? e0 : 0));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint4 v = qp[i];
       qw[4 * i] = v.x; qw[4 * i + 1] = v.y; qw[4 * i + 2] = v.z; qw[4 * i + 3] = v.w;
     }
   }
-  const float w = a.idx_w[size_t(b) * a.h_idx + head];
+  const float w = act ? a.idx_w[size_t(b) * a.h_idx + head] : 0.f;
   const uint8_t* cb = a.codes + size_t(b) * a.nk * (R / 2);
   const uint8_t* sb = a.scales + size_t(b) * a.nk * (R / 32);
   const int step = gridDim.x * 4 * RPW * kFp4Unroll;
@@ -464,7 +465,7 @@ __global__ __launch_bounds__(256) void indexer_score_mxfp4_kernel(IndexerFp4Args
 #pragma unroll
     for (int u = 0; u < kFp4Unroll; ++u) {
       const int t = t0 + u * RPW + sub;
-      const bool in = t < a.nk;
+      const bool in = act && t < a.nk;
       cv[u] = in ? *reinterpret_cast<const uint4*>(cb + size_t(t) * (R / 2) + li * 16) : make_uint4(0u, 0u, 0u, 0u);
       ex[u] = in ? int(sb[size_t(t) * (R / 32) + li]) - 127 : 0;
     }
@@ -486,7 +487,7 @@ __global__ __launch_bounds__(256) void indexer_score_mxfp4_kernel(IndexerFp4Args
       }
       dp = ldexpf(dp, ex[u]);
       for (int o = 1; o < lph; o <<= 1) dp += __shfl_xor(dp, o);
-      float val = (li % lph) == 0 ? w * fmaxf(dp, 0.f) : 0.f;
+      float val = (act && (li % lph) == 0) ? w * fmaxf(dp, 0.f) : 0.f;
 #pragma unroll
       for (int o = 1; o < LPR; o <<= 1)
         if (o >= lph) val += __shfl_xor(val, o);
@@ -510,6 +511,138 @@ hipError_t launch_indexer_score_mxfp4(const IndexerFp4Args& a, hipStream_t s) {
   else if (lanes <= 2) launch_idx_fp4<2>(a, s);
   else if (lanes <= 4) launch_idx_fp4<4>(a, s);
   else launch_idx_fp4<8>(a, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- INT4 indexer keys
+// SpotAttention section 4 (selector K-cache as INT4 microscale): every 32
+// consecutive elements share one bf16 scale s = max|x| / 7 (rounded to
+// nearest even); each element is x / s rounded to the nearest integer (ties
+// to even) and clamped to [-7, 7], stored as a 4-bit two's-complement code,
+// two per byte with the even element in the low nibble.  An all-zero group
+// gets scale 0 and codes 0.  The division is IEEE fp32: for bf16 x and s the
+// exact quotient is either a half-integer or at least 2^-9 relative away
+// from one, so the rounded quotient takes the same integer as the exact one.
+__global__ __launch_bounds__(256) void quantize_int4_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
+                                                            uint16_t* __restrict__ scales, long long ngroups) {
+  const long long gi = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gi >= ngroups) return;
+  const uint4* src = reinterpret_cast<const uint4*>(x + gi * 32);
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = src[i];
+    w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+  }
+  uint32_t amax = 0;   // largest magnitude, compared as bf16 bit patterns (exact for finite values)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = max(amax, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+  const uint32_t sbits = pack_bf16x2(bf16_to_f32(uint16_t(amax)) / 7.0f, 0.f) & 0xFFFFu;
+  const float sc = bf16_to_f32(uint16_t(sbits));
+  scales[gi] = uint16_t(sbits);
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t word = w[4 * i + j / 2];
+      const float v = (j & 1) ? bf16_hi(word) : bf16_lo(word);
+      const int c = sc > 0.f ? int(fminf(fmaxf(rintf(v / sc), -7.f), 7.f)) : 0;
+      r |= (uint32_t(c) & 15u) << (4 * j);
+    }
+    out[i] = r;
+  }
+  *reinterpret_cast<uint4*>(codes + gi * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+hipError_t launch_quantize_int4(const uint16_t* x, uint8_t* codes, uint16_t* scales, long long ngroups,
+                                hipStream_t s) {
+  const long long blocks = (ngroups + 255) / 256;
+  quantize_int4_kernel<<<dim3(unsigned(blocks)), 256, 0, s>>>(x, codes, scales, ngroups);
+  return hipGetLastError();
+}
+
+// A row (one key block: h_idx x d_idx codes) is spread over LPR lanes, one
+// 32-element group (16 code bytes + its bf16 scale) per lane; codes widen to
+// fp32 by sign extension and multiply the bf16 query (exact products), the
+// group sum is scaled once.
+template <int LPR>
+__global__ __launch_bounds__(256) void indexer_score_int4_kernel(IndexerInt4Args a) {
+  constexpr int RPW = 64 / LPR;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / LPR, li = lane % LPR;
+  const int R = a.h_idx * a.d_idx;
+  const int lph = a.d_idx / 32;   // lanes per indexer head
+  const int e0 = li * 32;
+  const bool act = e0 < R;        // LPR rounds R / 32 up to a power of two: the extra lanes hold no group
+  const int head = act ? e0 / a.d_idx : 0;
+  float qf[32];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(a.idx_q + size_t(b) * R + (act ? e0 : 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = qp[i];
+      const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        qf[8 * i + 2 * k] = bf16_lo(vw[k]);
+        qf[8 * i + 2 * k + 1] = bf16_hi(vw[k]);
+      }
+    }
+  }
+  const float w = act ? a.idx_w[size_t(b) * a.h_idx + head] : 0.f;
+  const uint8_t* cb = a.codes + size_t(b) * a.nk * (R / 2);
+  const uint16_t* sb = a.scales + size_t(b) * a.nk * (R / 32);
+  const int step = gridDim.x * 4 * RPW * kFp4Unroll;
+  for (int t0 = (blockIdx.x * 4 + wave) * RPW * kFp4Unroll; t0 < a.nk; t0 += step) {
+    uint4 cv[kFp4Unroll];
+    float scv[kFp4Unroll];
+#pragma unroll
+    for (int u = 0; u < kFp4Unroll; ++u) {
+      const int t = t0 + u * RPW + sub;
+      const bool in = act && t < a.nk;
+      cv[u] = in ? *reinterpret_cast<const uint4*>(cb + size_t(t) * (R / 2) + li * 16) : make_uint4(0u, 0u, 0u, 0u);
+      scv[u] = in ? bf16_to_f32(sb[size_t(t) * (R / 32) + li]) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kFp4Unroll; ++u) {
+      const uint32_t cw[4] = {cv[u].x, cv[u].y, cv[u].z, cv[u].w};
+      float dp = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {   // nibble j of word i: element 8i + j, sign-extended
+          const int c = int(cw[i] << (28 - 4 * j)) >> 28;
+          dp = fmaf(float(c), qf[8 * i + j], dp);
+        }
+      dp *= scv[u];
+      for (int o = 1; o < lph; o <<= 1) dp += __shfl_xor(dp, o);
+      float val = (act && (li % lph) == 0) ? w * fmaxf(dp, 0.f) : 0.f;
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1)
+        if (o >= lph) val += __shfl_xor(val, o);
+      const int t = t0 + u * RPW + sub;
+      if (li == 0 && t < a.nk) a.scores[size_t(b) * a.nk + t] = val;
+    }
+  }
+}
+
+template <int LPR>
+static void launch_idx_int4(const IndexerInt4Args& a, hipStream_t s) {
+  const int per_block = 4 * (64 / LPR) * kFp4Unroll;
+  int blocks = (a.nk + per_block - 1) / per_block;
+  if (blocks > kFp4MaxBlocks) blocks = kFp4MaxBlocks;
+  indexer_score_int4_kernel<LPR><<<dim3(blocks, a.batch), 256, 0, s>>>(a);
+}
+
+hipError_t launch_indexer_score_int4(const IndexerInt4Args& a, hipStream_t s) {
+  const int lanes = (a.h_idx * a.d_idx) / 32;   // one 32-element group per lane (R <= 256)
+  if (lanes <= 1) launch_idx_int4<1>(a, s);
+  else if (lanes <= 2) launch_idx_int4<2>(a, s);
+  else if (lanes <= 4) launch_idx_int4<4>(a, s);
+  else launch_idx_int4<8>(a, s);
   return hipGetLastError();
 }
 

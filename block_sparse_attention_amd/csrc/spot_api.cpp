@@ -285,18 +285,19 @@ int spot_sparse_attn_prefill(const spot_desc* desc, const void* q, const void* k
   return launched(spot::launch_prefill(a, static_cast<hipStream_t>(stream)), "sparse_attn_prefill");
 }
 
-static int check_mxfp4_indexer(const spot_desc* desc) {
+static int check_grouped_indexer(const spot_desc* desc) {
   int st = check_common(desc);
   if (st) return st;
   if (desc->score_kind != SPOT_SCORE_RELU_INDEXER) return fail(SPOT_ERR_INVALID, "score_kind must be RELU_INDEXER");
   if ((st = check_indexer(desc))) return st;
-  if (desc->d_idx % 32) return fail(SPOT_ERR_UNSUPPORTED, "MXFP4 needs d_idx a multiple of 32 (got %d)", desc->d_idx);
+  if (desc->d_idx % 32)
+    return fail(SPOT_ERR_UNSUPPORTED, "32-element key groups need d_idx a multiple of 32 (got %d)", desc->d_idx);
   return SPOT_OK;
 }
 
 int spot_quantize_indexer_keys(const spot_desc* desc, const void* idx_k, uint8_t* k_codes, uint8_t* k_scales,
                                void* stream) {
-  int st = check_mxfp4_indexer(desc);
+  int st = check_grouped_indexer(desc);
   if (st) return st;
   if (!idx_k || !k_codes || !k_scales) return fail(SPOT_ERR_INVALID, "idx_k, k_codes and k_scales are required");
   if ((st = check_aligned16("idx_k", idx_k)) || (st = check_aligned16("k_codes", k_codes))) return st;
@@ -309,7 +310,7 @@ int spot_quantize_indexer_keys(const spot_desc* desc, const void* idx_k, uint8_t
 
 int spot_indexer_score_mxfp4(const spot_desc* desc, const void* idx_q, const float* idx_w, const uint8_t* k_codes,
                              const uint8_t* k_scales, float* scores, void* stream) {
-  int st = check_mxfp4_indexer(desc);
+  int st = check_grouped_indexer(desc);
   if (st) return st;
   if (!idx_q || !idx_w || !k_codes || !k_scales || !scores)
     return fail(SPOT_ERR_INVALID, "idx_q, idx_w, k_codes, k_scales and scores are required");
@@ -317,6 +318,34 @@ int spot_indexer_score_mxfp4(const spot_desc* desc, const void* idx_q, const flo
   spot::IndexerFp4Args a{static_cast<const uint16_t*>(idx_q), idx_w, k_codes, k_scales, scores, desc->batch,
                          int(ceil_div64(desc->kv_len, desc->block)), desc->h_idx, desc->d_idx};
   return launched(spot::launch_indexer_score_mxfp4(a, static_cast<hipStream_t>(stream)), "indexer_score_mxfp4");
+}
+
+int spot_quantize_indexer_keys_int4(const spot_desc* desc, const void* idx_k, uint8_t* k_codes, void* k_scales,
+                                    void* stream) {
+  int st = check_grouped_indexer(desc);
+  if (st) return st;
+  if (!idx_k || !k_codes || !k_scales) return fail(SPOT_ERR_INVALID, "idx_k, k_codes and k_scales are required");
+  if ((st = check_aligned16("idx_k", idx_k)) || (st = check_aligned16("k_codes", k_codes))) return st;
+  if (reinterpret_cast<uintptr_t>(k_scales) & 1u) return fail(SPOT_ERR_INVALID, "k_scales must be 2-byte aligned");
+  const long long nk = ceil_div64(desc->kv_len, desc->block);
+  const long long groups = (long long)desc->batch * nk * (desc->h_idx * desc->d_idx / 32);
+  return launched(spot::launch_quantize_int4(static_cast<const uint16_t*>(idx_k), k_codes,
+                                             static_cast<uint16_t*>(k_scales), groups,
+                                             static_cast<hipStream_t>(stream)),
+                  "quantize_indexer_keys_int4");
+}
+
+int spot_indexer_score_int4(const spot_desc* desc, const void* idx_q, const float* idx_w, const uint8_t* k_codes,
+                            const void* k_scales, float* scores, void* stream) {
+  int st = check_grouped_indexer(desc);
+  if (st) return st;
+  if (!idx_q || !idx_w || !k_codes || !k_scales || !scores)
+    return fail(SPOT_ERR_INVALID, "idx_q, idx_w, k_codes, k_scales and scores are required");
+  if ((st = check_aligned16("idx_q", idx_q)) || (st = check_aligned16("k_codes", k_codes))) return st;
+  if (reinterpret_cast<uintptr_t>(k_scales) & 1u) return fail(SPOT_ERR_INVALID, "k_scales must be 2-byte aligned");
+  spot::IndexerInt4Args a{static_cast<const uint16_t*>(idx_q), idx_w, k_codes, static_cast<const uint16_t*>(k_scales),
+                          scores, desc->batch, int(ceil_div64(desc->kv_len, desc->block)), desc->h_idx, desc->d_idx};
+  return launched(spot::launch_indexer_score_int4(a, static_cast<hipStream_t>(stream)), "indexer_score_int4");
 }
 
 int spot_history_map(const spot_desc* desc, const void* q, const void* k, int32_t* hmap, void* workspace,

@@ -37,9 +37,10 @@ TRACKED = [
     ("prefill_mfma_kernel<128, 8, 1, true, true, true>", "prefill.hip",
      "prefill_mfma_kernel_early_stop@heavy-perm-bf16-L32768", 0, 0),
     ("decode_split_kernel<128, 4", "decode.hip", "decode_split_kernel@decode-b16-T131072", 0, 1),
-    ("decode_split_kernel<128, 4", "decode.hip", "decode_split_kernel@decode-b16-T131072-keep-all", 2, 1),
+    ("decode_split_kernel<128, 4", "decode.hip", "decode_split_kernel@decode-b16-T131072-keep-all", 3, 1),
     ("indexer_score_kernel<", "score.hip", "indexer_score_kernel@decode-b16-T131072", 0, 1),
     ("indexer_score_mxfp4_kernel", "score.hip", "indexer_score_mxfp4_kernel@decode-b16-T131072", 0, 0),
+    ("indexer_score_int4_kernel", "score.hip", "indexer_score_int4_kernel@decode-b16-T131072", 0, 0),
     ("pool_blocks_kernel<unsigned short>", "score.hip", "pool_blocks_kernel@long-bf16-L131072", 0, 1),
     ("pool_blocks_kernel<unsigned short>", "score.hip", "pool_blocks_kernel@gqa-bf16-L8192", 1, 1),
 ]

@@ -4,8 +4,8 @@ Runs, on cuda:0, in this order: `--steps` prefill steps of the long-context
 workload (L=131072, 32/8 heads, d=128, bf16, block 128, top-p 0.9), `--steps`
 prefill steps of the GQA workload (L=8192, block 64, top-p 0.9), `--steps`
 decode steps of the sparse decode workload (batch 16, context 131072) with the
-bf16 indexer cache, then with the MXFP4 indexer cache, then keeping every
-block (p = 1), `--steps` early-stopped prefill steps of the heavy-hitter
+bf16 indexer cache, then with the MXFP4 indexer cache, then with the INT4
+indexer cache, then keeping every block (p = 1), `--steps` early-stopped prefill steps of the heavy-hitter
 workload (L=32768, segment 2048, tau 0.01, permutation on the GPU), and
 `--steps` plain device copies of 1 GiB, whose counter readings calibrate
 FETCH_SIZE / WRITE_SIZE against a known byte count.  The summariser
@@ -67,13 +67,19 @@ def main():
                              dc.block, dc.top_p, bufs=dbufs)
         torch.cuda.synchronize()
         print(f"decode steps with the MXFP4 indexer cache done: {args.steps}", flush=True)
+        codes4, scales4 = B.quantize_indexer_keys_int4(t["idx_k"], dc.block, dc.T)
+        for _ in range(args.steps):
+            dbufs = B.decode(t["q"], t["k_cache"], t["v_cache"], t["idx_q"], t["idx_w"], (codes4, scales4),
+                             dc.block, dc.top_p, bufs=dbufs)
+        torch.cuda.synchronize()
+        print(f"decode steps with the INT4 indexer cache done: {args.steps}", flush=True)
         abufs = None
         for _ in range(args.steps):
             abufs = B.decode(t["q"], t["k_cache"], t["v_cache"], t["idx_q"], t["idx_w"], t["idx_k"], dc.block, 1.0,
                              bufs=abufs)
         torch.cuda.synchronize()
         print(f"decode steps keeping every block done: {args.steps}", flush=True)
-        del t, codes, scales, dbufs, abufs
+        del t, codes, scales, codes4, scales4, dbufs, abufs
 
     if not args.no_early_stop:
         ec = I.C3

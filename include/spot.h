@@ -283,6 +283,31 @@ int spot_indexer_score_mxfp4(const spot_desc* desc, const void* idx_q, const flo
                              const uint8_t* k_scales, float* scores, void* stream);
 
 /*
+ * Selector key cache in INT4 microscaling ([Spot] §4 quantisation: the
+ * selector's K-cache held as INT4/FP4 microscale).  Every 32 consecutive
+ * elements of an indexer key row (d_idx a multiple of 32) share one bf16
+ * scale s = max|x| / 7 (rounded to nearest, ties to even); each element is
+ * x / s rounded to the nearest integer (ties to the even one), clamped to
+ * [-7, 7], and stored as a 4-bit two's-complement code, two per byte with the
+ * even element in the low nibble; an all-zero group has s = 0 and codes 0.
+ * 4.5 bits per element: 3.56x smaller than bf16.
+ * Layouts: k_codes uint8 [batch, nk, h_idx*d_idx/2]; k_scales bf16
+ * [batch, nk, h_idx*d_idx/32]; nk = ceil(kv_len / block).
+ *
+ * spot_quantize_indexer_keys_int4: idx_k bf16 [batch, nk, h_idx, d_idx]
+ *   (finite) -> codes and scales (deterministic, equal to the exact rule).
+ * spot_indexer_score_int4: as spot_block_score with RELU_INDEXER, with the
+ *   keys read from the encoding (decoded value = code * s).
+ * Both need score_kind RELU_INDEXER and the indexer limits of
+ * spot_block_score, idx_k, idx_q and k_codes 16-byte aligned and k_scales
+ * 2-byte aligned; no workspace.
+ */
+int spot_quantize_indexer_keys_int4(const spot_desc* desc, const void* idx_k, uint8_t* k_codes, void* k_scales,
+                                    void* stream);
+int spot_indexer_score_int4(const spot_desc* desc, const void* idx_q, const float* idx_w, const uint8_t* k_codes,
+                            const void* k_scales, float* scores, void* stream);
+
+/*
  * Visiting order for early stopping ([S2O] §2: candidate blocks are processed
  * in descending estimated importance).  For each row (b, g, i) of the MEANPOOL
  * scores [batch, hkv, nb, nb]: the history blocks of query block i, i.e. the

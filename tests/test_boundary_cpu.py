@@ -278,6 +278,29 @@ def test_mxfp4_indexer_validation():
     assert sc(_decode(), c=FAKE + 1) == B.SPOT_ERR_INVALID
 
 
+def test_int4_indexer_validation():
+    lib = B.load_library()
+
+    def q(d, x=FAKE, c=FAKE, s=FAKE):
+        return lib.spot_quantize_indexer_keys_int4(ctypes.byref(d), x, c, s, None)
+
+    def sc(d, iq=FAKE, iw=FAKE, c=FAKE, s=FAKE, out=FAKE):
+        return lib.spot_indexer_score_int4(ctypes.byref(d), iq, iw, c, s, out, None)
+
+    assert q(_decode(d_idx=16, h_idx=4)) == B.SPOT_ERR_UNSUPPORTED          # groups of 32 need d_idx % 32 == 0
+    assert sc(_decode(d_idx=16, h_idx=4)) == B.SPOT_ERR_UNSUPPORTED
+    assert q(_decode(h_idx=8, d_idx=64)) == B.SPOT_ERR_UNSUPPORTED           # row wider than 256
+    assert q(_decode(score_kind=B.SPOT_SCORE_MEANPOOL)) == B.SPOT_ERR_INVALID
+    assert q(_decode(), x=None) == B.SPOT_ERR_INVALID
+    assert sc(_decode(), s=None) == B.SPOT_ERR_INVALID
+    assert sc(_decode(), out=None) == B.SPOT_ERR_INVALID
+    assert q(_decode(), x=FAKE + 2) == B.SPOT_ERR_INVALID                   # 16-byte loads and stores
+    assert q(_decode(), c=FAKE + 8) == B.SPOT_ERR_INVALID
+    assert q(_decode(), s=FAKE + 1) == B.SPOT_ERR_INVALID                   # bf16 scales
+    assert sc(_decode(), iq=FAKE + 4) == B.SPOT_ERR_INVALID
+    assert sc(_decode(), s=FAKE + 1) == B.SPOT_ERR_INVALID
+
+
 def test_history_map_validation():
     lib = B.load_library()
 

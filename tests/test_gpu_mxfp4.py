@@ -83,7 +83,9 @@ def _oracle_scores(D, b):
 
 
 @pytest.mark.parametrize("kw", [dict(batch=2, T=16 * 1000 + 5), dict(batch=3, T=4096, hq=16, hkv=2, d=64),
-                                dict(batch=2, T=3000, h_idx=2, d_idx=128), dict(batch=1, T=10)],
+                                dict(batch=2, T=3000, h_idx=2, d_idx=128), dict(batch=1, T=10),
+                                # three groups per key row (the scan's lane count rounds up to four)
+                                dict(batch=2, T=2000, h_idx=3, d_idx=32), dict(batch=2, T=2000, h_idx=3, d_idx=64)],
                          ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
 def test_mxfp4_decode_small(gpu, kw):
     cfg = I.C4.with_(name="dec-mx", seed=31, **kw)
