@@ -565,8 +565,8 @@ hipError_t launch_quantize_int4(const uint16_t* x, uint8_t* codes, uint16_t* sca
 
 // A row (one key block: h_idx x d_idx codes) is spread over LPR lanes, one
 // 32-element group (16 code bytes + its bf16 scale) per lane; codes widen to
-// fp32 by sign extension and multiply the bf16 query (exact products), the
-// group sum is scaled once.
+// fp32 and multiply the bf16 query (exact products), the group sum is scaled
+// once.
 template <int LPR>
 __global__ __launch_bounds__(256) void indexer_score_int4_kernel(IndexerInt4Args a) {
   constexpr int RPW = 64 / LPR;
@@ -609,15 +609,24 @@ __global__ __launch_bounds__(256) void indexer_score_int4_kernel(IndexerInt4Args
 #pragma unroll
     for (int u = 0; u < kFp4Unroll; ++u) {
       const uint32_t cw[4] = {cv[u].x, cv[u].y, cv[u].z, cv[u].w};
+      // v_cvt_off_f32_i4 turns the low nibble of a byte (selected in the
+      // instruction) into c / 16: the even elements from the word, the odd
+      // ones from the word shifted by a nibble.  The sum is 1/16 of the sum of
+      // c * q taken in the same order, exactly (a power-of-two scaling), and
+      // the factor 16 goes back with the scale.
       float dp = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = cw[i];
+        uint32_t hi = cw[i] >> 4;
+        asm volatile("" : "+v"(hi));   // one shift per word, then byte selects (not a field extract per element)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {   // nibble j of word i: element 8i + j, sign-extended
-          const int c = int(cw[i] << (28 - 4 * j)) >> 28;
-          dp = fmaf(float(c), qf[8 * i + j], dp);
+        for (int j = 0; j < 4; ++j) {   // byte j of word i: elements 8i + 2j (low nibble) and 8i + 2j + 1
+          dp = fmaf(__builtin_amdgcn_cvt_off_f32_i4((lo >> (8 * j)) & 0xffu), qf[8 * i + 2 * j], dp);
+          dp = fmaf(__builtin_amdgcn_cvt_off_f32_i4((hi >> (8 * j)) & 0xffu), qf[8 * i + 2 * j + 1], dp);
         }
-      dp *= scv[u];
+      }
+      dp = (dp * 16.0f) * scv[u];
       for (int o = 1; o < lph; o <<= 1) dp += __shfl_xor(dp, o);
       float val = (act && (li % lph) == 0) ? w * fmaxf(dp, 0.f) : 0.f;
 #pragma unroll
