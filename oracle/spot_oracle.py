@@ -50,6 +50,9 @@ What each function follows:
   attend_prefill_es  [S2O] §2 (monotone-gain early stopping) and §3 (dense
                      causal pass over the own segment, then the permuted
                      history in that order, resuming the same softmax state)
+  rla_prefill,       [SPLA] §2.2 (residual linear attention: the long tail
+  rla_decode         outside the kept blocks through linear attention) and
+                     §2.3 (parameter-free exponential feature map)
 
 Readings taken where the pages leave a step open (each is also listed with the
 design notes): the block distribution for top-p is the softmax of the block
@@ -76,6 +79,13 @@ Representative query: the mean of Q over the group's heads and the segment's
 rows; the history map sorts the prefix by sm_scale * <representative, key>
 descending, ties by position; early-stopped attention on the map visits its
 consecutive runs of B positions in order.
+Residual linear attention: phi(x) = exp(x) elementwise on the raw query and
+key rows (no scale); the linear attention carries no normaliser, so the
+page's difference of the all-blocks and kept-blocks estimates is exactly the
+linear attention over the keys outside the kept blocks (normalisation is the
+RMS norm the page applies afterwards, with trained scales: not part of this
+output); the keys are the causally visible ones, {t <= r}, in prefill and
+every cached key in decode.
 Taylor score: the second-order expansion is taken for the scaled query
 (sm_scale * qbar) and enters the top-p rule as the log of the estimated block
 mass, so the softmax over blocks is the normalised mass estimate; variances
@@ -465,6 +475,68 @@ def attend_decode(q, k_cache, v_cache, kept, block, T, sm_scale):
             o[h] = (e @ vs) / z
             lse[h] = m + np.log(z)
     return o, lse
+
+
+# ----------------------------------------------------------------- residual linear attention
+def rla_feature(x):
+    """[SPLA] §2.3: the parameter-free exponential feature map, elementwise."""
+    return np.exp(np.asarray(x, dtype=np.float64))
+
+
+def rla_prefill(q, k, v, kept_lists, block, segment=0, perm=None, qblocks=None):
+    """[SPLA] §2.2 residual linear attention of every query row.
+
+    The row's linear attention (feature map phi = exp, no normaliser) over
+    the causally visible keys that its kept blocks do not hold:
+        o_rla[h, r] = sum over t <= r, t not a kept key of r, of
+                      (phi(q[h, r]) . phi(k[g, t])) * v[g, t]
+    (the keys of earlier segments are all visible whether or not the
+    permutation reorders them, so the visible set is {t <= r} either way).
+    q: (Hq, L, d); k, v: (Hkv, L, d).  Returns (Hq, L, d), rows of query
+    blocks not in `qblocks` NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    hq, L, d = q.shape
+    hkv = k.shape[0]
+    G = hq // hkv
+    nb = n_blocks(L, block)
+    qblocks = range(nb) if qblocks is None else qblocks
+    out = np.full((hq, L, d), np.nan)
+    for g in range(hkv):
+        fk = rla_feature(k[g])
+        for i in qblocks:
+            i = int(i)
+            rows = block_rows(i, block, L)
+            phys, lim = prefill_key_set(kept_lists[g][i], i, g, block, segment, perm, L)
+            rest = np.arange(L)[None, :] <= rows[:, None]               # visible keys of each row
+            for r_idx, r in enumerate(rows):
+                rest[r_idx, phys[lim <= r]] = False                     # minus the row's kept keys
+            for h in range(g * G, (g + 1) * G):
+                w = (rla_feature(q[h, rows]) @ fk.T) * rest             # (rows, L)
+                out[h, rows] = w @ v[g]
+    return out
+
+
+def rla_decode(q, k_cache, v_cache, kept, block, T):
+    """[SPLA] §2.2 residual linear attention of the decode query (position
+    T-1, every cached key visible) over the keys outside the kept blocks.
+    q: (Hq, d); k_cache, v_cache: (Hkv, T, d).  Returns (Hq, d)."""
+    q = np.asarray(q, dtype=np.float64)
+    hq, d = q.shape
+    hkv = k_cache.shape[0]
+    G = hq // hkv
+    rest = np.ones(T, dtype=bool)
+    for t in kept:
+        rest[block_rows(int(t), block, T)] = False
+    out = np.empty((hq, d))
+    for g in range(hkv):
+        fk = rla_feature(np.asarray(k_cache[g, :T], dtype=np.float64)[rest])
+        vs = np.asarray(v_cache[g, :T], dtype=np.float64)[rest]
+        for h in range(g * G, (g + 1) * G):
+            out[h] = (fk @ rla_feature(q[h])) @ vs
+    return out
 
 
 # ----------------------------------------------------------------- key permutation

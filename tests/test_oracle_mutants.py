@@ -23,9 +23,21 @@ TAYLOR = "tests/test_oracle_taylor.py"
 MXFP4 = "tests/test_oracle_mxfp4.py"
 INT4 = "tests/test_oracle_int4.py"
 S2O = "tests/test_oracle_s2o_map.py"
+RLA = "tests/test_oracle_rla.py"
 
 # (name, pin file, line fragment as written in the oracle, planted mistake)
 MUTANTS = [
+    ("RLA feature map with the attention scale", RLA,
+     "return np.exp(np.asarray(x, dtype=np.float64))",
+     "return np.exp(np.asarray(x, dtype=np.float64) / np.sqrt(np.shape(x)[-1]))"),
+    ("RLA rest without the causal mask", RLA,
+     "rest = np.arange(L)[None, :] <= rows[:, None]", "rest = np.ones((rows.shape[0], L), dtype=bool)"),
+    ("RLA removes only the history keys it keeps", RLA,
+     "rest[r_idx, phys[lim <= r]] = False", "rest[r_idx, phys[lim < 0]] = False"),
+    ("RLA normalised by the feature mass", RLA,
+     "out[h, rows] = w @ v[g]", "out[h, rows] = (w @ v[g]) / np.maximum(w.sum(axis=1, keepdims=True), 1e-300)"),
+    ("RLA decode keeps the kept blocks", RLA,
+     "rest[block_rows(int(t), block, T)] = False", "rest[block_rows(int(t), block, T)] = True"),
     ("history rows through the inverse permutation", PINS,
      "phys.append(perm[g, ts])", "phys.append(np.argsort(perm[g])[ts])"),
     ("exclusive top-p crossing", PINS, "c >= top_p", "c > top_p"),
