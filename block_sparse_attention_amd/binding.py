@@ -20,7 +20,7 @@ SPOT_OK, SPOT_ERR_INVALID, SPOT_ERR_UNSUPPORTED, SPOT_ERR_WORKSPACE, SPOT_ERR_LA
 SPOT_F32, SPOT_BF16 = 0, 1
 SPOT_SCORE_MEANPOOL, SPOT_SCORE_RELU_INDEXER, SPOT_SCORE_TAYLOR = 0, 1, 2
 SPOT_OP_BLOCK_SCORE, SPOT_OP_SELECT_TOPP, SPOT_OP_PREFILL, SPOT_OP_DECODE, SPOT_OP_KEY_PERMUTATION = 0, 1, 2, 3, 4
-SPOT_OP_ORDER_HISTORY, SPOT_OP_PREFILL_EARLY_STOP, SPOT_OP_HISTORY_MAP = 5, 6, 7
+SPOT_OP_ORDER_HISTORY, SPOT_OP_PREFILL_EARLY_STOP, SPOT_OP_HISTORY_MAP, SPOT_OP_RLA_DECODE_STATE = 5, 6, 7, 8
 ABI_VERSION = 1
 
 EXPORTS = ("spot_version", "spot_status_string", "spot_last_error", "spot_workspace_size", "spot_block_score",
@@ -28,7 +28,8 @@ EXPORTS = ("spot_version", "spot_status_string", "spot_last_error", "spot_worksp
            "spot_order_history", "spot_sparse_attn_prefill_early_stop", "spot_quantize_indexer_keys",
            "spot_indexer_score_mxfp4", "spot_history_map", "spot_sparse_attn_prefill_history_map",
            "spot_validate_perm", "spot_sparse_attn_decode_noalloc", "spot_quantize_indexer_keys_int4",
-           "spot_indexer_score_int4")
+           "spot_indexer_score_int4", "spot_rla_block_states", "spot_rla_prefill", "spot_rla_decode_state",
+           "spot_rla_decode")
 
 
 class spot_desc(ctypes.Structure):
@@ -82,6 +83,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spot_sparse_attn_decode_noalloc.argtypes = [D, P, P, P, P, P, P, P, P]
     lib.spot_quantize_indexer_keys_int4.argtypes = [D, P, P, P, P]
     lib.spot_indexer_score_int4.argtypes = [D, P, P, P, P, P, P]
+    lib.spot_rla_block_states.argtypes = [D, P, P, P, P, P, P]
+    lib.spot_rla_prefill.argtypes = [D, P, P, P, P, P, P, P]
+    lib.spot_rla_decode_state.argtypes = [D, P, P, P, P, S, P]
+    lib.spot_rla_decode.argtypes = [D, P, P, P, P, P, P, P, P]
     for name in EXPORTS[3:]:
         getattr(lib, name).restype = I
     _lib = lib
@@ -221,6 +226,31 @@ def spot_sparse_attn_prefill_early_stop(desc, tau, q, k, v, perm, order, cnt, o,
         ctypes.byref(desc), float(tau), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(order), _ptr(cnt), _ptr(o),
         _ptr(lse), _ptr(nused), _ptr(workspace), ws_bytes, _stream() if stream is None else stream)
     _check("spot_sparse_attn_prefill_early_stop", st)
+
+
+def spot_rla_block_states(desc, k, v, perm, states, states_perm=None, stream=None):
+    st = load_library().spot_rla_block_states(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(perm), _ptr(states),
+                                              _ptr(states_perm), _stream() if stream is None else stream)
+    _check("spot_rla_block_states", st)
+
+
+def spot_rla_prefill(desc, q, states, states_perm, idx, cnt, o_rla, stream=None):
+    st = load_library().spot_rla_prefill(ctypes.byref(desc), _ptr(q), _ptr(states), _ptr(states_perm), _ptr(idx),
+                                         _ptr(cnt), _ptr(o_rla), _stream() if stream is None else stream)
+    _check("spot_rla_prefill", st)
+
+
+def spot_rla_decode_state(desc, k_cache, v_cache, state, workspace=None, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load_library().spot_rla_decode_state(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(state),
+                                              _ptr(workspace), ws_bytes, _stream() if stream is None else stream)
+    _check("spot_rla_decode_state", st)
+
+
+def spot_rla_decode(desc, q, k_cache, v_cache, state, idx, cnt, o_rla, stream=None):
+    st = load_library().spot_rla_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(state),
+                                        _ptr(idx), _ptr(cnt), _ptr(o_rla), _stream() if stream is None else stream)
+    _check("spot_rla_decode", st)
 
 
 # ----------------------------------------------------------------- descriptors
@@ -403,6 +433,55 @@ def prefill_history_map(q, k, v, block: int, segment: int, tau: float, *, hmap=N
         bufs = alloc_prefill_early_stop(desc, q.device)
     spot_sparse_attn_prefill_history_map(desc, tau, q, k, v, hmap, bufs.o, bufs.lse, bufs.nused)
     return bufs
+
+
+@dataclass
+class RlaPrefillBuffers:
+    states: torch.Tensor
+    states_perm: torch.Tensor | None
+    o_rla: torch.Tensor
+
+
+def rla_prefill(desc: spot_desc, q, k, v, idx, cnt, *, perm=None,
+                bufs: RlaPrefillBuffers | None = None) -> RlaPrefillBuffers:
+    """Residual linear attention of every query row over the visible keys
+    outside its kept blocks: block states, then the per-block residual.
+
+    desc: the prefill descriptor of the selection; q, k, v as for prefill;
+    idx/cnt the kept lists of spot_select_topp; perm as for the attention.
+    Returns buffers whose o_rla is fp32 (batch, hq, L, d)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, dtype=q.dtype)
+    nb = -(-desc.q_len // desc.block)
+    if bufs is None:
+        shape = (desc.batch, desc.hkv, nb, desc.d, desc.d)
+        bufs = RlaPrefillBuffers(
+            states=torch.empty(shape, dtype=torch.float32, device=q.device),
+            states_perm=torch.empty(shape, dtype=torch.float32, device=q.device) if perm is not None else None,
+            o_rla=torch.empty(desc.batch, desc.hq, desc.q_len, desc.d, dtype=torch.float32, device=q.device))
+    spot_rla_block_states(desc, k, v, perm, bufs.states, bufs.states_perm)
+    spot_rla_prefill(desc, q, bufs.states, bufs.states_perm, idx, cnt, bufs.o_rla)
+    return bufs
+
+
+def rla_decode_state(desc: spot_desc, k_cache, v_cache):
+    """State of the whole cache for decode residual linear attention:
+    fp32 (batch, hkv, d, d) = sum over the cache of exp(k) v^T."""
+    _require(k_cache, "k_cache", dtype=torch.bfloat16)
+    _require(v_cache, "v_cache", dtype=torch.bfloat16)
+    ws = torch.empty(max(spot_workspace_size(desc, SPOT_OP_RLA_DECODE_STATE), 1), dtype=torch.uint8,
+                     device=k_cache.device)
+    state = torch.empty(desc.batch, desc.hkv, desc.d, desc.d, dtype=torch.float32, device=k_cache.device)
+    spot_rla_decode_state(desc, k_cache, v_cache, state, ws)
+    return state
+
+
+def rla_decode(desc: spot_desc, q, k_cache, v_cache, state, idx, cnt, o_rla=None):
+    """Residual linear attention of the decode queries: fp32 (batch, hq, d)."""
+    if o_rla is None:
+        o_rla = torch.empty(desc.batch, desc.hq, desc.d, dtype=torch.float32, device=q.device)
+    spot_rla_decode(desc, q, k_cache, v_cache, state, idx, cnt, o_rla)
+    return o_rla
 
 
 @dataclass

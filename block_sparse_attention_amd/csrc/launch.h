@@ -171,4 +171,40 @@ struct PermCheckArgs {
 hipError_t launch_perm_check(const PermCheckArgs& a, hipStream_t s);
 constexpr int kPermRowsPerGroup = 256;   // query rows per workgroup in the permutation passes
 
+// residual linear attention (feature map exp, no normaliser)
+struct RlaStateArgs {
+  const void* k;         // [pairs, L, d]
+  const void* v;
+  const int32_t* perm;   // [pairs, L] or nullptr: position t of a range reads row perm[t]
+  float* states;         // [pairs, nranges, d, d]
+  int bf16, pairs, d, L, span, nranges;
+};
+hipError_t launch_rla_states(const RlaStateArgs& a, hipStream_t s);
+hipError_t launch_rla_reduce(const float* chunks, float* out, int nranges, int d, int pairs, hipStream_t s);
+constexpr int kRlaMaxBlocks = 4096;     // blocks per sequence (kept and rest lists staged in LDS)
+constexpr int kRlaDecodeSpan = 4096;    // keys per chunk state of the cache
+
+struct RlaPrefillArgs {
+  const void* q;              // [batch, hq, L, d]
+  const float* states;        // [batch, hkv, nb, d, d] natural blocks
+  const float* states_perm;   // same, blocks through the permutation; nullptr: natural everywhere
+  const int32_t* idx;         // [batch, hkv, nb, nb] ascending kept lists
+  const int32_t* cnt;         // [batch, hkv, nb]
+  float* o;                   // [batch, hq, L, d]
+  int bf16, batch, hq, hkv, d, L, block, segment, nb;
+};
+hipError_t launch_rla_prefill(const RlaPrefillArgs& a, hipStream_t s);
+
+struct RlaDecodeArgs {
+  const uint16_t* q;     // [batch, hq, d] bf16
+  const uint16_t* k;     // [batch, hkv, T, d]
+  const uint16_t* v;
+  const float* state;    // [batch, hkv, d, d] state of the whole cache
+  const int32_t* idx;    // [batch, nk]
+  const int32_t* cnt;    // [batch]
+  float* o;              // [batch, hq, d]
+  int batch, hq, hkv, d, T, block, nk;
+};
+hipError_t launch_rla_decode(const RlaDecodeArgs& a, hipStream_t s);
+
 }  // namespace spot

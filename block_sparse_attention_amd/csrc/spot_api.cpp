@@ -173,6 +173,11 @@ int spot_workspace_size(const spot_desc* desc, int op, size_t* bytes) {
       *bytes = spot::perm_workspace_bytes(desc->batch, desc->hkv, int(desc->q_len), desc->hq / desc->hkv, nr);
       break;
     }
+    case SPOT_OP_RLA_DECODE_STATE: {
+      const size_t nr = size_t(ceil_div64(desc->kv_len, spot::kRlaDecodeSpan));
+      *bytes = size_t(desc->batch) * desc->hkv * nr * desc->d * desc->d * sizeof(float);
+      break;
+    }
     case SPOT_OP_DECODE: {
       const int nk = int(ceil_div64(desc->kv_len, desc->block));
       const int ns = spot::decode_num_splits(desc->batch, desc->hkv, nk);
@@ -555,6 +560,100 @@ int spot_validate_perm(const spot_desc* desc, const int32_t* perm, int32_t* bad,
     return fail(SPOT_ERR_UNSUPPORTED, "segment %d (max %d)", desc->segment, spot::kPermMaxSegment);
   spot::PermCheckArgs a{perm, bad, int(desc->q_len), desc->segment, desc->batch * desc->hkv};
   return launched(spot::launch_perm_check(a, static_cast<hipStream_t>(stream)), "validate_perm");
+}
+
+// ---------------------------------------------------------------- residual linear attention
+int spot_rla_block_states(const spot_desc* desc, const void* k, const void* v, const int32_t* perm, float* states,
+                          float* states_perm, void* stream) {
+  int st = check_common(desc);
+  if (st) return st;
+  if ((st = check_prefill_shape(desc))) return st;
+  if (!k || !v || !states) return fail(SPOT_ERR_INVALID, "k, v and states are required");
+  if (perm && (desc->segment <= 0 || !states_perm))
+    return fail(SPOT_ERR_INVALID, "perm needs segment > 0 and states_perm");
+  if (!perm && states_perm) return fail(SPOT_ERR_INVALID, "states_perm given without perm");
+  if ((st = check_aligned16("k", k)) || (st = check_aligned16("v", v)) || (st = check_aligned16("states", states)) ||
+      (st = check_aligned16("states_perm", states_perm)))
+    return st;
+  const int pairs = desc->batch * desc->hkv;
+  if (pairs > 65535) return fail(SPOT_ERR_UNSUPPORTED, "batch * hkv = %d (max 65535)", pairs);
+  const int nb = int(ceil_div64(desc->q_len, desc->block));
+  spot::RlaStateArgs a{k, v, nullptr, states, desc->dtype == SPOT_BF16, pairs, desc->d, int(desc->q_len),
+                       desc->block, nb};
+  if ((st = launched(spot::launch_rla_states(a, static_cast<hipStream_t>(stream)), "rla_block_states"))) return st;
+  if (!perm) return SPOT_OK;
+  a.perm = perm;
+  a.states = states_perm;
+  return launched(spot::launch_rla_states(a, static_cast<hipStream_t>(stream)), "rla_block_states (permuted)");
+}
+
+int spot_rla_prefill(const spot_desc* desc, const void* q, const float* states, const float* states_perm,
+                     const int32_t* idx, const int32_t* cnt, float* o_rla, void* stream) {
+  int st = check_common(desc);
+  if (st) return st;
+  if ((st = check_prefill_shape(desc))) return st;
+  if (!q || !states || !idx || !cnt || !o_rla) return fail(SPOT_ERR_INVALID, "q, states, idx, cnt and o_rla are required");
+  if (states_perm && desc->segment <= 0) return fail(SPOT_ERR_INVALID, "states_perm given but segment is 0");
+  if (desc->n_recent < 1)
+    return fail(SPOT_ERR_UNSUPPORTED, "residual linear attention needs n_recent >= 1 (each query block keeps its own block)");
+  const int nb = int(ceil_div64(desc->q_len, desc->block));
+  if (nb > spot::kRlaMaxBlocks) return fail(SPOT_ERR_UNSUPPORTED, "%d blocks per sequence (max %d)", nb, spot::kRlaMaxBlocks);
+  const long long units = (long long)desc->batch * desc->hkv * nb;
+  if (units > 0x7fffffffLL) return fail(SPOT_ERR_UNSUPPORTED, "too many work units");
+  if ((st = check_aligned16("q", q)) || (st = check_aligned16("states", states)) ||
+      (st = check_aligned16("states_perm", states_perm)))
+    return st;
+  spot::RlaPrefillArgs a{q, states, states_perm, idx, cnt, o_rla, desc->dtype == SPOT_BF16, desc->batch, desc->hq,
+                         desc->hkv, desc->d, int(desc->q_len), desc->block, desc->segment, nb};
+  return launched(spot::launch_rla_prefill(a, static_cast<hipStream_t>(stream)), "rla_prefill");
+}
+
+static int check_rla_decode(const spot_desc* desc) {
+  int st = check_common(desc);
+  if (st) return st;
+  if (desc->q_len != 1) return fail(SPOT_ERR_INVALID, "decode needs q_len == 1");
+  if (desc->dtype != SPOT_BF16) return fail(SPOT_ERR_UNSUPPORTED, "decode supports bf16 only");
+  const int G = desc->hq / desc->hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(SPOT_ERR_UNSUPPORTED, "hq/hkv = %d (supported: 1, 2, 4, 8)", G);
+  if (desc->batch * desc->hkv > 65535) return fail(SPOT_ERR_UNSUPPORTED, "batch * hkv = %d (max 65535)", desc->batch * desc->hkv);
+  return SPOT_OK;
+}
+
+int spot_rla_decode_state(const spot_desc* desc, const void* k_cache, const void* v_cache, float* state,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_rla_decode(desc);
+  if (st) return st;
+  if (!k_cache || !v_cache || !state) return fail(SPOT_ERR_INVALID, "k_cache, v_cache and state are required");
+  const int pairs = desc->batch * desc->hkv;
+  const int nr = int(ceil_div64(desc->kv_len, spot::kRlaDecodeSpan));
+  const size_t need = size_t(pairs) * nr * desc->d * desc->d * sizeof(float);
+  if ((st = check_workspace(need, workspace, workspace_bytes))) return st;
+  if ((st = check_aligned16("k_cache", k_cache)) || (st = check_aligned16("v_cache", v_cache)) ||
+      (st = check_aligned16("state", state)) || (st = check_aligned16("workspace", workspace)))
+    return st;
+  spot::RlaStateArgs a{k_cache, v_cache, nullptr, static_cast<float*>(workspace), 1, pairs, desc->d,
+                       int(desc->kv_len), spot::kRlaDecodeSpan, nr};
+  if ((st = launched(spot::launch_rla_states(a, static_cast<hipStream_t>(stream)), "rla_decode_state (chunks)")))
+    return st;
+  return launched(spot::launch_rla_reduce(static_cast<const float*>(workspace), state, nr, desc->d, pairs,
+                                          static_cast<hipStream_t>(stream)),
+                  "rla_decode_state (sum)");
+}
+
+int spot_rla_decode(const spot_desc* desc, const void* q, const void* k_cache, const void* v_cache,
+                    const float* state, const int32_t* idx, const int32_t* cnt, float* o_rla, void* stream) {
+  int st = check_rla_decode(desc);
+  if (st) return st;
+  if (!q || !k_cache || !v_cache || !state || !idx || !cnt || !o_rla)
+    return fail(SPOT_ERR_INVALID, "q, k_cache, v_cache, state, idx, cnt and o_rla are required");
+  if ((st = check_aligned16("k_cache", k_cache)) || (st = check_aligned16("v_cache", v_cache)))
+    return st;
+  if (reinterpret_cast<uintptr_t>(q) & 1u) return fail(SPOT_ERR_INVALID, "q must be 2-byte aligned");
+  const int nk = int(ceil_div64(desc->kv_len, desc->block));
+  spot::RlaDecodeArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+                        static_cast<const uint16_t*>(v_cache), state, idx, cnt, o_rla, desc->batch, desc->hq,
+                        desc->hkv, desc->d, int(desc->kv_len), desc->block, nk};
+  return launched(spot::launch_rla_decode(a, static_cast<hipStream_t>(stream)), "rla_decode");
 }
 
 }  // extern "C"

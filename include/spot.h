@@ -94,7 +94,8 @@ enum spot_op {
   SPOT_OP_KEY_PERMUTATION = 4,
   SPOT_OP_ORDER_HISTORY = 5,
   SPOT_OP_PREFILL_EARLY_STOP = 6,
-  SPOT_OP_HISTORY_MAP = 7
+  SPOT_OP_HISTORY_MAP = 7,
+  SPOT_OP_RLA_DECODE_STATE = 8
 };
 
 /* Problem descriptor.  `version` must be SPOT_ABI_VERSION. */
@@ -378,6 +379,56 @@ int spot_history_map(const spot_desc* desc, const void* q, const void* k, int32_
 int spot_sparse_attn_prefill_history_map(const spot_desc* desc, float tau, const void* q, const void* k,
                                          const void* v, const int32_t* hmap, void* o, float* lse, int32_t* nused,
                                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Residual linear attention ([SPLA] §2.2: the blocks outside the selection
+ * enter through linear attention, evaluated as the all-blocks estimate minus
+ * the selected-blocks estimate; §2.3: parameter-free exponential feature
+ * map).  For a query row q with kept key set K(q) and visible key set A(q):
+ *   o_rla = sum over t in A(q) \ K(q) of (phi(q) . phi(k_t)) v_t,
+ *   phi(x) = exp(x) elementwise on the raw q and k rows, no normaliser
+ * (the page normalises the branch afterwards with a trained RMS norm and
+ * gates it into the output; those trained parts are not in this library).
+ * Prefill: A = {t <= r}, K = the keys of the row's kept blocks (earlier
+ * segments through the permutation, as in spot_sparse_attn_prefill).
+ * Decode: A = the whole cache, K = the keys of the kept blocks.
+ * Linear attention is evaluated through d x d fp32 states
+ * S = sum_t phi(k_t) v_t^T of key ranges; every sum runs in a fixed order in
+ * fp32, so results are deterministic.  Outputs are fp32.
+ *
+ * spot_rla_block_states: prefill descriptor.  states [batch, hkv, nb, d, d]:
+ *   the state of each key block j (rows jB .. min((j+1)B, L)); with perm (and
+ *   segment > 0) also states_perm, the state of the rows perm[b,g,t] for t in
+ *   block j.  k, v: [batch, hkv, L, d] (bf16 or fp32), 16-byte aligned;
+ *   states 16-byte aligned.  perm entries outside [0, L) are clamped (wrong
+ *   sums, never out-of-range reads).  No workspace.
+ * spot_rla_prefill: prefill descriptor.  q [batch, hq, L, d], the states
+ *   above (states_perm non-NULL: blocks of earlier segments use it; requires
+ *   segment > 0), the kept lists idx/cnt of spot_select_topp ->
+ *   o_rla fp32 [batch, hq, L, d].  Each query block's own block must be in
+ *   its list, which n_recent >= 1 guarantees: n_recent = 0 returns
+ *   SPOT_ERR_UNSUPPORTED.  nb <= 4096.  q and the states 16-byte aligned.
+ *   No workspace.
+ * spot_rla_decode_state: decode descriptor (bf16).  state [batch, hkv, d, d]
+ *   = the state of the whole cache [0, kv_len), built from chunk states in
+ *   the workspace (spot_workspace_size(SPOT_OP_RLA_DECODE_STATE)).  Run when
+ *   the cache changes, not per step.  k_cache, v_cache, state and workspace
+ *   16-byte aligned.
+ * spot_rla_decode: decode descriptor (bf16, hq/hkv in 1, 2, 4, 8).  q
+ *   [batch, hq, d], the caches, the state above and the kept lists of
+ *   spot_select_topp -> o_rla fp32 [batch, hq, d] = phi(q)^T state minus the
+ *   linear attention over the kept keys (only the kept blocks are read; list
+ *   entries outside the cache add nothing).  k_cache, v_cache 16-byte
+ *   aligned.  No workspace.
+ */
+int spot_rla_block_states(const spot_desc* desc, const void* k, const void* v, const int32_t* perm, float* states,
+                          float* states_perm, void* stream);
+int spot_rla_prefill(const spot_desc* desc, const void* q, const float* states, const float* states_perm,
+                     const int32_t* idx, const int32_t* cnt, float* o_rla, void* stream);
+int spot_rla_decode_state(const spot_desc* desc, const void* k_cache, const void* v_cache, float* state,
+                          void* workspace, size_t workspace_bytes, void* stream);
+int spot_rla_decode(const spot_desc* desc, const void* q, const void* k_cache, const void* v_cache,
+                    const float* state, const int32_t* idx, const int32_t* cnt, float* o_rla, void* stream);
 
 #ifdef __cplusplus
 }

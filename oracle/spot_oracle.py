@@ -504,18 +504,20 @@ def rla_prefill(q, k, v, kept_lists, block, segment=0, perm=None, qblocks=None):
     nb = n_blocks(L, block)
     qblocks = range(nb) if qblocks is None else qblocks
     out = np.full((hq, L, d), np.nan)
+    qblocks = [int(i) for i in qblocks]
+    top = min(L, (max(qblocks) + 1) * block) if qblocks else 0   # no row of these blocks sees a key beyond
     for g in range(hkv):
-        fk = rla_feature(k[g])
+        fk = rla_feature(k[g, :top])
         for i in qblocks:
-            i = int(i)
             rows = block_rows(i, block, L)
+            hi = rows[-1] + 1
             phys, lim = prefill_key_set(kept_lists[g][i], i, g, block, segment, perm, L)
-            rest = np.arange(L)[None, :] <= rows[:, None]               # visible keys of each row
+            rest = np.arange(hi)[None, :] <= rows[:, None]              # visible keys of each row
             for r_idx, r in enumerate(rows):
                 rest[r_idx, phys[lim <= r]] = False                     # minus the row's kept keys
             for h in range(g * G, (g + 1) * G):
-                w = (rla_feature(q[h, rows]) @ fk.T) * rest             # (rows, L)
-                out[h, rows] = w @ v[g]
+                w = (rla_feature(q[h, rows]) @ fk[:hi].T) * rest        # (rows, keys up to the last row)
+                out[h, rows] = w @ v[g, :hi]
     return out
 
 

@@ -327,3 +327,48 @@ def test_history_map_validation():
     for kw in (dict(q=FAKE + 8), dict(k=FAKE + 4), dict(v=FAKE + 2), dict(o=FAKE + 4)):
         assert att(_prefill(segment=256), **kw) == B.SPOT_ERR_INVALID, kw
     assert att(_prefill(segment=256, block=16)) == B.SPOT_ERR_UNSUPPORTED
+
+
+def test_rla_validation():
+    """Residual linear attention entry points: every rejected call returns
+    before anything is launched (the pointers here are never dereferenced)."""
+    lib = B.load_library()
+
+    def st(d, k=FAKE, v=FAKE, perm=None, s=FAKE, sp=None):
+        return lib.spot_rla_block_states(ctypes.byref(d), k, v, perm, s, sp, None)
+
+    def pre(d, q=FAKE, s=FAKE, sp=None, idx=FAKE, cnt=FAKE, o=FAKE):
+        return lib.spot_rla_prefill(ctypes.byref(d), q, s, sp, idx, cnt, o, None)
+
+    def dst(d, k=FAKE, v=FAKE, s=FAKE, ws=FAKE, ws_bytes=1 << 40):
+        return lib.spot_rla_decode_state(ctypes.byref(d), k, v, s, ws, ws_bytes, None)
+
+    def dec(d, q=FAKE, k=FAKE, v=FAKE, s=FAKE, idx=FAKE, cnt=FAKE, o=FAKE):
+        return lib.spot_rla_decode(ctypes.byref(d), q, k, v, s, idx, cnt, o, None)
+
+    assert st(_prefill(), k=None) == B.SPOT_ERR_INVALID
+    assert st(_prefill(), s=None) == B.SPOT_ERR_INVALID
+    assert st(_prefill(), perm=FAKE) == B.SPOT_ERR_INVALID                     # perm needs segment > 0
+    assert st(_prefill(segment=256), perm=FAKE) == B.SPOT_ERR_INVALID          # ... and states_perm
+    assert st(_prefill(), sp=FAKE) == B.SPOT_ERR_INVALID                       # states_perm without perm
+    assert st(_prefill(), v=FAKE + 8) == B.SPOT_ERR_INVALID                    # 16-byte loads
+    assert st(_prefill(), s=FAKE + 4) == B.SPOT_ERR_INVALID
+    assert st(_prefill(d=96)) == B.SPOT_ERR_UNSUPPORTED
+    assert st(_prefill(batch=70000)) == B.SPOT_ERR_UNSUPPORTED                 # batch * hkv beyond the grid
+    assert pre(_prefill(), o=None) == B.SPOT_ERR_INVALID
+    assert pre(_prefill(), cnt=None) == B.SPOT_ERR_INVALID
+    assert pre(_prefill(n_recent=0)) == B.SPOT_ERR_UNSUPPORTED                 # own block must be kept
+    assert pre(_prefill(), sp=FAKE) == B.SPOT_ERR_INVALID                      # permuted states need segments
+    assert pre(_prefill(q_len=64 * 4097, kv_len=64 * 4097)) == B.SPOT_ERR_UNSUPPORTED   # 4097 blocks
+    assert pre(_prefill(), q=FAKE + 2) == B.SPOT_ERR_INVALID
+    assert dst(_decode(), ws=None) == B.SPOT_ERR_WORKSPACE
+    assert dst(_decode(), ws_bytes=16) == B.SPOT_ERR_WORKSPACE
+    assert dst(_decode(dtype=B.SPOT_F32)) == B.SPOT_ERR_UNSUPPORTED
+    assert dst(_decode(q_len=2)) == B.SPOT_ERR_INVALID
+    assert dst(_decode(), s=FAKE + 4) == B.SPOT_ERR_INVALID
+    assert dec(_decode(hq=6, hkv=2)) == B.SPOT_ERR_UNSUPPORTED                 # G = 3
+    assert dec(_decode(), s=None) == B.SPOT_ERR_INVALID
+    assert dec(_decode(), k=FAKE + 2) == B.SPOT_ERR_INVALID
+    assert dec(_decode(), q=FAKE + 1) == B.SPOT_ERR_INVALID
+    dd = _decode(kv_len=131072)
+    assert B.spot_workspace_size(dd, B.SPOT_OP_RLA_DECODE_STATE) == 2 * 2 * 32 * 128 * 128 * 4

@@ -1,0 +1,139 @@
+"""Residual linear attention ([SPLA] §2.2-2.3) on the GPU against the float64
+oracle, evaluated on the GPU's own kept lists (and, with a permutation, the
+oracle's permutation given to both sides).
+
+Window: the GPU sums in fp32 in a fixed order: a block (or cache chunk) state
+over its keys, the residual over the block states, the output over d.  With
+unit roundoff u = 2^-24 the error of such a sum of n terms is at most about
+n u times the sum of the terms' magnitudes, and every term here is
+phi(q).phi(k_t) * |v_t| summed over the keys involved (phi > 0), so
+    |o_gpu - o| <= (n_terms * u + 2^-20) * sum_t (phi(q).phi(k_t)) |v_t|
+per element, with n_terms the longest chain of additions and 2^-20 covering
+the two fp32 exponentials (a few ulp each).  The magnitude sum is the oracle
+run on |v|.  A block added or dropped changes the output by about
+1/(blocks in the sum) of that magnitude, far above the window (in decode the
+magnitude is that of the whole cache: on the short caches below a block of 16
+keys is 0.16-5% of it, against windows of 2.7-3.3e-4)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_amd import binding as B
+from block_sparse_attention_amd import inputs as I
+from tests import parity as P
+from tests.test_gpu_parity import gpu_prefill, log, upload_prefill
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+EXP_SLACK = 2.0 ** -20
+SPAN = 4096   # keys per cache chunk state in decode
+
+
+def _check(name, got, ref, mag, n_terms):
+    tol = n_terms * U + EXP_SLACK
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    assert np.isfinite(got).all(), name
+    ratio = float(np.max(err / np.maximum(mag, 1e-300))) if err.size else 0.0
+    log(name, f"max|d|={float(err.max()) if err.size else 0.0:.3g}", f"max |d|/mag={ratio:.3g}", f"window {tol:.3g}")
+    assert np.all(err <= tol * mag), (name, ratio, tol)
+
+
+def _prefill_case(cfg, gpu, top_p=None, perm=None, qblocks=None):
+    host, dev = upload_prefill(cfg, gpu, perm)
+    bufs = gpu_prefill(cfg, dev, perm_dev=dev[3], top_p=top_p)
+    desc = B.prefill_desc(dev[0], dev[1], cfg.block, cfg.top_p if top_p is None else top_p,
+                          segment=cfg.segment if perm is not None else 0)
+    rb = B.rla_prefill(desc, dev[0], dev[1], dev[2], bufs.idx, bufs.cnt, perm=dev[3])
+    torch.cuda.synchronize()
+    q, k, v = host
+    lists = P.kept_lists(bufs.idx, bufs.cnt)[0]
+    got = rb.o_rla.cpu().numpy()[0]
+    qb = np.arange(cfg.nb) if qblocks is None else np.asarray(qblocks)
+    seg = cfg.segment if perm is not None else 0
+    pm = None if perm is None else perm[0]
+    ref = oracle.spot_oracle.rla_prefill(q[0], k[0], v[0], lists, cfg.block, segment=seg, perm=pm, qblocks=qb)
+    mag = oracle.spot_oracle.rla_prefill(q[0], k[0], np.abs(v[0]), lists, cfg.block, segment=seg, perm=pm,
+                                         qblocks=qb)
+    rows = np.concatenate([np.arange(i * cfg.block, min((i + 1) * cfg.block, cfg.L)) for i in qb])
+    return got[:, rows], ref[:, rows], mag[:, rows], lists
+
+
+@pytest.mark.parametrize("kw", [dict(L=256, hq=1, hkv=1, d=64, dtype="f32", block=16, seed=1),
+                                dict(L=1000, hq=8, hkv=2, d=128, block=64, seed=21),
+                                dict(L=777, hq=4, hkv=1, d=64, block=32, seed=22),
+                                dict(L=640, hq=16, hkv=2, d=128, block=128, seed=23, top_p=0.6)],
+                         ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_rla_prefill_small(gpu, kw):
+    cfg = I.small_prefill(name="rla", **kw)
+    got, ref, mag, _ = _prefill_case(cfg, gpu)
+    _check(cfg.name + str(kw), got, ref, mag, cfg.block + cfg.nb + cfg.d)
+
+
+def test_rla_prefill_with_permutation(gpu):
+    cfg = I.small_prefill(name="rla-perm", L=2048, hq=8, hkv=2, d=128, block=64, segment=512, seed=24,
+                          heavy_hitters=True)
+    q, k, _ = I.prefill_inputs(cfg)
+    perm, _ = oracle.key_permutation(q[0], k[0], cfg.block, cfg.segment, 1 / math.sqrt(cfg.d))
+    got, ref, mag, _ = _prefill_case(cfg, gpu, perm=perm[None])
+    _check("rla permuted", got, ref, mag, cfg.block + cfg.nb + cfg.d)
+
+
+def test_rla_prefill_keep_all_is_zero(gpu):
+    cfg = I.small_prefill(name="rla-all", L=512, hq=8, hkv=2, d=128, block=64, seed=25)
+    got, ref, mag, _ = _prefill_case(cfg, gpu, top_p=1.0)
+    assert np.all(ref == 0.0) and np.all(got == 0.0)
+
+
+def test_rla_prefill_c2_sampled(gpu):
+    """The GQA workload at full size (every block state and residual on the
+    GPU), checked on four query blocks."""
+    cfg = I.C2
+    got, ref, mag, _ = _prefill_case(cfg, gpu, qblocks=[0, 1, 64, cfg.nb - 1])
+    _check("rla C2", got, ref, mag, cfg.block + cfg.nb + cfg.d)
+
+
+def test_rla_prefill_c5_sampled(gpu):
+    """The long-context workload at full size, checked on three early query
+    blocks (the oracle's cost grows with the prefix)."""
+    cfg = I.C5
+    got, ref, mag, _ = _prefill_case(cfg, gpu, qblocks=[1, 2, 21])
+    _check("rla C5", got, ref, mag, cfg.block + cfg.nb + cfg.d)
+
+
+def _decode_case(cfg, gpu, seqs=None, top_p=None):
+    D = I.decode_inputs(cfg)
+    dev = {k: (torch.from_numpy(v).to(gpu) if k == "idx_w" else P.to_dev(v, "bf16", gpu)) for k, v in D.items()}
+    p = cfg.top_p if top_p is None else top_p
+    bufs = B.decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["idx_q"], dev["idx_w"], dev["idx_k"], cfg.block, p)
+    desc = B.decode_desc(dev["q"], dev["k_cache"], cfg.block, p, cfg.h_idx, cfg.d_idx)
+    state = B.rla_decode_state(desc, dev["k_cache"], dev["v_cache"])
+    o = B.rla_decode(desc, dev["q"], dev["k_cache"], dev["v_cache"], state, bufs.idx, bufs.cnt)
+    torch.cuda.synchronize()
+    got = o.cpu().numpy()
+    gl, gc = bufs.idx.cpu().numpy()[:, 0, 0], bufs.cnt.cpu().numpy()[:, 0, 0]
+    n_terms = SPAN + -(-cfg.T // SPAN) + 2 * cfg.d + int(gc.max()) * cfg.block
+    for b in (range(cfg.batch) if seqs is None else seqs):
+        kept = gl[b, :gc[b]]
+        ref = oracle.spot_oracle.rla_decode(D["q"][b], D["k_cache"][b], D["v_cache"][b], kept, cfg.block, cfg.T)
+        mag = oracle.spot_oracle.rla_decode(D["q"][b], D["k_cache"][b], np.abs(D["v_cache"][b]), [], cfg.block,
+                                            cfg.T)
+        _check(f"{cfg.name} seq {b} kept {len(kept)}", got[b], ref, mag, n_terms)
+    return got
+
+
+@pytest.mark.parametrize("kw", [dict(batch=2, T=2000), dict(batch=2, T=10000 + 7, hq=16, hkv=2),
+                                dict(batch=1, T=4096 * 2, hq=8, hkv=8, d=64), dict(batch=3, T=300, top_p=0.5)],
+                         ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_rla_decode_small(gpu, kw):
+    cfg = I.C4.with_(name="rla-dec", seed=41, **kw)
+    _decode_case(cfg, gpu)
+
+
+def test_rla_decode_c4(gpu):
+    """The decode workload (batch 16, context 131072): the whole-cache state
+    and the residual of every sequence on the GPU, three sequences checked."""
+    _decode_case(I.C4, gpu, seqs=[0, 7, 15])

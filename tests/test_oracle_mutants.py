@@ -31,11 +31,12 @@ MUTANTS = [
      "return np.exp(np.asarray(x, dtype=np.float64))",
      "return np.exp(np.asarray(x, dtype=np.float64) / np.sqrt(np.shape(x)[-1]))"),
     ("RLA rest without the causal mask", RLA,
-     "rest = np.arange(L)[None, :] <= rows[:, None]", "rest = np.ones((rows.shape[0], L), dtype=bool)"),
+     "rest = np.arange(hi)[None, :] <= rows[:, None]", "rest = np.ones((rows.shape[0], hi), dtype=bool)"),
     ("RLA removes only the history keys it keeps", RLA,
      "rest[r_idx, phys[lim <= r]] = False", "rest[r_idx, phys[lim < 0]] = False"),
     ("RLA normalised by the feature mass", RLA,
-     "out[h, rows] = w @ v[g]", "out[h, rows] = (w @ v[g]) / np.maximum(w.sum(axis=1, keepdims=True), 1e-300)"),
+     "out[h, rows] = w @ v[g, :hi]",
+     "out[h, rows] = (w @ v[g, :hi]) / np.maximum(w.sum(axis=1, keepdims=True), 1e-300)"),
     ("RLA decode keeps the kept blocks", RLA,
      "rest[block_rows(int(t), block, T)] = False", "rest[block_rows(int(t), block, T)] = True"),
     ("history rows through the inverse permutation", PINS,
