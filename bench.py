@@ -372,6 +372,79 @@ def bench_decode(args, torch, B, cfg, t, cache="bf16", top_p=None):
     )
 
 
+# ----------------------------------------------------------------- residual linear attention
+def _event_ms(torch, fn, n):
+    times = []
+    for _ in range(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return float(np.median(times))
+
+
+def bench_rla_prefill(args, torch, B, cfg, dev_in):
+    """Residual linear attention ([SPLA] §2.2) beside the prefill step: the
+    block states (once per K/V) and the residual of every query block over
+    the blocks its list does not keep, on the lists of one pipeline step."""
+    dq, dk, dv = dev_in
+    dev = torch.device("cuda:0")
+    desc = B.prefill_desc(dq, dk, cfg.block, cfg.top_p)
+    bufs = B.prefill(dq, dk, dv, cfg.block, cfg.top_p)
+    rb = B.rla_prefill(desc, dq, dk, dv, bufs.idx, bufs.cnt)
+    torch.cuda.synchronize()
+    n = max(args.steps // 2, 3)
+    ms_states = _event_ms(torch, lambda: B.spot_rla_block_states(desc, dk, dv, None, rb.states), n)
+    ms_res = _event_ms(torch, lambda: B.spot_rla_prefill(desc, dq, rb.states, None, bufs.idx, bufs.cnt, rb.o_rla), n)
+    cnt = bufs.cnt.cpu().numpy().astype(np.int64)                      # (batch, hkv, nb), own block included
+    rest_blocks = float((np.arange(cfg.nb)[None, None, :] + 1 - cnt).clip(min=0).sum())
+    d2 = cfg.d * cfg.d
+    state_flop = 2.0 * d2 * cfg.L * cfg.hkv * cfg.batch
+    out_flop = 2.0 * d2 * cfg.L * cfg.hq * cfg.batch
+    res_bytes = rest_blocks * d2 * 4.0
+    del rb, bufs
+    return {"workload": cfg.name, "ms_block_states": round(ms_states, 4), "ms_residual": round(ms_res, 4),
+            "block_states_tflops": round(state_flop / (ms_states * 1e-3) / 1e12, 2),
+            "residual_state_reads_gb": round(res_bytes / 1e9, 3),
+            "residual_gbs": round(res_bytes / (ms_res * 1e-3) / 1e9, 1),
+            "residual_output_tflops": round(out_flop / (ms_res * 1e-3) / 1e12, 2),
+            "blocks_outside_lists": int(rest_blocks)}
+
+
+def bench_rla_decode(args, torch, B, cfg, t):
+    """Residual linear attention of the decode step: the whole-cache state is
+    built once (it changes only with the cache); per step the state's
+    contribution minus the kept keys', on the lists of the bf16-indexer step."""
+    dev = torch.device("cuda:0")
+    q, kc, vc = t["q"], t["kc"], t["vc"]
+    desc = B.decode_desc(q, kc, cfg.block, cfg.top_p, cfg.h_idx, cfg.d_idx)
+    bufs = B.decode(q, kc, vc, t["iq"], t["iw"], t["ik"], cfg.block, cfg.top_p)
+    ws = torch.empty(max(B.spot_workspace_size(desc, B.SPOT_OP_RLA_DECODE_STATE), 1), dtype=torch.uint8, device=dev)
+    state = torch.empty(cfg.batch, cfg.hkv, cfg.d, cfg.d, dtype=torch.float32, device=dev)
+    o = torch.empty(cfg.batch, cfg.hq, cfg.d, dtype=torch.float32, device=dev)
+    dws = torch.empty(max(B.spot_workspace_size(desc, B.SPOT_OP_RLA_DECODE), 1), dtype=torch.uint8, device=dev)
+    ms_state = _event_ms(torch, lambda: B.spot_rla_decode_state(desc, kc, vc, state, ws), 2)
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    times = []
+    for _ in range(max(args.steps, 3)):
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        B.spot_rla_decode(desc, q, kc, vc, state, bufs.idx, bufs.cnt, o, dws)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    cnt = bufs.cnt.cpu().numpy()[:, 0, 0].astype(np.int64)
+    kv_bytes = float(cnt.sum()) * cfg.block * cfg.hkv * cfg.d * 2 * 2
+    st_bytes = cfg.batch * cfg.hkv * cfg.d * cfg.d * 4.0
+    del ws, flush
+    return {"workload": cfg.name, "ms_cache_state": round(ms_state, 4), "ms_per_step": round(ms, 4),
+            "bytes_per_step": kv_bytes + st_bytes, "gbs": round((kv_bytes + st_bytes) / (ms * 1e-3) / 1e9, 1)}
+
+
 # ----------------------------------------------------------------- early stopping
 def bench_early_stop(args, torch, B, cfg, dev_in):
     """Early-stopped prefill on the heavy-hitter workload (L=32768, segment
@@ -711,6 +784,8 @@ def main():
                                        "ms_score_select": round(t["ms_sel"], 4),
                                        "ms_attention": round(t["ms_attn"], 4),
                                        "kept_fraction": round(t["kept_fraction"], 4), "flop_per_step": t["flops"]}
+            if cfg.name == I.C2.name:
+                obj["residual_linear_attention"] = bench_rla_prefill(args, torch, B, cfg, dev_in)
             if cfg.name == I.C3.name and not args.no_early_stop:
                 obj["early_stop"] = bench_early_stop(args, torch, B, cfg, dev_in)
                 obj["early_stop_history_map"] = bench_history_map(args, torch, B, cfg, dev_in)
@@ -729,6 +804,8 @@ def main():
             # every block kept (p = 1): the attention streams the whole 8 GiB KV cache
             dec["keep_all"] = bench_decode(args, torch, B, dcfg, t, top_p=1.0)
             say(f"decode keep-all: {dec['keep_all']}")
+            dec["residual_linear_attention"] = bench_rla_decode(args, torch, B, dcfg, t)
+            say(f"decode residual linear attention: {dec['residual_linear_attention']}")
             configs[dcfg.name] = dict(dec, workload=dcfg.name, batch=dcfg.batch, context=dcfg.T, hq=dcfg.hq,
                                       hkv=dcfg.hkv, d=dcfg.d, block=dcfg.block, h_idx=dcfg.h_idx, d_idx=dcfg.d_idx,
                                       top_p=dcfg.top_p)

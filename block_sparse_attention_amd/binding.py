@@ -21,6 +21,7 @@ SPOT_F32, SPOT_BF16 = 0, 1
 SPOT_SCORE_MEANPOOL, SPOT_SCORE_RELU_INDEXER, SPOT_SCORE_TAYLOR = 0, 1, 2
 SPOT_OP_BLOCK_SCORE, SPOT_OP_SELECT_TOPP, SPOT_OP_PREFILL, SPOT_OP_DECODE, SPOT_OP_KEY_PERMUTATION = 0, 1, 2, 3, 4
 SPOT_OP_ORDER_HISTORY, SPOT_OP_PREFILL_EARLY_STOP, SPOT_OP_HISTORY_MAP, SPOT_OP_RLA_DECODE_STATE = 5, 6, 7, 8
+SPOT_OP_RLA_DECODE = 9
 ABI_VERSION = 1
 
 EXPORTS = ("spot_version", "spot_status_string", "spot_last_error", "spot_workspace_size", "spot_block_score",
@@ -86,7 +87,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spot_rla_block_states.argtypes = [D, P, P, P, P, P, P]
     lib.spot_rla_prefill.argtypes = [D, P, P, P, P, P, P, P]
     lib.spot_rla_decode_state.argtypes = [D, P, P, P, P, S, P]
-    lib.spot_rla_decode.argtypes = [D, P, P, P, P, P, P, P, P]
+    lib.spot_rla_decode.argtypes = [D, P, P, P, P, P, P, P, P, S, P]
     for name in EXPORTS[3:]:
         getattr(lib, name).restype = I
     _lib = lib
@@ -247,9 +248,11 @@ def spot_rla_decode_state(desc, k_cache, v_cache, state, workspace=None, stream=
     _check("spot_rla_decode_state", st)
 
 
-def spot_rla_decode(desc, q, k_cache, v_cache, state, idx, cnt, o_rla, stream=None):
+def spot_rla_decode(desc, q, k_cache, v_cache, state, idx, cnt, o_rla, workspace=None, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load_library().spot_rla_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(state),
-                                        _ptr(idx), _ptr(cnt), _ptr(o_rla), _stream() if stream is None else stream)
+                                        _ptr(idx), _ptr(cnt), _ptr(o_rla), _ptr(workspace), ws_bytes,
+                                        _stream() if stream is None else stream)
     _check("spot_rla_decode", st)
 
 
@@ -476,11 +479,14 @@ def rla_decode_state(desc: spot_desc, k_cache, v_cache):
     return state
 
 
-def rla_decode(desc: spot_desc, q, k_cache, v_cache, state, idx, cnt, o_rla=None):
+def rla_decode(desc: spot_desc, q, k_cache, v_cache, state, idx, cnt, o_rla=None, workspace=None):
     """Residual linear attention of the decode queries: fp32 (batch, hq, d)."""
     if o_rla is None:
         o_rla = torch.empty(desc.batch, desc.hq, desc.d, dtype=torch.float32, device=q.device)
-    spot_rla_decode(desc, q, k_cache, v_cache, state, idx, cnt, o_rla)
+    if workspace is None:
+        workspace = torch.empty(max(spot_workspace_size(desc, SPOT_OP_RLA_DECODE), 1), dtype=torch.uint8,
+                                device=q.device)
+    spot_rla_decode(desc, q, k_cache, v_cache, state, idx, cnt, o_rla, workspace)
     return o_rla
 
 

@@ -19,10 +19,12 @@
 //                     then phi(q)^T R for the G*B rows of the block.  Block i
 //                     itself is always kept (recency), so no partial block
 //                     enters, and the set is the same for every row of i.
-// rla_decode_kernel   per (batch, KV head): phi(q)^T S_cache minus the linear
+// rla_decode_split_kernel + rla_decode_combine_kernel
+//                     per (batch, KV head): phi(q)^T S_cache minus the linear
 //                     attention over the kept keys read from the cache (the
 //                     page's difference of the all-blocks and kept-blocks
-//                     estimates: only the kept blocks are read).
+//                     estimates: only the kept blocks are read), the kept
+//                     keys split over several workgroups.
 // Every sum runs in a fixed order in fp32, so results are deterministic.
 #include "../launch.h"
 #include "common.h"
@@ -259,68 +261,99 @@ __global__ __launch_bounds__(256) void rla_prefill_kernel(RlaPrefillArgs a) {
 }
 
 // ---------------------------------------------------------------- decode
+// rla_decode_split_kernel: workgroup (split, pair) takes its share of the
+// rows of S_cache for phi(q)^T S_cache and the kept key slots in chunks of
+// kRlaStage (chunk c = split, split + nsplit, ...; the next chunk's rows are
+// loaded while the current one is used), and writes its share of the state
+// term minus its partial linear attention over those keys (G x D floats).
+// rla_decode_combine_kernel: per pair, the sum of the partials in split order.
 template <int D, int G>
-__global__ __launch_bounds__(256) void rla_decode_kernel(RlaDecodeArgs a) {
+__global__ __launch_bounds__(256) void rla_decode_split_kernel(RlaDecodeArgs a) {
   constexpr int LD = D + 4;
   constexpr int OUTS = (G * D + 255) / 256;   // outputs (head, column) per thread
-  constexpr int PIECES = kRlaStage * D / 8;
+  constexpr int PIECES = kRlaStage * D / 8;   // 16-byte pieces of a staged chunk, per tensor
+  constexpr int PPT = (PIECES + 255) / 256;
   static_assert(G * kRlaStage <= 256, "one key-head dot product per thread");
   __shared__ __attribute__((aligned(16))) float fq[G * D];
   __shared__ __attribute__((aligned(16))) float fk[kRlaStage * LD];
   __shared__ __attribute__((aligned(16))) float fv[kRlaStage * LD];
   __shared__ float w[G * kRlaStage];
   const int tid = threadIdx.x;
-  const int pair = blockIdx.x;
+  const int split = blockIdx.x, pair = blockIdx.y;
   const int b = pair / a.hkv, g = pair % a.hkv;
   const int B = a.block, T = a.T;
   for (int e = tid; e < G * D; e += 256)
     fq[e] = expf(bf16_to_f32(a.q[(size_t(b) * a.hq + g * G + e / D) * D + e % D]));
   __syncthreads();
 
-  // phi(q)^T S over the whole cache; the thread's column c is the same for all its outputs
-  const int c = tid % D;
-  float obar[OUTS], otil[OUTS];
+  // this split's share of phi(q)^T S_cache: rows k0 .. k1 of the state
+  const int c_col = tid % D;
+  float part_o[OUTS];
 #pragma unroll
-  for (int u = 0; u < OUTS; ++u) obar[u] = otil[u] = 0.f;
-  const float* S = a.state + size_t(pair) * D * D;
-#pragma unroll 8
-  for (int k = 0; k < D; ++k) {
-    const float sk = S[k * D + c];
+  for (int u = 0; u < OUTS; ++u) part_o[u] = 0.f;
+  {
+    const int rows_per = (D + a.nsplit - 1) / a.nsplit;
+    const int k0 = min(D, split * rows_per), k1 = min(D, k0 + rows_per);
+    const float* S = a.state + size_t(pair) * D * D;
+    for (int k = k0; k < k1; ++k) {
+      const float sk = S[k * D + c_col];
 #pragma unroll
-    for (int u = 0; u < OUTS; ++u) {
-      const int o = tid + u * 256;
-      if (o < G * D) obar[u] = fmaf(fq[(o / D) * D + k], sk, obar[u]);
+      for (int u = 0; u < OUTS; ++u) {
+        const int o = tid + u * 256;
+        if (o < G * D) part_o[u] = fmaf(fq[(o / D) * D + k], sk, part_o[u]);
+      }
     }
   }
 
-  // linear attention over the kept keys, kRlaStage key slots at a time
   const int nkept = min(max(a.cnt[b], 0), a.nk);
   const int32_t* list = a.idx + size_t(b) * a.nk;
   const uint16_t* K = a.k + size_t(pair) * T * D;
   const uint16_t* V = a.v + size_t(pair) * T * D;
   const int nslots = nkept * B;
-  for (int s0 = 0; s0 < nslots; s0 += kRlaStage) {
-    for (int pc = tid; pc < PIECES; pc += 256) {
+  const int nchunks = (nslots + kRlaStage - 1) / kRlaStage;
+  uint4 kr[PPT], vr[PPT];
+  bool ok[PPT];
+  auto fetch = [&](int c) {
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+      const int pc = tid + p * 256;
       const int row = pc / (D / 8), col = (pc % (D / 8)) * 8;
-      const int sl = s0 + row;
-      const long long pos = sl < nslots ? (long long)list[sl / B] * B + sl % B : (long long)T;
-      float kx[8], vx[8];
-      if (pos >= 0 && pos < T) {   // list entries outside the cache add nothing
-        load8(K + size_t(pos) * D + col, kx);
-        load8(V + size_t(pos) * D + col, vx);
+      const int sl = c * kRlaStage + row;
+      const long long pos = (pc < PIECES && sl < nslots) ? (long long)list[sl / B] * B + sl % B : -1;
+      ok[p] = pos >= 0 && pos < T;   // list entries outside the cache add nothing
+      kr[p] = ok[p] ? *reinterpret_cast<const uint4*>(K + size_t(pos) * D + col) : make_uint4(0u, 0u, 0u, 0u);
+      vr[p] = ok[p] ? *reinterpret_cast<const uint4*>(V + size_t(pos) * D + col) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  float otil[OUTS];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kx[e] = expf(kx[e]);
-      } else {
+  for (int u = 0; u < OUTS; ++u) otil[u] = 0.f;
+  if (split < nchunks) fetch(split);
+  for (int c = split; c < nchunks; c += a.nsplit) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kx[e] = vx[e] = 0.f;
-      }
+    for (int p = 0; p < PPT; ++p) {
+      const int pc = tid + p * 256;
+      if (pc < PIECES) {
+        const int row = pc / (D / 8), col = (pc % (D / 8)) * 8;
+        const uint32_t kw[4] = {kr[p].x, kr[p].y, kr[p].z, kr[p].w};
+        const uint32_t vw[4] = {vr[p].x, vr[p].y, vr[p].z, vr[p].w};
+        float kx[8], vx[8];
 #pragma unroll
-      for (int e = 0; e < 8; e += 4) {
-        *reinterpret_cast<float4*>(fk + row * LD + col + e) = make_float4(kx[e], kx[e + 1], kx[e + 2], kx[e + 3]);
-        *reinterpret_cast<float4*>(fv + row * LD + col + e) = make_float4(vx[e], vx[e + 1], vx[e + 2], vx[e + 3]);
+        for (int e = 0; e < 4; ++e) {
+          kx[2 * e] = ok[p] ? expf(bf16_lo(kw[e])) : 0.f;
+          kx[2 * e + 1] = ok[p] ? expf(bf16_hi(kw[e])) : 0.f;
+          vx[2 * e] = bf16_lo(vw[e]);
+          vx[2 * e + 1] = bf16_hi(vw[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e += 4) {
+          *reinterpret_cast<float4*>(fk + row * LD + col + e) = make_float4(kx[e], kx[e + 1], kx[e + 2], kx[e + 3]);
+          *reinterpret_cast<float4*>(fv + row * LD + col + e) = make_float4(vx[e], vx[e + 1], vx[e + 2], vx[e + 3]);
+        }
       }
     }
     __syncthreads();
+    if (c + a.nsplit < nchunks) fetch(c + a.nsplit);   // in flight while this chunk is used
     if (tid < G * kRlaStage) {
       const int h = tid / kRlaStage, t = tid % kRlaStage;
       float d = 0.f;
@@ -341,16 +374,29 @@ __global__ __launch_bounds__(256) void rla_decode_kernel(RlaDecodeArgs a) {
       if (o < G * D) {
         const int h = o / D;
         float acc = otil[u];
-        for (int t = 0; t < kRlaStage; ++t) acc = fmaf(w[h * kRlaStage + t], fv[t * LD + c], acc);
+        for (int t = 0; t < kRlaStage; ++t) acc = fmaf(w[h * kRlaStage + t], fv[t * LD + c_col], acc);
         otil[u] = acc;
       }
     }
     __syncthreads();
   }
+  float* part = a.partials + (size_t(pair) * a.nsplit + split) * G * D;
 #pragma unroll
   for (int u = 0; u < OUTS; ++u) {
     const int o = tid + u * 256;
-    if (o < G * D) a.o[(size_t(b) * a.hq + g * G + o / D) * D + c] = obar[u] - otil[u];
+    if (o < G * D) part[o] = part_o[u] - otil[u];
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void rla_decode_combine_kernel(RlaDecodeArgs a) {
+  const int pair = blockIdx.x;
+  const int b = pair / a.hkv, g = pair % a.hkv;
+  const float* part = a.partials + size_t(pair) * a.nsplit * G * D;
+  for (int o = threadIdx.x; o < G * D; o += 256) {
+    float r = 0.f;
+    for (int sp = 0; sp < a.nsplit; ++sp) r += part[size_t(sp) * G * D + o];
+    a.o[(size_t(b) * a.hq + g * G + o / D) * D + o % D] = r;
   }
 }
 
@@ -385,15 +431,27 @@ hipError_t launch_rla_prefill(const RlaPrefillArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, int G>
+static void launch_rla_decode_dg(const RlaDecodeArgs& a, hipStream_t s) {
+  const unsigned pairs = unsigned(a.batch * a.hkv);
+  rla_decode_split_kernel<D, G><<<dim3(unsigned(a.nsplit), pairs), 256, 0, s>>>(a);
+  rla_decode_combine_kernel<D, G><<<pairs, 256, 0, s>>>(a);
+}
+
 template <int D>
 static void launch_rla_decode_d(const RlaDecodeArgs& a, hipStream_t s) {
-  const unsigned grid = unsigned(a.batch * a.hkv);
   switch (a.hq / a.hkv) {
-    case 1: rla_decode_kernel<D, 1><<<grid, 256, 0, s>>>(a); break;
-    case 2: rla_decode_kernel<D, 2><<<grid, 256, 0, s>>>(a); break;
-    case 4: rla_decode_kernel<D, 4><<<grid, 256, 0, s>>>(a); break;
-    default: rla_decode_kernel<D, 8><<<grid, 256, 0, s>>>(a); break;
+    case 1: launch_rla_decode_dg<D, 1>(a, s); break;
+    case 2: launch_rla_decode_dg<D, 2>(a, s); break;
+    case 4: launch_rla_decode_dg<D, 4>(a, s); break;
+    default: launch_rla_decode_dg<D, 8>(a, s); break;
   }
+}
+
+int rla_decode_num_splits(int batch, int hkv) {
+  const int pairs = batch * hkv;
+  int n = 1024 / (pairs > 0 ? pairs : 1);   // measured: 8 splits at the decode workload beat 32
+  return n < 1 ? 1 : (n > 64 ? 64 : n);
 }
 
 hipError_t launch_rla_decode(const RlaDecodeArgs& a, hipStream_t s) {

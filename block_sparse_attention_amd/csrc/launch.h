@@ -203,8 +203,10 @@ struct RlaDecodeArgs {
   const int32_t* idx;    // [batch, nk]
   const int32_t* cnt;    // [batch]
   float* o;              // [batch, hq, d]
-  int batch, hq, hkv, d, T, block, nk;
+  float* partials;       // workspace: [batch, hkv, nsplit, G, d]
+  int batch, hq, hkv, d, T, block, nk, nsplit;
 };
 hipError_t launch_rla_decode(const RlaDecodeArgs& a, hipStream_t s);
+int rla_decode_num_splits(int batch, int hkv);
 
 }  // namespace spot

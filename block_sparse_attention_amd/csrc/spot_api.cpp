@@ -178,6 +178,11 @@ int spot_workspace_size(const spot_desc* desc, int op, size_t* bytes) {
       *bytes = size_t(desc->batch) * desc->hkv * nr * desc->d * desc->d * sizeof(float);
       break;
     }
+    case SPOT_OP_RLA_DECODE: {
+      const size_t ns = size_t(spot::rla_decode_num_splits(desc->batch, desc->hkv));
+      *bytes = size_t(desc->batch) * desc->hq * ns * desc->d * sizeof(float);
+      break;
+    }
     case SPOT_OP_DECODE: {
       const int nk = int(ceil_div64(desc->kv_len, desc->block));
       const int ns = spot::decode_num_splits(desc->batch, desc->hkv, nk);
@@ -641,18 +646,24 @@ int spot_rla_decode_state(const spot_desc* desc, const void* k_cache, const void
 }
 
 int spot_rla_decode(const spot_desc* desc, const void* q, const void* k_cache, const void* v_cache,
-                    const float* state, const int32_t* idx, const int32_t* cnt, float* o_rla, void* stream) {
+                    const float* state, const int32_t* idx, const int32_t* cnt, float* o_rla, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   int st = check_rla_decode(desc);
   if (st) return st;
   if (!q || !k_cache || !v_cache || !state || !idx || !cnt || !o_rla)
     return fail(SPOT_ERR_INVALID, "q, k_cache, v_cache, state, idx, cnt and o_rla are required");
+  const int ns = spot::rla_decode_num_splits(desc->batch, desc->hkv);
+  const size_t need = size_t(desc->batch) * desc->hq * ns * desc->d * sizeof(float);
+  if ((st = check_workspace(need, workspace, workspace_bytes))) return st;
   if ((st = check_aligned16("k_cache", k_cache)) || (st = check_aligned16("v_cache", v_cache)))
     return st;
   if (reinterpret_cast<uintptr_t>(q) & 1u) return fail(SPOT_ERR_INVALID, "q must be 2-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) & 3u) return fail(SPOT_ERR_INVALID, "workspace must be 4-byte aligned");
   const int nk = int(ceil_div64(desc->kv_len, desc->block));
   spot::RlaDecodeArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-                        static_cast<const uint16_t*>(v_cache), state, idx, cnt, o_rla, desc->batch, desc->hq,
-                        desc->hkv, desc->d, int(desc->kv_len), desc->block, nk};
+                        static_cast<const uint16_t*>(v_cache), state, idx, cnt, o_rla,
+                        static_cast<float*>(workspace), desc->batch, desc->hq, desc->hkv, desc->d,
+                        int(desc->kv_len), desc->block, nk, ns};
   return launched(spot::launch_rla_decode(a, static_cast<hipStream_t>(stream)), "rla_decode");
 }
 

@@ -95,7 +95,8 @@ enum spot_op {
   SPOT_OP_ORDER_HISTORY = 5,
   SPOT_OP_PREFILL_EARLY_STOP = 6,
   SPOT_OP_HISTORY_MAP = 7,
-  SPOT_OP_RLA_DECODE_STATE = 8
+  SPOT_OP_RLA_DECODE_STATE = 8,
+  SPOT_OP_RLA_DECODE = 9
 };
 
 /* Problem descriptor.  `version` must be SPOT_ABI_VERSION. */
@@ -418,8 +419,10 @@ int spot_sparse_attn_prefill_history_map(const spot_desc* desc, float tau, const
  *   [batch, hq, d], the caches, the state above and the kept lists of
  *   spot_select_topp -> o_rla fp32 [batch, hq, d] = phi(q)^T state minus the
  *   linear attention over the kept keys (only the kept blocks are read; list
- *   entries outside the cache add nothing).  k_cache, v_cache 16-byte
- *   aligned.  No workspace.
+ *   entries outside the cache add nothing).  The kept keys are split over
+ *   several workgroups whose partial sums sit in the workspace
+ *   (spot_workspace_size(SPOT_OP_RLA_DECODE)) and are subtracted in a fixed
+ *   order.  k_cache, v_cache 16-byte aligned, workspace 4-byte aligned.
  */
 int spot_rla_block_states(const spot_desc* desc, const void* k, const void* v, const int32_t* perm, float* states,
                           float* states_perm, void* stream);
@@ -428,7 +431,8 @@ int spot_rla_prefill(const spot_desc* desc, const void* q, const float* states, 
 int spot_rla_decode_state(const spot_desc* desc, const void* k_cache, const void* v_cache, float* state,
                           void* workspace, size_t workspace_bytes, void* stream);
 int spot_rla_decode(const spot_desc* desc, const void* q, const void* k_cache, const void* v_cache,
-                    const float* state, const int32_t* idx, const int32_t* cnt, float* o_rla, void* stream);
+                    const float* state, const int32_t* idx, const int32_t* cnt, float* o_rla, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -343,8 +343,8 @@ def test_rla_validation():
     def dst(d, k=FAKE, v=FAKE, s=FAKE, ws=FAKE, ws_bytes=1 << 40):
         return lib.spot_rla_decode_state(ctypes.byref(d), k, v, s, ws, ws_bytes, None)
 
-    def dec(d, q=FAKE, k=FAKE, v=FAKE, s=FAKE, idx=FAKE, cnt=FAKE, o=FAKE):
-        return lib.spot_rla_decode(ctypes.byref(d), q, k, v, s, idx, cnt, o, None)
+    def dec(d, q=FAKE, k=FAKE, v=FAKE, s=FAKE, idx=FAKE, cnt=FAKE, o=FAKE, ws=FAKE, ws_bytes=1 << 40):
+        return lib.spot_rla_decode(ctypes.byref(d), q, k, v, s, idx, cnt, o, ws, ws_bytes, None)
 
     assert st(_prefill(), k=None) == B.SPOT_ERR_INVALID
     assert st(_prefill(), s=None) == B.SPOT_ERR_INVALID
@@ -370,5 +370,9 @@ def test_rla_validation():
     assert dec(_decode(), s=None) == B.SPOT_ERR_INVALID
     assert dec(_decode(), k=FAKE + 2) == B.SPOT_ERR_INVALID
     assert dec(_decode(), q=FAKE + 1) == B.SPOT_ERR_INVALID
+    assert dec(_decode(), ws=None) == B.SPOT_ERR_WORKSPACE
+    assert dec(_decode(), ws_bytes=4) == B.SPOT_ERR_WORKSPACE
+    assert dec(_decode(), ws=FAKE + 2) == B.SPOT_ERR_INVALID
     dd = _decode(kv_len=131072)
     assert B.spot_workspace_size(dd, B.SPOT_OP_RLA_DECODE_STATE) == 2 * 2 * 32 * 128 * 128 * 4
+    assert B.spot_workspace_size(dd, B.SPOT_OP_RLA_DECODE) == 2 * 8 * 64 * 128 * 4     # 64 splits of 4 pairs

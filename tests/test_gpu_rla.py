@@ -115,7 +115,7 @@ def _decode_case(cfg, gpu, seqs=None, top_p=None):
     torch.cuda.synchronize()
     got = o.cpu().numpy()
     gl, gc = bufs.idx.cpu().numpy()[:, 0, 0], bufs.cnt.cpu().numpy()[:, 0, 0]
-    n_terms = SPAN + -(-cfg.T // SPAN) + 2 * cfg.d + int(gc.max()) * cfg.block
+    n_terms = SPAN + -(-cfg.T // SPAN) + 2 * cfg.d + int(gc.max()) * cfg.block + 64   # + the split partials
     for b in (range(cfg.batch) if seqs is None else seqs):
         kept = gl[b, :gc[b]]
         ref = oracle.spot_oracle.rla_decode(D["q"][b], D["k_cache"][b], D["v_cache"][b], kept, cfg.block, cfg.T)
