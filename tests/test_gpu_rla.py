@@ -42,24 +42,32 @@ def _check(name, got, ref, mag, n_terms):
     assert np.all(err <= tol * mag), (name, ratio, tol)
 
 
-def _prefill_case(cfg, gpu, top_p=None, perm=None, qblocks=None):
+def _prefill_case(cfg, gpu, top_p=None, perm=None, qblocks=None, **sel):
+    """GPU pipeline lists, then the residual on the GPU and in the oracle for every sequence of the batch."""
     host, dev = upload_prefill(cfg, gpu, perm)
-    bufs = gpu_prefill(cfg, dev, perm_dev=dev[3], top_p=top_p)
+    bufs = gpu_prefill(cfg, dev, perm_dev=dev[3], top_p=top_p, **sel)
     desc = B.prefill_desc(dev[0], dev[1], cfg.block, cfg.top_p if top_p is None else top_p,
-                          segment=cfg.segment if perm is not None else 0)
+                          segment=cfg.segment if perm is not None else 0, n_sink=sel.get("n_sink", cfg.n_sink),
+                          n_recent=sel.get("n_recent", cfg.n_recent))
     rb = B.rla_prefill(desc, dev[0], dev[1], dev[2], bufs.idx, bufs.cnt, perm=dev[3])
     torch.cuda.synchronize()
     q, k, v = host
-    lists = P.kept_lists(bufs.idx, bufs.cnt)[0]
-    got = rb.o_rla.cpu().numpy()[0]
+    all_lists = P.kept_lists(bufs.idx, bufs.cnt)
+    o_all = rb.o_rla.cpu().numpy()
     qb = np.arange(cfg.nb) if qblocks is None else np.asarray(qblocks)
     seg = cfg.segment if perm is not None else 0
-    pm = None if perm is None else perm[0]
-    ref = oracle.spot_oracle.rla_prefill(q[0], k[0], v[0], lists, cfg.block, segment=seg, perm=pm, qblocks=qb)
-    mag = oracle.spot_oracle.rla_prefill(q[0], k[0], np.abs(v[0]), lists, cfg.block, segment=seg, perm=pm,
-                                         qblocks=qb)
     rows = np.concatenate([np.arange(i * cfg.block, min((i + 1) * cfg.block, cfg.L)) for i in qb])
-    return got[:, rows], ref[:, rows], mag[:, rows], lists
+    got, ref, mag = [], [], []
+    for b in range(cfg.batch):
+        pm = None if perm is None else perm[b]
+        r = oracle.spot_oracle.rla_prefill(q[b], k[b], v[b], all_lists[b], cfg.block, segment=seg, perm=pm,
+                                           qblocks=qb)
+        m = oracle.spot_oracle.rla_prefill(q[b], k[b], np.abs(v[b]), all_lists[b], cfg.block, segment=seg,
+                                           perm=pm, qblocks=qb)
+        got.append(o_all[b][:, rows])
+        ref.append(r[:, rows])
+        mag.append(m[:, rows])
+    return np.stack(got), np.stack(ref), np.stack(mag), all_lists
 
 
 @pytest.mark.parametrize("kw", [dict(L=256, hq=1, hkv=1, d=64, dtype="f32", block=16, seed=1),
@@ -80,6 +88,33 @@ def test_rla_prefill_with_permutation(gpu):
     perm, _ = oracle.key_permutation(q[0], k[0], cfg.block, cfg.segment, 1 / math.sqrt(cfg.d))
     got, ref, mag, _ = _prefill_case(cfg, gpu, perm=perm[None])
     _check("rla permuted", got, ref, mag, cfg.block + cfg.nb + cfg.d)
+
+
+def test_rla_prefill_batch_and_sink(gpu):
+    """Two sequences (batch indexing of states, lists and outputs) and no sink block."""
+    cfg = I.small_prefill(name="rla-b2", L=900, hq=8, hkv=2, d=128, block=64, seed=26, batch=2)
+    got, ref, mag, _ = _prefill_case(cfg, gpu, n_sink=0)
+    _check("rla batch 2, no sink", got, ref, mag, cfg.block + cfg.nb + cfg.d)
+
+
+def test_rla_prefill_fp32_with_permutation(gpu):
+    cfg = I.small_prefill(name="rla-f32-perm", L=512, hq=4, hkv=2, d=64, dtype="f32", block=32, segment=128,
+                          seed=27, heavy_hitters=True)
+    q, k, _ = I.prefill_inputs(cfg)
+    perm, _ = oracle.key_permutation(q[0], k[0], cfg.block, cfg.segment, 1 / math.sqrt(cfg.d))
+    got, ref, mag, _ = _prefill_case(cfg, gpu, perm=perm[None])
+    _check("rla fp32 permuted", got, ref, mag, cfg.block + cfg.nb + cfg.d)
+
+
+def test_rla_prefill_c3_sampled(gpu):
+    """The heavy-hitter workload with its segment permutation at full size, three query blocks of later
+    segments checked."""
+    cfg = I.C3
+    q, k, _ = I.prefill_inputs(cfg)
+    perm, _ = oracle.key_permutation(q[0], k[0], cfg.block, cfg.segment, 1 / math.sqrt(cfg.d))
+    del q, k
+    got, ref, mag, _ = _prefill_case(cfg, gpu, perm=perm[None], qblocks=[17, 40, 63])
+    _check("rla C3 permuted", got, ref, mag, cfg.block + cfg.nb + cfg.d)
 
 
 def test_rla_prefill_keep_all_is_zero(gpu):
