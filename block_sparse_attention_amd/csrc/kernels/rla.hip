@@ -32,6 +32,9 @@
 namespace spot {
 
 constexpr int kRlaStage = 32;   // keys staged in LDS per round
+#ifndef SPOT_RLA_MFMA
+#define SPOT_RLA_MFMA 1   // prefill residual output phi(Q) R on fp32 MFMA (0: fp32 VALU)
+#endif
 
 // eight consecutive elements as floats (16 bytes of bf16 or 32 of fp32)
 __device__ __forceinline__ void load8(const uint16_t* p, float* o) {
@@ -217,6 +220,56 @@ __global__ __launch_bounds__(256) void rla_prefill_kernel(RlaPrefillArgs a) {
   for (int m = 0; m < PER; ++m) *reinterpret_cast<f32x4_t*>(Rs + (tid + m * 256) * 4) = acc[m];
   __syncthreads();
 
+#if SPOT_RLA_MFMA
+  // o = phi(Q) R on v_mfma_f32_32x32x2_f32, k two at a time: a wave takes tiles of 32 packed rows and all
+  // D columns; lane l holds phi(q) of row l % 32 at the k of parity l / 32 (A operand), reads
+  // R[2j + l / 32][32 ct + l % 32] from LDS (B operand) and keeps D / 32 accumulator tiles, whose
+  // element e of lane l is row 8 (e / 4) + 4 (l / 32) + e % 4, column 32 ct + l % 32.
+  {
+    const int rl = lane & 31, kh = lane >> 5;
+    const int GB = G * B;
+    const T* Q = static_cast<const T*>(a.q);
+    for (int tr = wv; tr * 32 < GB; tr += 4) {
+      float fa[D / 2];
+      {
+        const int pr = tr * 32 + rl;
+        const int h = g * G + pr / B, rr = i * B + pr % B;
+        const bool valid = pr < GB && rr < L;
+        const T* qrow = Q + ((size_t(b) * a.hq + (valid ? h : 0)) * L + (valid ? rr : 0)) * D;
+#pragma unroll
+        for (int pc = 0; pc < D / 8; ++pc) {
+          float x[8];
+          load8(qrow + pc * 8, x);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fa[pc * 4 + e] = valid ? expf(x[2 * e + kh]) : 0.f;
+        }
+      }
+      constexpr int CT = 2;   // column tiles per pass (accumulator registers: 16 per tile)
+#pragma unroll
+      for (int c0 = 0; c0 < D / 32; c0 += CT) {
+        f32x16_t acc[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x16_t{};
+#pragma unroll 4
+        for (int j = 0; j < D / 2; ++j)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[j], Rs[(2 * j + kh) * D + (c0 + ct) * 32 + rl],
+                                                           acc[ct], 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int pr = tr * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
+          const int h = g * G + pr / B, rr = i * B + pr % B;
+          if (pr < GB && rr < L) {
+            float* orow = a.o + ((size_t(b) * a.hq + h) * L + rr) * D;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) orow[(c0 + ct) * 32 + rl] = acc[ct][e];
+          }
+        }
+      }
+    }
+  }
+#else
   // o[p, c] = sum_k phi(q_p)[k] * R[k][c]: thread owns column c, rows p = s, s + NS, ...
   const int c = tid % D, s = tid / D;
   float rc[D];
@@ -258,6 +311,7 @@ __global__ __launch_bounds__(256) void rla_prefill_kernel(RlaPrefillArgs a) {
     }
     __syncthreads();
   }
+#endif
 }
 
 // ---------------------------------------------------------------- decode
