@@ -416,7 +416,8 @@ def bench_rla_prefill(args, torch, B, cfg, dev_in):
 def bench_rla_decode(args, torch, B, cfg, t):
     """Residual linear attention of the decode step: the whole-cache state is
     built once (it changes only with the cache); per step the state's
-    contribution minus the kept keys', on the lists of the bf16-indexer step."""
+    contribution minus the kept keys', on the lists of the bf16-indexer step,
+    as its own pass and inside the attention pass."""
     dev = torch.device("cuda:0")
     q, kc, vc = t["q"], t["kc"], t["vc"]
     desc = B.decode_desc(q, kc, cfg.block, cfg.top_p, cfg.h_idx, cfg.d_idx)
@@ -437,12 +438,33 @@ def bench_rla_decode(args, torch, B, cfg, t):
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
     ms = float(np.median(times))
+    # the same term inside the attention pass (the kept tiles it already reads), against the plain attention
+    fws = torch.empty(B.spot_workspace_size(desc, B.SPOT_OP_DECODE_RLA), dtype=torch.uint8, device=dev)
+    o2, lse2 = torch.empty_like(bufs.o), torch.empty_like(bufs.lse)
+
+    def timed(fn):
+        ts = []
+        for _ in range(max(args.steps, 3)):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    ms_plain = timed(lambda: B.spot_sparse_attn_decode(desc, q, kc, vc, bufs.idx, bufs.cnt, o2, lse2,
+                                                       bufs.workspace))
+    ms_fused = timed(lambda: B.spot_sparse_attn_decode_rla(desc, q, kc, vc, bufs.idx, bufs.cnt, state, o2, lse2, o,
+                                                           fws))
     cnt = bufs.cnt.cpu().numpy()[:, 0, 0].astype(np.int64)
     kv_bytes = float(cnt.sum()) * cfg.block * cfg.hkv * cfg.d * 2 * 2
     st_bytes = cfg.batch * cfg.hkv * cfg.d * cfg.d * 4.0
-    del ws, flush
+    del ws, fws, flush
     return {"workload": cfg.name, "ms_cache_state": round(ms_state, 4), "ms_per_step": round(ms, 4),
-            "bytes_per_step": kv_bytes + st_bytes, "gbs": round((kv_bytes + st_bytes) / (ms * 1e-3) / 1e9, 1)}
+            "bytes_per_step": kv_bytes + st_bytes, "gbs": round((kv_bytes + st_bytes) / (ms * 1e-3) / 1e9, 1),
+            "fused_with_attention": {"ms_attention": round(ms_plain, 4), "ms_attention_and_residual": round(ms_fused, 4)}}
 
 
 # ----------------------------------------------------------------- early stopping

@@ -21,7 +21,7 @@ SPOT_F32, SPOT_BF16 = 0, 1
 SPOT_SCORE_MEANPOOL, SPOT_SCORE_RELU_INDEXER, SPOT_SCORE_TAYLOR = 0, 1, 2
 SPOT_OP_BLOCK_SCORE, SPOT_OP_SELECT_TOPP, SPOT_OP_PREFILL, SPOT_OP_DECODE, SPOT_OP_KEY_PERMUTATION = 0, 1, 2, 3, 4
 SPOT_OP_ORDER_HISTORY, SPOT_OP_PREFILL_EARLY_STOP, SPOT_OP_HISTORY_MAP, SPOT_OP_RLA_DECODE_STATE = 5, 6, 7, 8
-SPOT_OP_RLA_DECODE = 9
+SPOT_OP_RLA_DECODE, SPOT_OP_DECODE_RLA = 9, 10
 ABI_VERSION = 1
 
 EXPORTS = ("spot_version", "spot_status_string", "spot_last_error", "spot_workspace_size", "spot_block_score",
@@ -30,7 +30,7 @@ EXPORTS = ("spot_version", "spot_status_string", "spot_last_error", "spot_worksp
            "spot_indexer_score_mxfp4", "spot_history_map", "spot_sparse_attn_prefill_history_map",
            "spot_validate_perm", "spot_sparse_attn_decode_noalloc", "spot_quantize_indexer_keys_int4",
            "spot_indexer_score_int4", "spot_rla_block_states", "spot_rla_prefill", "spot_rla_decode_state",
-           "spot_rla_decode")
+           "spot_rla_decode", "spot_sparse_attn_decode_rla")
 
 
 class spot_desc(ctypes.Structure):
@@ -88,6 +88,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spot_rla_prefill.argtypes = [D, P, P, P, P, P, P, P]
     lib.spot_rla_decode_state.argtypes = [D, P, P, P, P, S, P]
     lib.spot_rla_decode.argtypes = [D, P, P, P, P, P, P, P, P, S, P]
+    lib.spot_sparse_attn_decode_rla.argtypes = [D, P, P, P, P, P, P, P, P, P, P, S, P]
     for name in EXPORTS[3:]:
         getattr(lib, name).restype = I
     _lib = lib
@@ -254,6 +255,16 @@ def spot_rla_decode(desc, q, k_cache, v_cache, state, idx, cnt, o_rla, workspace
                                         _ptr(idx), _ptr(cnt), _ptr(o_rla), _ptr(workspace), ws_bytes,
                                         _stream() if stream is None else stream)
     _check("spot_rla_decode", st)
+
+
+def spot_sparse_attn_decode_rla(desc, q, k_cache, v_cache, idx, cnt, rla_state, o, lse, o_rla, workspace=None,
+                                stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load_library().spot_sparse_attn_decode_rla(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                    _ptr(idx), _ptr(cnt), _ptr(rla_state), _ptr(o), _ptr(lse),
+                                                    _ptr(o_rla), _ptr(workspace), ws_bytes,
+                                                    _stream() if stream is None else stream)
+    _check("spot_sparse_attn_decode_rla", st)
 
 
 # ----------------------------------------------------------------- descriptors

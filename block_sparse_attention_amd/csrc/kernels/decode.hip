@@ -18,6 +18,11 @@
 // decode_combine_kernel: merges the partials of the splits in split order
 //   (deterministic; all loads issued before the merge) and writes O (bf16)
 //   and the natural-log LSE.
+// With the residual linear attention (SPLA section 2.2) the split kernel also
+// sums (exp(q) . exp(k)) v over the kept keys it reads and takes its share of
+// the rows of exp(q)^T S_cache (S_cache = sum over the cache of exp(k) v^T,
+// built once per cache; the share's loads overlap those of the kept list);
+// the combine adds every split's difference in order.
 #include <mutex>
 
 #include "../launch.h"
@@ -49,7 +54,11 @@ template <> struct DVec<4> {
   static __device__ __forceinline__ uint32_t w(const T& v, int k) { return k == 0 ? v.x : v.y; }
 };
 
-template <int D, int G, int NT>
+// RLA: the same pass also accumulates the residual linear attention's kept-key
+// term (SPLA section 2.2: the selected blocks' linear attention, computed on
+// the kept tiles the attention already loads): per head, sum over the kept
+// keys of (exp(q) . exp(k)) v, merged over the streams by a plain sum.
+template <int D, int G, int NT, bool RLA>
 __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeArgs a, float scale_log2) {
   constexpr int EPL = D / 16;           // elements per lane
   constexpr int KS = NT / 16;           // key-slot streams per workgroup
@@ -57,6 +66,7 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeArgs a, float sc
   using V = DVec<EPL>;
   __shared__ float s_m[KS][G], s_l[KS][G];
   __shared__ float s_acc[KS][G][D];
+  __shared__ float s_racc[RLA ? KS : 1][G][RLA ? D : 1];
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, c = tid & 15, ks = tid >> 4;
@@ -71,9 +81,37 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeArgs a, float sc
     const int bi = s + ((ks + KS * u) >> lgB) * a.nsplit;
     ids[u] = il[bi < a.nk ? bi : 0];
   }
-  const int n = a.cnt[b];
-  if (s >= n) return;   // the combine reads splits [0, min(n, nsplit)) only
   const size_t pair = size_t(b) * a.hkv + g;
+  // residual: this split's rows k0 .. k1 of exp(q)^T S_cache for the outputs (head o / D, column o % D) it
+  // writes; it needs neither the count nor the list, so its loads overlap theirs
+  constexpr int ROUTS = RLA ? (G * D + NT - 1) / NT : 1;
+  float share[ROUTS];
+  if constexpr (RLA) {
+    const int rows_per = (D + a.nsplit - 1) / a.nsplit;
+    const int k0 = min(D, s * rows_per), k1 = min(D, k0 + rows_per);
+#pragma unroll
+    for (int u = 0; u < ROUTS; ++u) {
+      const int o = tid + u * NT;
+      share[u] = 0.f;
+      if (o < G * D) {
+        const uint16_t* qh = a.q + (size_t(b) * a.hq + g * G + o / D) * D;
+        const float* S = a.rla_state + pair * D * D + o % D;
+#pragma unroll 8
+        for (int k = k0; k < k1; ++k) share[u] = fmaf(expf(bf16_to_f32(qh[k])), S[size_t(k) * D], share[u]);
+      }
+    }
+  }
+  const int n = a.cnt[b];
+  if (s >= n) {   // no kept block of its own: the attention combine reads splits [0, min(n, nsplit)) only
+    if constexpr (RLA) {
+#pragma unroll
+      for (int u = 0; u < ROUTS; ++u) {
+        const int o = tid + u * NT;
+        if (o < G * D) a.rla_partials[(pair * a.nsplit + s) * G * D + o] = share[u];
+      }
+    }
+    return;
+  }
   const int nmine = (n - s + a.nsplit - 1) / a.nsplit;   // blocks s, s + nsplit, ... below n
 
   {
@@ -95,6 +133,18 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeArgs a, float sc
       l[hh] = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
+    }
+    float fq[RLA ? G : 1][EPL], racc[RLA ? G : 1][EPL];   // exp(q) of the lane's dims; kept-key term
+    if constexpr (RLA) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int k2 = 0; k2 < EPL / 2; ++k2) {
+          const uint32_t w = V::w(qv[hh], k2);
+          fq[hh][2 * k2] = expf(bf16_lo(w));
+          fq[hh][2 * k2 + 1] = expf(bf16_hi(w));
+          racc[hh][2 * k2] = racc[hh][2 * k2 + 1] = 0.f;
+        }
     }
 
     // slot j of stream ks is slot ks + KS j of the split: key (ks + KS j) mod B of local block (ks + KS j) / B
@@ -126,6 +176,26 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeArgs a, float sc
           const uint32_t w = V::w(vv[u], k2);
           vf[2 * k2] = bf16_lo(w);
           vf[2 * k2 + 1] = bf16_hi(w);
+        }
+        if constexpr (RLA) {
+          float fk[EPL];
+#pragma unroll
+          for (int k2 = 0; k2 < EPL / 2; ++k2) {
+            const uint32_t w = V::w(kv[u], k2);
+            fk[2 * k2] = expf(bf16_lo(w));
+            fk[2 * k2 + 1] = expf(bf16_hi(w));
+          }
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            float wd = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) wd = fmaf(fq[hh][e], fk[e], wd);
+            wd = row16_sum(wd);
+            if (ok[u]) {
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) racc[hh][e] = fmaf(wd, vf[e], racc[hh][e]);
+            }
+          }
         }
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
@@ -178,6 +248,10 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeArgs a, float sc
       }
 #pragma unroll
       for (int e = 0; e < EPL; ++e) s_acc[ks][hh][c * EPL + e] = acc[hh][e];
+      if constexpr (RLA) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s_racc[ks][hh][c * EPL + e] = racc[hh][e];
+      }
     }
     __syncthreads();
     float* part = a.partials + (pair * a.nsplit + s) * G * (D + 2);
@@ -201,11 +275,17 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeArgs a, float sc
         ph[D] = M;
         ph[D + 1] = Lsum;
       }
+      if constexpr (RLA) {   // its share of the state term minus the kept keys' term of its streams
+        float R = 0.f;
+#pragma unroll
+        for (int q = 0; q < KS; ++q) R += s_racc[q][hh][dd];
+        a.rla_partials[(pair * a.nsplit + s) * G * D + o] = share[(o - tid) / NT] - R;
+      }
     }
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool RLA>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, dd = threadIdx.x;
   const int g = h / G, hh = h % G;
@@ -236,6 +316,17 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const float val = Lsum > 0.f ? A / Lsum : 0.f;
   a.o[(size_t(b) * a.hq + h) * D + dd] = uint16_t(pack_bf16x2(val, 0.f) & 0xFFFFu);
   if (a.lse && dd == 0) a.lse[size_t(b) * a.hq + h] = (Lsum > 0.f) ? (M + __log2f(Lsum)) * kLn2 : -kInf;
+  if constexpr (RLA) {
+    // every split's partial (its share of exp(q)^T S_cache minus its kept keys' term), in split order
+    const float* rp = a.rla_partials + ((size_t(b) * a.hkv + g) * a.nsplit) * G * D + hh * D + dd;
+    float rs[kDecMaxSplits];
+#pragma unroll
+    for (int s2 = 0; s2 < kDecMaxSplits; ++s2) rs[s2] = s2 < a.nsplit ? rp[size_t(s2) * G * D] : 0.f;
+    float r = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < kDecMaxSplits; ++s2) r += rs[s2];
+    a.o_rla[(size_t(b) * a.hq + h) * D + dd] = r;
+  }
 }
 
 #ifndef SPOT_DECODE_TARGET_WGS
@@ -283,10 +374,13 @@ hipError_t decode_scratch(float** ptr) {
 
 template <int D, int G>
 static hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, float scale_log2) {
-  decode_split_kernel<D, G, kDecThreads><<<dim3(a.nsplit, a.hkv, a.batch), kDecThreads, 0, s>>>(a, scale_log2);
+  const dim3 grid(a.nsplit, a.hkv, a.batch);
+  if (a.o_rla) decode_split_kernel<D, G, kDecThreads, true><<<grid, kDecThreads, 0, s>>>(a, scale_log2);
+  else decode_split_kernel<D, G, kDecThreads, false><<<grid, kDecThreads, 0, s>>>(a, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_combine_kernel<D, G><<<dim3(a.hq, a.batch), D, 0, s>>>(a);
+  if (a.o_rla) decode_combine_kernel<D, G, true><<<dim3(a.hq, a.batch), D, 0, s>>>(a);
+  else decode_combine_kernel<D, G, false><<<dim3(a.hq, a.batch), D, 0, s>>>(a);
   return hipGetLastError();
 }
 

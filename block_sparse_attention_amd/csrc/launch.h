@@ -138,6 +138,10 @@ struct DecodeArgs {
   float* partials;     // workspace: [batch, hkv, nsplit, G, d + 2] fp32 (acc, max, sum)
   int batch, hq, hkv, d, T, block, nk, nsplit;
   float sm_scale;
+  // residual linear attention beside the attention (all three set, or none)
+  const float* rla_state;   // [batch, hkv, d, d] state of the whole cache
+  float* rla_partials;      // workspace: [batch, hkv, nsplit, G, d] kept-key terms
+  float* o_rla;             // [batch, hq, d]
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 int decode_num_splits(int batch, int hkv, int nk);

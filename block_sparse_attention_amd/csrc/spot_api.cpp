@@ -178,6 +178,13 @@ int spot_workspace_size(const spot_desc* desc, int op, size_t* bytes) {
       *bytes = size_t(desc->batch) * desc->hkv * nr * desc->d * desc->d * sizeof(float);
       break;
     }
+    case SPOT_OP_DECODE_RLA: {
+      const int nk = int(ceil_div64(desc->kv_len, desc->block));
+      const int ns = spot::decode_num_splits(desc->batch, desc->hkv, nk);
+      *bytes = spot::decode_partials_bytes(desc->batch, desc->hq, desc->d, ns) +
+               size_t(desc->batch) * desc->hq * ns * desc->d * sizeof(float);
+      break;
+    }
     case SPOT_OP_RLA_DECODE: {
       const size_t ns = size_t(spot::rla_decode_num_splits(desc->batch, desc->hkv));
       *bytes = size_t(desc->batch) * desc->hq * ns * desc->d * sizeof(float);
@@ -487,6 +494,34 @@ int spot_sparse_attn_decode(const spot_desc* desc, const void* q, const void* k_
                      static_cast<float*>(workspace), desc->batch, desc->hq, desc->hkv, desc->d, int(desc->kv_len),
                      desc->block, nk, ns, effective_scale(desc)};
   return launched(spot::launch_decode(a, static_cast<hipStream_t>(stream)), "sparse_attn_decode");
+}
+
+int spot_sparse_attn_decode_rla(const spot_desc* desc, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* idx, const int32_t* cnt, const float* rla_state, void* o, float* lse,
+                                float* o_rla, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_common(desc);
+  if (st) return st;
+  if (desc->q_len != 1) return fail(SPOT_ERR_INVALID, "decode needs q_len == 1");
+  if (desc->dtype != SPOT_BF16) return fail(SPOT_ERR_UNSUPPORTED, "decode supports bf16 only");
+  const int G = desc->hq / desc->hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(SPOT_ERR_UNSUPPORTED, "hq/hkv = %d (supported: 1, 2, 4, 8)", G);
+  if (!q || !k_cache || !v_cache || !idx || !cnt || !rla_state || !o || !o_rla)
+    return fail(SPOT_ERR_INVALID, "q, k_cache, v_cache, idx, cnt, rla_state, o and o_rla are required");
+  const int nk = int(ceil_div64(desc->kv_len, desc->block));
+  const int ns = spot::decode_num_splits(desc->batch, desc->hkv, nk);
+  const size_t att = spot::decode_partials_bytes(desc->batch, desc->hq, desc->d, ns);
+  const size_t need = att + size_t(desc->batch) * desc->hq * ns * desc->d * sizeof(float);
+  if ((st = check_workspace(need, workspace, workspace_bytes))) return st;
+  if ((st = check_aligned16("q", q)) || (st = check_aligned16("k_cache", k_cache)) ||
+      (st = check_aligned16("v_cache", v_cache)) || (st = check_aligned16("workspace", workspace)))
+    return st;
+  if (reinterpret_cast<uintptr_t>(rla_state) & 3u) return fail(SPOT_ERR_INVALID, "rla_state must be 4-byte aligned");
+  spot::DecodeArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+                     static_cast<const uint16_t*>(v_cache), idx, cnt, static_cast<uint16_t*>(o), lse,
+                     static_cast<float*>(workspace), desc->batch, desc->hq, desc->hkv, desc->d, int(desc->kv_len),
+                     desc->block, nk, ns, effective_scale(desc), rla_state,
+                     reinterpret_cast<float*>(static_cast<char*>(workspace) + att), o_rla};
+  return launched(spot::launch_decode(a, static_cast<hipStream_t>(stream)), "sparse_attn_decode_rla");
 }
 
 int spot_sparse_attn_decode_noalloc(const spot_desc* desc, const void* q, const void* k_cache, const void* v_cache,

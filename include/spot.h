@@ -96,7 +96,8 @@ enum spot_op {
   SPOT_OP_PREFILL_EARLY_STOP = 6,
   SPOT_OP_HISTORY_MAP = 7,
   SPOT_OP_RLA_DECODE_STATE = 8,
-  SPOT_OP_RLA_DECODE = 9
+  SPOT_OP_RLA_DECODE = 9,
+  SPOT_OP_DECODE_RLA = 10
 };
 
 /* Problem descriptor.  `version` must be SPOT_ABI_VERSION. */
@@ -424,6 +425,20 @@ int spot_sparse_attn_prefill_history_map(const spot_desc* desc, float tau, const
  *   (spot_workspace_size(SPOT_OP_RLA_DECODE)) and are subtracted in a fixed
  *   order.  k_cache, v_cache 16-byte aligned, workspace 4-byte aligned.
  */
+/*
+ * Decode attention with the residual linear attention in the same pass
+ * ([SPLA] §2.2: the selected blocks' linear-attention term is computed in the
+ * fused kernel from the kept tiles the attention already reads).  Exactly
+ * spot_sparse_attn_decode (o and lse, the same arithmetic), plus o_rla fp32
+ * [batch, hq, d] = exp(q)^T rla_state minus the kept keys' sum of
+ * (exp(q) . exp(k)) v, with rla_state from spot_rla_decode_state.  Same
+ * requirements as spot_sparse_attn_decode; rla_state 4-byte aligned;
+ * workspace: spot_workspace_size(SPOT_OP_DECODE_RLA).
+ */
+int spot_sparse_attn_decode_rla(const spot_desc* desc, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* idx, const int32_t* cnt, const float* rla_state, void* o, float* lse,
+                                float* o_rla, void* workspace, size_t workspace_bytes, void* stream);
+
 int spot_rla_block_states(const spot_desc* desc, const void* k, const void* v, const int32_t* perm, float* states,
                           float* states_perm, void* stream);
 int spot_rla_prefill(const spot_desc* desc, const void* q, const float* states, const float* states_perm,

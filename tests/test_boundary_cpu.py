@@ -373,6 +373,17 @@ def test_rla_validation():
     assert dec(_decode(), ws=None) == B.SPOT_ERR_WORKSPACE
     assert dec(_decode(), ws_bytes=4) == B.SPOT_ERR_WORKSPACE
     assert dec(_decode(), ws=FAKE + 2) == B.SPOT_ERR_INVALID
+    def fused(d, rs=FAKE, o_rla=FAKE, ws=FAKE, ws_bytes=1 << 40):
+        return lib.spot_sparse_attn_decode_rla(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, rs, FAKE, None, o_rla,
+                                               ws, ws_bytes, None)
+
+    assert fused(_decode(), rs=None) == B.SPOT_ERR_INVALID
+    assert fused(_decode(), o_rla=None) == B.SPOT_ERR_INVALID
+    assert fused(_decode(), ws_bytes=16) == B.SPOT_ERR_WORKSPACE
+    assert fused(_decode(), rs=FAKE + 2) == B.SPOT_ERR_INVALID
+    assert fused(_decode(hq=6, hkv=2)) == B.SPOT_ERR_UNSUPPORTED
     dd = _decode(kv_len=131072)
+    assert B.spot_workspace_size(dd, B.SPOT_OP_DECODE_RLA) == (B.spot_workspace_size(dd, B.SPOT_OP_DECODE)
+                                                               + 2 * 8 * 32 * 128 * 4)
     assert B.spot_workspace_size(dd, B.SPOT_OP_RLA_DECODE_STATE) == 2 * 2 * 32 * 128 * 128 * 4
     assert B.spot_workspace_size(dd, B.SPOT_OP_RLA_DECODE) == 2 * 8 * 64 * 128 * 4     # 64 splits of 4 pairs

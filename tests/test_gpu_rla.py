@@ -172,3 +172,41 @@ def test_rla_decode_c4(gpu):
     """The decode workload (batch 16, context 131072): the whole-cache state
     and the residual of every sequence on the GPU, three sequences checked."""
     _decode_case(I.C4, gpu, seqs=[0, 7, 15])
+
+
+def _fused_case(cfg, gpu, seqs=None):
+    """The decode attention with the residual in the same pass: O and LSE equal to the plain call's bit for
+    bit, the residual against the oracle on the same lists."""
+    D = I.decode_inputs(cfg)
+    dev = {k: (torch.from_numpy(v).to(gpu) if k == "idx_w" else P.to_dev(v, "bf16", gpu)) for k, v in D.items()}
+    bufs = B.decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["idx_q"], dev["idx_w"], dev["idx_k"], cfg.block,
+                    cfg.top_p)
+    desc = B.decode_desc(dev["q"], dev["k_cache"], cfg.block, cfg.top_p, cfg.h_idx, cfg.d_idx)
+    state = B.rla_decode_state(desc, dev["k_cache"], dev["v_cache"])
+    ws = torch.empty(B.spot_workspace_size(desc, B.SPOT_OP_DECODE_RLA), dtype=torch.uint8, device=gpu)
+    o2, lse2 = torch.empty_like(bufs.o), torch.empty_like(bufs.lse)
+    o_rla = torch.empty(cfg.batch, cfg.hq, cfg.d, dtype=torch.float32, device=gpu)
+    B.spot_sparse_attn_decode_rla(desc, dev["q"], dev["k_cache"], dev["v_cache"], bufs.idx, bufs.cnt, state, o2,
+                                  lse2, o_rla, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, bufs.o) and torch.equal(lse2, bufs.lse)
+    got = o_rla.cpu().numpy()
+    gl, gc = bufs.idx.cpu().numpy()[:, 0, 0], bufs.cnt.cpu().numpy()[:, 0, 0]
+    n_terms = SPAN + -(-cfg.T // SPAN) + 2 * cfg.d + int(gc.max()) * cfg.block + 64
+    for b in (range(cfg.batch) if seqs is None else seqs):
+        kept = gl[b, :gc[b]]
+        ref = oracle.spot_oracle.rla_decode(D["q"][b], D["k_cache"][b], D["v_cache"][b], kept, cfg.block, cfg.T)
+        mag = oracle.spot_oracle.rla_decode(D["q"][b], D["k_cache"][b], np.abs(D["v_cache"][b]), [], cfg.block,
+                                            cfg.T)
+        _check(f"fused {cfg.name} seq {b} kept {len(kept)}", got[b], ref, mag, n_terms)
+
+
+@pytest.mark.parametrize("kw", [dict(batch=2, T=2000), dict(batch=2, T=10000 + 7, hq=16, hkv=2),
+                                dict(batch=1, T=4096 * 2, hq=8, hkv=8, d=64), dict(batch=3, T=300, top_p=0.5)],
+                         ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_rla_decode_fused_small(gpu, kw):
+    _fused_case(I.C4.with_(name="rla-fused", seed=43, **kw), gpu)
+
+
+def test_rla_decode_fused_c4(gpu):
+    _fused_case(I.C4, gpu, seqs=[0, 9, 15])
