@@ -210,3 +210,36 @@ def test_rla_decode_fused_small(gpu, kw):
 
 def test_rla_decode_fused_c4(gpu):
     _fused_case(I.C4, gpu, seqs=[0, 9, 15])
+
+
+def test_rla_decode_on_host_lists(gpu):
+    """Both decode forms of the residual on lists drawn on the host: an empty list (the whole cache is the
+    rest), the ragged last block alone, a sparse random list and every block (nothing is left: zero up to
+    the window)."""
+    cfg = I.C4.with_(name="rla-lists", seed=29, batch=4, T=16 * 300 + 9)
+    D = I.decode_inputs(cfg)
+    nt = cfg.nt
+    rng = np.random.default_rng(31)
+    lists = [np.zeros(0, np.int64), np.array([nt - 1]), np.sort(rng.choice(nt, 37, replace=False)), np.arange(nt)]
+    dev = {k: P.to_dev(D[k], "bf16", gpu) for k in ("q", "k_cache", "v_cache")}
+    desc = B.decode_desc(dev["q"], dev["k_cache"], cfg.block, cfg.top_p, cfg.h_idx, cfg.d_idx)
+    bufs = B.alloc_decode(desc, gpu)
+    idx = np.full((cfg.batch, 1, 1, nt), -1, np.int32)
+    for b, kl in enumerate(lists):
+        idx[b, 0, 0, :len(kl)] = kl
+    bufs.idx.copy_(torch.from_numpy(idx))
+    bufs.cnt.copy_(torch.tensor([len(kl) for kl in lists], dtype=torch.int32).view(cfg.batch, 1, 1))
+    state = B.rla_decode_state(desc, dev["k_cache"], dev["v_cache"])
+    sep = B.rla_decode(desc, dev["q"], dev["k_cache"], dev["v_cache"], state, bufs.idx, bufs.cnt)
+    ws = torch.empty(B.spot_workspace_size(desc, B.SPOT_OP_DECODE_RLA), dtype=torch.uint8, device=gpu)
+    fused = torch.empty_like(sep)
+    B.spot_sparse_attn_decode_rla(desc, dev["q"], dev["k_cache"], dev["v_cache"], bufs.idx, bufs.cnt, state, bufs.o,
+                                  bufs.lse, fused, ws)
+    torch.cuda.synchronize()
+    n_terms = SPAN + -(-cfg.T // SPAN) + 2 * cfg.d + nt * cfg.block + 64
+    for name, out in (("own pass", sep.cpu().numpy()), ("fused", fused.cpu().numpy())):
+        for b, kl in enumerate(lists):
+            ref = oracle.spot_oracle.rla_decode(D["q"][b], D["k_cache"][b], D["v_cache"][b], kl, cfg.block, cfg.T)
+            mag = oracle.spot_oracle.rla_decode(D["q"][b], D["k_cache"][b], np.abs(D["v_cache"][b]), [], cfg.block,
+                                                cfg.T)
+            _check(f"host lists {name} seq {b} kept {len(kl)}", out[b], ref, mag, n_terms)
