@@ -229,13 +229,24 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
   // where this thread's chunks of tile t come from: byte offset in the slab
   // (out of range for an empty slot) and the row's mask limit (-1: always
   // visible, position: visible iff <= query row, INT_MAX: no key)
+  // With the permutation, the permuted row of a history slot is loaded when the tile is mapped and
+  // chosen only when the tile is gathered, a step later: a select right after the load becomes a
+  // branch around it whose wait (vmcnt 0) would also wait for the tile loads in flight.
   struct RowMap {
-    uint32_t off[CH];
+    uint32_t off[CH];        // the slot's natural row and chunk (out of range for an empty slot)
     int lim[CH];
+    int pp[PERM ? CH : 1];   // the permuted row of the slot's position
   };
   auto swz = [](int r) {
     return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
   };
+  // the lane fills slot cid % CPR of tile row cid / CPR: it loads the chunk that slot holds
+  uint32_t colb[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int cid = tid + c * NT;
+    colb[c] = uint32_t(((cid % CPR) ^ swz(cid / CPR)) << 4);
+  }
   auto map_tile = [&](int t, RowMap& m) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -247,23 +258,22 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
       const int pos = base + (s & (B - 1));
       const bool valid = inl && unsigned(pos) < unsigned(L);
       const bool hist = base < seg_start;
-      int phys = pos;
-      if constexpr (PERM) {
-        const int pp = permg[valid ? pos : 0];
-        phys = hist ? pp : pos;
-      }
-      // the lane fills slot cid % CPR of tile row cid / CPR: it loads the chunk that slot holds
-      m.off[c] = valid ? uint32_t(phys) * RB + uint32_t(((cid % CPR) ^ swz(cid / CPR)) << 4) : 0x80000000u;
+      m.off[c] = valid ? uint32_t(pos) * RB + colb[c] : 0x80000000u;
       m.lim[c] = valid ? (hist ? -1 : pos) : 0x7fffffff;
+      if constexpr (PERM) m.pp[c] = permg[valid ? pos : 0];
     }
   };
   // HBM -> LDS without registers: the wave's 64 lanes of chunk round c fill
-  // the 1 KiB that starts at chunk wv * 64 + c * NT of the tile
+  // the 1 KiB that starts at chunk wv * 64 + c * NT of the tile; a history
+  // slot (mask limit -1) reads the permuted row
   auto gather = [&](const __amdgpu_buffer_rsrc_t& rs, const RowMap& m, uint16_t* tile) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c)
+    for (int c = 0; c < CH; ++c) {
+      uint32_t off = m.off[c];
+      if constexpr (PERM) off = m.lim[c] == -1 ? uint32_t(m.pp[c]) * RB + colb[c] : off;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(tile + (wv * 64 + c * NT) * 8), 16, uint32_t(m.off[c]), 0, 0, 0);
+          rs, (__attribute__((address_space(3))) void*)(tile + (wv * 64 + c * NT) * 8), 16, off, 0, 0, 0);
+    }
   };
   // s_waitcnt vmcnt(0) (immediate fields: vmcnt 3:0, expcnt 6:4, lgkmcnt 11:8;
   // the last two at their maxima): this wave's tile loads are in LDS
