@@ -456,8 +456,12 @@ __global__ __launch_bounds__(256) void indexer_score_mxfp4_kernel(IndexerFp4Args
     }
   }
   const float w = act ? a.idx_w[size_t(b) * a.h_idx + head] : 0.f;
-  const uint8_t* cb = a.codes + size_t(b) * a.nk * (R / 2);
-  const uint8_t* sb = a.scales + size_t(b) * a.nk * (R / 32);
+  // codes and scales of sequence b as buffer resources: a lane without a row reads out of range (zero), so
+  // every load of the round is issued unconditionally and all are in flight together
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.codes + size_t(b) * a.nk * (R / 2)), 0, a.nk * (R / 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.scales + size_t(b) * a.nk * (R / 32)), 0, a.nk * (R / 32), 0x00020000);
   const int step = gridDim.x * 4 * RPW * kFp4Unroll;
   for (int t0 = (blockIdx.x * 4 + wave) * RPW * kFp4Unroll; t0 < a.nk; t0 += step) {
     uint4 cv[kFp4Unroll];
@@ -466,8 +470,9 @@ __global__ __launch_bounds__(256) void indexer_score_mxfp4_kernel(IndexerFp4Args
     for (int u = 0; u < kFp4Unroll; ++u) {
       const int t = t0 + u * RPW + sub;
       const bool in = act && t < a.nk;
-      cv[u] = in ? *reinterpret_cast<const uint4*>(cb + size_t(t) * (R / 2) + li * 16) : make_uint4(0u, 0u, 0u, 0u);
-      ex[u] = in ? int(sb[size_t(t) * (R / 32) + li]) - 127 : 0;
+      cv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rc, in ? uint32_t(t * (R / 2) + li * 16) : 0x80000000u, 0, 0));
+      ex[u] = __builtin_amdgcn_raw_buffer_load_b8(rsc, in ? uint32_t(t * (R / 32) + li) : 0x80000000u, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kFp4Unroll; ++u) {
@@ -485,7 +490,7 @@ __global__ __launch_bounds__(256) void indexer_score_mxfp4_kernel(IndexerFp4Args
         dp = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[i], 1.0f, 3)),
                        qw[4 * i + 3], dp);
       }
-      dp = ldexpf(dp, ex[u]);
+      dp = ldexpf(dp, ex[u] - 127);
       for (int o = 1; o < lph; o <<= 1) dp += __shfl_xor(dp, o);
       float val = (act && (li % lph) == 0) ? w * fmaxf(dp, 0.f) : 0.f;
 #pragma unroll
@@ -593,18 +598,22 @@ __global__ __launch_bounds__(256) void indexer_score_int4_kernel(IndexerInt4Args
     }
   }
   const float w = act ? a.idx_w[size_t(b) * a.h_idx + head] : 0.f;
-  const uint8_t* cb = a.codes + size_t(b) * a.nk * (R / 2);
-  const uint16_t* sb = a.scales + size_t(b) * a.nk * (R / 32);
+  // as in the MXFP4 scan: out-of-range buffer reads (zero) for lanes without a row, every load in flight
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.codes + size_t(b) * a.nk * (R / 2)), 0, a.nk * (R / 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.scales + size_t(b) * a.nk * (R / 32)), 0, a.nk * (R / 32) * 2, 0x00020000);
   const int step = gridDim.x * 4 * RPW * kFp4Unroll;
   for (int t0 = (blockIdx.x * 4 + wave) * RPW * kFp4Unroll; t0 < a.nk; t0 += step) {
     uint4 cv[kFp4Unroll];
-    float scv[kFp4Unroll];
+    uint32_t scb[kFp4Unroll];   // scale bits, widened where they are used
 #pragma unroll
     for (int u = 0; u < kFp4Unroll; ++u) {
       const int t = t0 + u * RPW + sub;
       const bool in = act && t < a.nk;
-      cv[u] = in ? *reinterpret_cast<const uint4*>(cb + size_t(t) * (R / 2) + li * 16) : make_uint4(0u, 0u, 0u, 0u);
-      scv[u] = in ? bf16_to_f32(sb[size_t(t) * (R / 32) + li]) : 0.f;
+      cv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rc, in ? uint32_t(t * (R / 2) + li * 16) : 0x80000000u, 0, 0));
+      scb[u] = __builtin_amdgcn_raw_buffer_load_b16(rsc, in ? uint32_t((t * (R / 32) + li) * 2) : 0x80000000u, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kFp4Unroll; ++u) {
@@ -626,7 +635,7 @@ __global__ __launch_bounds__(256) void indexer_score_int4_kernel(IndexerInt4Args
           dp = fmaf(__builtin_amdgcn_cvt_off_f32_i4((hi >> (8 * j)) & 0xffu), qf[8 * i + 2 * j + 1], dp);
         }
       }
-      dp = (dp * 16.0f) * scv[u];
+      dp = (dp * 16.0f) * bf16_to_f32(uint16_t(scb[u]));
       for (int o = 1; o < lph; o <<= 1) dp += __shfl_xor(dp, o);
       float val = (act && (li % lph) == 0) ? w * fmaxf(dp, 0.f) : 0.f;
 #pragma unroll
