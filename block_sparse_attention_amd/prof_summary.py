@@ -29,13 +29,16 @@ COPY_BYTES = 1 << 30
 # (kernel-name fragment, source file, workload key, first, count): the launches
 # of that kernel from position first * steps to (first + count) * steps - 1,
 # in the profiling workload's fixed order (long-context prefill, GQA prefill,
-# decode with the bf16 indexer cache, with the MXFP4 cache, keeping every
-# block, early-stopped heavy-hitter prefill); count 0 takes every launch.
+# decode with the bf16 indexer cache, with the MXFP4 cache, with the INT4
+# cache, keeping every block, early-stopped heavy-hitter prefill, top-p
+# heavy-hitter prefill through the permutation); count 0 takes every launch.
 TRACKED = [
     ("prefill_mfma_kernel<128, 8, 1, false, false, true>", "prefill.hip", "prefill_mfma_kernel@long-bf16-L131072", 0, 1),
     ("prefill_mfma_kernel<128, 8, 1, false, false, true>", "prefill.hip", "prefill_mfma_kernel@gqa-bf16-L8192", 1, 1),
     ("prefill_mfma_kernel<128, 8, 1, true, true, true>", "prefill.hip",
      "prefill_mfma_kernel_early_stop@heavy-perm-bf16-L32768", 0, 0),
+    ("prefill_mfma_kernel<128, 8, 1, true, false, true>", "prefill.hip", "prefill_mfma_kernel@heavy-perm-bf16-L32768",
+     0, 0),
     ("decode_split_kernel<128, 4", "decode.hip", "decode_split_kernel@decode-b16-T131072", 0, 1),
     ("decode_split_kernel<128, 4", "decode.hip", "decode_split_kernel@decode-b16-T131072-keep-all", 3, 1),
     ("indexer_score_kernel<", "score.hip", "indexer_score_kernel@decode-b16-T131072", 0, 1),

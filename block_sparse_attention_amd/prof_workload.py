@@ -6,7 +6,8 @@ prefill steps of the GQA workload (L=8192, block 64, top-p 0.9), `--steps`
 decode steps of the sparse decode workload (batch 16, context 131072) with the
 bf16 indexer cache, then with the MXFP4 indexer cache, then with the INT4
 indexer cache, then keeping every block (p = 1), `--steps` early-stopped prefill steps of the heavy-hitter
-workload (L=32768, segment 2048, tau 0.01, permutation on the GPU), and
+workload (L=32768, segment 2048, tau 0.01, permutation on the GPU), `--steps`
+top-p prefill steps of that workload through the same permutation, and
 `--steps` plain device copies of 1 GiB, whose counter readings calibrate
 FETCH_SIZE / WRITE_SIZE against a known byte count.  The summariser
 attributes launches of a kernel that several parts use by this order.
@@ -92,7 +93,12 @@ def main():
             ebufs = B.prefill_early_stop(eq, ek, ev, ec.block, ec.segment, 0.01, perm=perm, bufs=ebufs)
         torch.cuda.synchronize()
         print(f"early-stopped prefill steps done: {args.steps}", flush=True)
-        del eq, ek, ev, perm, ebufs
+        pbufs = None
+        for _ in range(args.steps):
+            pbufs = B.prefill(eq, ek, ev, ec.block, ec.top_p, perm=perm, segment=ec.segment, bufs=pbufs)
+        torch.cuda.synchronize()
+        print(f"top-p prefill steps through the permutation done: {args.steps}", flush=True)
+        del eq, ek, ev, perm, ebufs, pbufs
 
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
