@@ -333,8 +333,8 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
   };
 
   f32x16_t oacc[QG][D / 32];
-  float m_run[QG], l_run[QG];   // ES: l_run is the whole row's sum (both lane halves); else this half's
-  float dsum[QG];               // ES: mass of the history block in progress
+  float m_run[QG], l_run[QG];   // l_run: this lane half's share of the row sum
+  float dsum[QG];               // ES: this lane half's share of the mass of the history block in progress
   int nused[QG];                // ES: history blocks taken
   bool active[QG];              // ES: the row still takes blocks
 #pragma unroll
@@ -396,10 +396,11 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
             if (kp[rt * 32 + 8 * (e >> 2) + 4 * hf + (e & 3)] > r_[gq]) s_cur[gq][rt][e] = -kInf;
         mx = lane_max(s_cur[gq]);
       }
-      mx = xhalf_max(mx);
-      const float mcand = mx * scale_log2;
-      const bool need = active[gq] && mcand > m_run[gq] + kRescaleThreshold;
-      if (__ballot(need)) {
+      // A row's max exceeds the threshold only if the max of one of its lane halves does, so the
+      // lane-half exchange is needed only when the wave votes for a rescale (rare after the first tile).
+      if (__ballot(active[gq] && mx * scale_log2 > m_run[gq] + kRescaleThreshold)) {
+        const float mcand = xhalf_max(mx) * scale_log2;
+        const bool need = active[gq] && mcand > m_run[gq] + kRescaleThreshold;
         const float m_new = need ? mcand : m_run[gq];
         const float alpha = need ? __builtin_amdgcn_exp2f(m_run[gq] - m_new) : 1.0f;
         l_run[gq] *= alpha;
@@ -469,13 +470,15 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
       bool any = false;
 #pragma unroll
       for (int gq = 0; gq < QG; ++gq) {
-        const float rsum = xhalf_sum(rs[gq]);
-        l_run[gq] += rsum;
-        if (t >= own_tiles) dsum[gq] += rsum;
+        l_run[gq] += rs[gq];
+        if (t >= own_tiles) dsum[gq] += rs[gq];
         if (block_end) {
+          // the row stops when block mass < tau * row sum: the sign of the sum over both lane halves of
+          // (mass - tau * sum), one lane-half exchange per block
+          const float below = xhalf_sum(dsum[gq] - a.tau * l_run[gq]);
           if (active[gq]) {
             ++nused[gq];
-            if (dsum[gq] < a.tau * l_run[gq]) active[gq] = false;
+            if (below < 0.f) active[gq] = false;
           }
           dsum[gq] = 0.f;
         }
@@ -518,7 +521,7 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
 
 #pragma unroll
   for (int gq = 0; gq < QG; ++gq) {
-    const float l_tot = ES ? l_run[gq] : xhalf_sum(l_run[gq]);
+    const float l_tot = xhalf_sum(l_run[gq]);
     if (qvalid[gq]) {
       if (ES && a.nused && hf == 0) a.nused[(size_t(b) * a.hq + hq_[gq]) * L + r_[gq]] = nused[gq];
       const float inv = 1.0f / l_tot;
