@@ -494,9 +494,10 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
     }
 
     // (C) tile t+2's mask limits; K(t+2) and V(t+1) in LDS before the barrier
-    // only a tile that is masked reads its limits: the ones touching the last kept block (top-p) or the
-    // diagonal block at the end of the own segment (early stop)
-    if (ES ? (t + 2 < own_tiles && t + 2 >= own_tiles - tpb) : (t + 2 >= nfull)) put_kpos(kpos[(t + 2) % 3], mK);
+    // only a tile that is masked reads its limits, and in the top-p kernel those are the tiles touching
+    // the last kept block; the early-stopped kernel writes them every tile (the test would take it past
+    // its 256 registers)
+    if (ES || t + 2 >= nfull) put_kpos(kpos[(t + 2) % 3], mK);
     loads_landed();
     __syncthreads();
     mV = mK;
