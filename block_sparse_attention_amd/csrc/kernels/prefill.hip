@@ -154,7 +154,8 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
   // early stopping always stages its (reordered) list; the top-p kernel when every list of the launch fits
   constexpr int LCAP = ES ? (kListCap > kEsMaxBlocks ? kListCap : kEsMaxBlocks) : kListCap;
   __shared__ int s_list[LCAP > 0 ? LCAP : 1];
-  __shared__ int s_act[2][NW];   // early stop: per-wave "a row is still taking blocks", by tile parity
+  // early stop: per-wave "a row is still taking blocks", by tile parity (one byte per wave, read as one word)
+  __shared__ __attribute__((aligned(8))) uint8_t s_act[2][NW];
   static_assert(!ES || LCAP >= kEsMaxBlocks, "early stopping stages its visiting list in LDS");
   static_assert(!ES || LLDS, "early stopping reads its list from LDS");
   static_assert(!LLDS || LCAP > 0, "no LDS copy of the list");
@@ -486,7 +487,7 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
       }
       if (block_end) {
         const bool wave_any = __ballot(any) != 0;   // whole wave: block_end is uniform
-        if (lane == 0) s_act[t & 1][wv] = wave_any;
+        if (lane == 0) s_act[t & 1][wv] = uint8_t(wave_any);
       }
     } else {
 #pragma unroll
@@ -504,21 +505,32 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
     mK = mN;
     if constexpr (ES) {
       if (block_end) {
-        int any = 0;
+        if constexpr (NW == 8) {
+          return *reinterpret_cast<const uint64_t*>(s_act[t & 1]) != 0;
+        } else {
+          int any = 0;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) any |= s_act[t & 1][w];
-        return any != 0;
+          for (int w = 0; w < NW; ++w) any |= s_act[t & 1][w];
+          return any != 0;
+        }
       }
     }
     return true;
   };
 
-  // unrolled by two so the score tiles alternate between register sets
+  // unrolled by two so the score tiles alternate between register sets.  The
+  // early-stopped loop is left only after the second step of a pair: with
+  // 64-key blocks every history tile ends a block, and with blocks of 128 or
+  // more keys the block ends fall on odd tiles, so the second step's vote
+  // covers the first's; a step taken after every row has stopped adds nothing
+  // (its exponentials are 0 and no count moves).  Testing after the first
+  // step as well made the compiler serialize the LDS fragment reads of the
+  // second (6% slower).
   int t = 0;
   bool go = true;
   for (; go && t + 1 < ntiles; t += 2) {
-    go = step(std::integral_constant<int, 0>{}, t, sa, sb, ma, mb);
-    if (go) go = step(std::integral_constant<int, 1>{}, t + 1, sb, sa, mb, ma);
+    step(std::integral_constant<int, 0>{}, t, sa, sb, ma, mb);   // a block end here is one at t + 1 too
+    go = step(std::integral_constant<int, 1>{}, t + 1, sb, sa, mb, ma);
   }
   if (go && t < ntiles) step(std::integral_constant<int, 0>{}, t, sa, sb, ma, mb);
 
