@@ -14,8 +14,6 @@ from block_sparse_attention_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "tests", "c_abi_check.c")
 INCLUDE = os.path.join(ROOT, "include")
-
-
 LIB = os.path.join(ROOT, "block_sparse_attention_amd", "libspot.so")
 
 
@@ -25,9 +23,8 @@ def c_results(tmp_path_factory):
     if cc is None:
         pytest.skip("no C compiler")
     assert os.path.exists(LIB), "build the library first (__graft_entry__.build())"
-    lib = LIB
     exe = str(tmp_path_factory.mktemp("cabi") / "c_abi_check")
-    libdir = os.path.dirname(lib)
+    libdir = os.path.dirname(LIB)
     subprocess.run([cc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", f"-I{INCLUDE}", SRC, "-o", exe,
                     f"-L{libdir}", "-l:libspot.so", f"-Wl,-rpath,{libdir}"], check=True, capture_output=True)
     out = subprocess.run([exe], check=True, capture_output=True, text=True, timeout=120).stdout
