@@ -496,8 +496,8 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? 2 : 1) void prefill_mfma_kernel(
 
     // (C) tile t+2's mask limits; K(t+2) and V(t+1) in LDS before the barrier
     // only a tile that is masked reads its limits, and in the top-p kernel those are the tiles touching
-    // the last kept block; the early-stopped kernel writes them every tile (the test would take it past
-    // its 256 registers)
+    // the last kept block; the early-stopped kernel writes them every tile (the same test there once
+    // spilled its registers, and with the current loop it measures no faster)
     if (ES || t + 2 >= nfull) put_kpos(kpos[(t + 2) % 3], mK);
     loads_landed();
     __syncthreads();
